@@ -1,0 +1,193 @@
+/*
+ * moedec.h - C ABI of libmoedec: the routed Mixture-of-Experts FFN step of
+ * GLM-5.2-style decode on AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the pages state it:
+ *   - Show HN page "धीमे कंप्यूटर पर GLM 5.2 चलाना" (hi.news.hada.io), section
+ *     "implement किए गए मुख्य features": a DeepSeek-V3-style sigmoid router
+ *     (noaux_tc correction, routed_scaling_factor, shared expert); int8,
+ *     packed int4 and packed int2 weights with one scale per row, dequantised
+ *     on use; batch-union MoE (each unique expert of a batch read once and
+ *     applied to every position routed to it).
+ *   - ideipro.ru, "Энтузиаст запустил GLM-5.2 на ноутбуке с 25 ГБ RAM": 8
+ *     experts per token in each MoE layer; packing checked bit for bit.
+ *   - same Show HN page, section "disk streaming आधारित MoE execution तरीका":
+ *     256 routed experts per layer, about 19 MB per int4 expert.
+ * Points the pages leave open are fixed as follows (and documented per call):
+ * group score = sum of the two largest bias-corrected scores of a group;
+ * corrected scores select, unbiased sigmoid scores weigh; ties go to the lower
+ * index; experts are SwiGLU (h = silu(Wg x) * (Wu x), y = Wd h, no biases);
+ * shared experts weigh 1; codes are two's complement, lowest column in the
+ * lowest bits of its byte; matrices are [out_rows, in] row-major, packed
+ * along the input dimension, one fp32 scale per output row.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns and
+ *     frees all memory.  The library allocates nothing, keeps no mutable global
+ *     state, and never synchronises: work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and the call returns at once.
+ *   - Struct arguments (moedec_experts, moedec_worklist) are HOST memory read
+ *     during the call; their pointer fields are device pointers.
+ *   - Arguments are validated before anything is enqueued.  Return values:
+ *     MOEDEC_OK, MOEDEC_ERR_INVALID_ARG (null pointer, inconsistent sizes),
+ *     MOEDEC_ERR_UNSUPPORTED (valid but outside the kernels' limits below),
+ *     MOEDEC_ERR_DEVICE (the HIP runtime reported a launch error).
+ *   - Non-finite inputs give unspecified (but memory-safe) results.
+ *   - Limits: 1 <= T <= MOEDEC_MAX_TOKENS; n_experts <= MOEDEC_MAX_EXPERTS;
+ *     n_group <= 64; top_k <= 32; n_shared <= 8; hidden and inter must be
+ *     multiples of 128/bits (one 16-byte group of codes) and at most 16384.
+ */
+#ifndef MOEDEC_H
+#define MOEDEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEDEC_OK 0
+#define MOEDEC_ERR_INVALID_ARG 1
+#define MOEDEC_ERR_UNSUPPORTED 2
+#define MOEDEC_ERR_DEVICE 3
+
+#define MOEDEC_MAX_TOKENS 64
+#define MOEDEC_MAX_EXPERTS 1024
+#define MOEDEC_MAX_DIM 16384
+
+/* A static, never-NULL description of a status code. */
+const char* moedec_status_string(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+int moedec_abi_version(void);
+
+/*
+ * One layer's experts.  Routed experts are 0..n_experts-1, shared experts
+ * n_experts..n_experts+n_shared-1; all have the same shape and bit width.
+ *   w_gate, w_up : uint8 [(E+S), inter,  hidden*bits/8]   packed codes
+ *   w_down       : uint8 [(E+S), hidden, inter*bits/8]
+ *   s_gate, s_up : fp32  [(E+S), inter]   one scale per output row
+ *   s_down       : fp32  [(E+S), hidden]
+ * Weight of row r, column c = code[r][c] * scale[r].
+ */
+typedef struct moedec_experts {
+    int32_t hidden, inter, n_experts, n_shared, bits;
+    const uint8_t* w_gate;
+    const uint8_t* w_up;
+    const uint8_t* w_down;
+    const float* s_gate;
+    const float* s_up;
+    const float* s_down;
+} moedec_experts;
+
+/*
+ * The batch union: every expert used by the batch, once, with the
+ * (token, slot) assignments routed to it.  Written by moe_route_topk, read by
+ * the expert calls.  With K = top_k, S = n_shared and
+ * max_active = min(n_experts, T*K) + S:
+ *   n_active  : int32 [1]               unique experts, shared ones included
+ *   expert_id : int32 [max_active]      ascending; shared expert j is E + j
+ *   seg       : int32 [max_active + 1]  assign[seg[i] .. seg[i+1]) belong to expert_id[i]
+ *   assign    : int32 [T*(K+S)]         assignment index t*(K+S)+slot, ascending
+ *                                       within each expert; slots 0..K-1 are the
+ *                                       routed slots of token t, K..K+S-1 its shared slots
+ * Only the first n_active (+1 for seg) entries are defined after the call.
+ */
+typedef struct moedec_worklist {
+    int32_t* n_active;
+    int32_t* expert_id;
+    int32_t* seg;
+    int32_t* assign;
+} moedec_worklist;
+
+/*
+ * Router (Show HN page, "implemented features", router item; ideipro.ru: top-8).
+ *   x        : fp32 [T, H]   token activations
+ *   router_w : fp32 [E, H]   router weight, row e = expert e
+ *   bias     : fp32 [E]      noaux_tc correction bias (selection only)
+ * Computes s[t][e] = sigmoid(router_w[e] . x[t]) and c = s + bias; keeps the
+ * topk_group groups (of n_group contiguous groups of E/n_group experts) with
+ * the largest top-2 sums of c; picks the top_k largest c among the kept
+ * groups' experts, in descending order (ties: lower index); weights
+ * w_k = s_k / (sum over the chosen s, taken in slot order) * routed_scaling_factor.
+ * Outputs:
+ *   scores   : fp32  [T, E]  the sigmoid scores s (unbiased)
+ *   topk_idx : int32 [T, top_k]
+ *   topk_w   : fp32  [T, top_k]
+ *   wl       : the batch union (may be NULL to skip it); n_shared sets its
+ *              shared slots
+ * Requires E % n_group == 0, E/n_group >= 2, 1 <= topk_group <= n_group,
+ * 1 <= top_k <= topk_group*E/n_group.  H must be a multiple of 4.
+ */
+int moe_route_topk(const float* x, const float* router_w, const float* bias,
+                   int T, int H, int E, int n_group, int topk_group, int top_k,
+                   int n_shared, float routed_scaling_factor,
+                   float* scores, int32_t* topk_idx, float* topk_w,
+                   const moedec_worklist* wl, void* stream);
+
+/*
+ * Gate/up projections and SwiGLU for every assignment of the batch union
+ * (Show HN page, "implemented features": dequant-on-use kernels and the
+ * batch-union item).  Each active expert's gate and up codes are read once
+ * for all tokens routed to it.
+ *   x : fp32 [T, H] (the same activations the router saw)
+ *   h : fp32 [T*(top_k+S), inter]; row a = assignment a of the worklist gets
+ *       silu(s_gate * (Qg x_t)) * (s_up * (Qu x_t))
+ * ex->bits must be 4 (q4), 8 (q8) or 2 (q2) to match the suffix.
+ */
+int moe_expert_gate_up_silu_q4(const float* x, const moedec_experts* ex, const moedec_worklist* wl,
+                               int T, int top_k, float* h, void* stream);
+int moe_expert_gate_up_silu_q8(const float* x, const moedec_experts* ex, const moedec_worklist* wl,
+                               int T, int top_k, float* h, void* stream);
+int moe_expert_gate_up_silu_q2(const float* x, const moedec_experts* ex, const moedec_worklist* wl,
+                               int T, int top_k, float* h, void* stream);
+
+/*
+ * Down projection and weighted combine (Show HN page, "implemented features":
+ * router item, shared expert, routed_scaling_factor already in topk_w).
+ *   h      : fp32 [T*(top_k+S), inter]  from the gate/up call
+ *   topk_w : fp32 [T, top_k]            from moe_route_topk
+ *   y      : fp32 [T, H]; y[t] = sum_k topk_w[t][k] * o(t, k) + sum_j o(t, K+j),
+ *            o(t, slot) = s_down * (Qd h[t*(K+S)+slot])
+ * Every output row is owned by one workgroup that adds the experts in
+ * ascending id order: the result is deterministic (no atomics).
+ */
+int moe_expert_down_combine_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                               const float* topk_w, int T, int top_k, float* y, void* stream);
+int moe_expert_down_combine_q8(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                               const float* topk_w, int T, int top_k, float* y, void* stream);
+int moe_expert_down_combine_q2(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                               const float* topk_w, int T, int top_k, float* y, void* stream);
+
+/*
+ * Packing of codes (ideipro.ru: packing checked bit for bit; Show HN page,
+ * "implemented features": int8, packed int4, packed int2).
+ *   codes  : int8  [rows, row_len]                 one code per int8
+ *   packed : uint8 [rows, row_len*bits/8]
+ * Field j of packed byte k holds column k*(8/bits)+j in bits j*bits ..
+ * j*bits+bits-1 (two's complement).  pack keeps the low `bits` bits of each
+ * code and does not range-check (codes must lie in [-2^(bits-1), 2^(bits-1)-1]);
+ * unpack sign-extends.  row_len must be a multiple of 8/bits.
+ */
+int moe_pack_q4(const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len, void* stream);
+int moe_unpack_q4(const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len, void* stream);
+int moe_pack_q8(const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len, void* stream);
+int moe_unpack_q8(const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len, void* stream);
+int moe_pack_q2(const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len, void* stream);
+int moe_unpack_q2(const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len, void* stream);
+
+/*
+ * Between stacked MoE layers: x <- x + y (skipped when y is NULL), then
+ * xn <- x / sqrt(mean(x^2) + eps) per token (weightless RMSNorm).  The pages
+ * describe the MoE layer only; this pre-norm residual form is the reading
+ * used for a stack of layers.
+ *   x : fp32 [T, H] (updated in place), y : fp32 [T, H] or NULL, xn : fp32 [T, H]
+ */
+int moe_residual_rmsnorm(float* x, const float* y, float* xn, int T, int H, float eps,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDEC_H */

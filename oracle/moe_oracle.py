@@ -112,8 +112,9 @@ def unpack_rows(packed: np.ndarray, bits: int) -> np.ndarray:
 
 def dequantize(packed: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
     """W[r, c] = code[r, c] * scale[r], exact in fp64 (dequant-on-use, R10)."""
-    q = unpack_rows(packed, bits).astype(np.float64)
-    return q * np.asarray(scales, dtype=np.float64)[:, None]
+    w = unpack_rows(packed, bits).astype(np.float64)
+    w *= np.asarray(scales, dtype=np.float64)[:, None]
+    return w
 
 
 # --------------------------------------------------------------------- router
@@ -191,6 +192,19 @@ def selection_margin(scores64: np.ndarray, bias: np.ndarray, n_group: int, topk_
     return out
 
 
+def order_margin(scores64: np.ndarray, bias: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Per token, the smallest fp64 gap between the corrected scores of
+    consecutive chosen slots (infinite for one slot): where it is wide, the
+    slot order is the same for any correct fp32 implementation."""
+    c = np.asarray(scores64, np.float64) + np.asarray(bias, np.float64)
+    out = np.full(idx.shape[0], np.inf)
+    for t in range(idx.shape[0]):
+        v = c[t, idx[t]]
+        if len(v) > 1:
+            out[t] = float(np.min(v[:-1] - v[1:]))
+    return out
+
+
 # ---------------------------------------------------------- batch union
 # [HN] batch-union item: each unique expert of the batch once, with every
 # (token, slot) routed to it.
@@ -248,25 +262,24 @@ class LayerResult:
     worklist: Worklist
     h: np.ndarray           # [T * (K + S), I] fp64, row = assignment index
     y: np.ndarray           # [T, H] fp64
-    margin: np.ndarray      # [T] fp64 selection margin
+    margin: np.ndarray      # [T] fp64 selection margin (decides the set)
+    order: np.ndarray       # [T] fp64 gap between consecutive slots (decides the order)
 
 
 def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
               expert: Callable[[int], dict], *, n_group: int, topk_group: int, top_k: int,
-              n_shared: int, rsf: float, bits: int, scores32: np.ndarray | None = None) -> LayerResult:
+              n_shared: int, rsf: float, bits: int) -> LayerResult:
     """One routed-MoE layer on T tokens.
 
     expert(e) returns the packed codes and row scales of expert e
     ({q_gate, q_up, q_down, s_gate, s_up, s_down}); routed experts are
-    0..E-1, shared ones E..E+S-1.  scores32, if given, replaces the fp32
-    rounding of the oracle's own router scores as the input of the selection
-    (used to check a selection taken from another implementation's scores)."""
+    0..E-1, shared ones E..E+S-1.  The selection is taken on the fp64 scores
+    rounded to fp32."""
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     E = router_w.shape[0]
     s64 = router_scores(x, router_w)
-    s32 = s64.astype(np.float32) if scores32 is None else np.asarray(scores32, np.float32)
-    idx, w = select_experts(s32, bias, n_group, topk_group, top_k, rsf)
+    idx, w = select_experts(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf)
     wl = batch_union(idx, E, n_shared)
     slots = top_k + n_shared
     y = np.zeros((T, router_w.shape[1]), np.float64)
@@ -285,7 +298,7 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
             coef = float(w[t, slot]) if slot < top_k else 1.0
             y[t] += coef * o
     margin = selection_margin(s64, bias, n_group, topk_group, top_k)
-    return LayerResult(s64, idx, w, wl, h_all, y, margin)
+    return LayerResult(s64, idx, w, wl, h_all, y, margin, order_margin(s64, bias, idx))
 
 
 def rmsnorm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:

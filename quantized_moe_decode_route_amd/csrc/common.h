@@ -1,0 +1,160 @@
+// Device helpers and internal launch interfaces of libmoedec (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moedec.h"
+
+namespace moedec {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float bits_f(int v) { return __int_as_float(v); }
+__device__ __forceinline__ int f_bits(float v) { return __float_as_int(v); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    // DPP move with every row and bank enabled; lanes without a source read 0.
+    return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPR lanes (LPR a power of two <= 64); the sum is
+// returned in every lane of the group.  Within a row of 16 lanes the exchange
+// uses DPP (quad swaps, half-row mirror, row mirror); beyond it, lane swizzles.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LPR >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+    if constexpr (LPR >= 16) v += dpp_f<0x140>(v);  // row_mirror
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Same for a group size known only at run time (small shapes; not hot).
+__device__ __forceinline__ float group_sum_rt(float v, int lpr) {
+    for (int off = 1; off < lpr; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ------------------------------------------------------------ code decoding
+//
+// A lane reads 16 bytes of a packed row: 16 * (8/BITS) consecutive columns.
+// The decoder turns each 32-bit word into floats without any per-field shift:
+//   t = word ^ OFFSET_PATTERN   maps every two's-complement field q to the
+//                                unsigned value q + 2^(BITS-1)
+//   m_j = t & FIELD_MASK_j      isolates field j of all four bytes in place
+//   v_cvt_f32_ubyte{k}(m_j)     = (q + 2^(BITS-1)) * 2^(j*BITS) for byte k
+// so a dot product over the word is sum_j 2^(-j*BITS) * sum_k m_jk * x, minus
+// 2^(BITS-1) * sum(x), which the callers subtract once per row.
+
+template <int BITS>
+struct Codec;
+
+template <>
+struct Codec<4> {
+    static constexpr int F = 2;                     // fields per byte
+    static constexpr uint32_t kFlip = 0x88888888u;
+    static constexpr float kOffset = 8.0f;
+    __device__ static constexpr uint32_t mask(int j) { return j == 0 ? 0x0F0F0F0Fu : 0xF0F0F0F0u; }
+    __device__ static constexpr float scale(int j) { return j == 0 ? 1.0f : 0.0625f; }
+};
+
+template <>
+struct Codec<8> {
+    static constexpr int F = 1;
+    static constexpr uint32_t kFlip = 0x80808080u;
+    static constexpr float kOffset = 128.0f;
+    __device__ static constexpr uint32_t mask(int) { return 0xFFFFFFFFu; }
+    __device__ static constexpr float scale(int) { return 1.0f; }
+};
+
+template <>
+struct Codec<2> {
+    static constexpr int F = 4;
+    static constexpr uint32_t kFlip = 0xAAAAAAAAu;
+    static constexpr float kOffset = 2.0f;
+    __device__ static constexpr uint32_t mask(int j) {
+        return j == 0 ? 0x03030303u : j == 1 ? 0x0C0C0C0Cu : j == 2 ? 0x30303030u : 0xC0C0C0C0u;
+    }
+    __device__ static constexpr float scale(int j) {
+        return j == 0 ? 1.0f : j == 1 ? 0.25f : j == 2 ? 0.0625f : 0.015625f;
+    }
+};
+
+// Unsigned byte k of w as a float: one v_cvt_f32_ubyte{k}.  Written as asm
+// because the compiler otherwise re-derives each byte with a bit-field extract
+// from the unmasked word (two instructions per field instead of one).
+template <int K>
+__device__ __forceinline__ float ubyte_f(uint32_t w) {
+    float r;
+    if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w));
+    return r;
+}
+
+// Decode one 16-byte group into 16*F floats (scaled field values, see above):
+// out[(4*d + k) * F + j] belongs to column (4*d + k) * F + j of the group.
+template <int BITS>
+__device__ __forceinline__ void decode16(const uint4& q, float* out) {
+    using C = Codec<BITS>;
+    const uint32_t w[4] = {q.x ^ C::kFlip, q.y ^ C::kFlip, q.z ^ C::kFlip, q.w ^ C::kFlip};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int j = 0; j < C::F; ++j) {
+            const uint32_t m = w[d] & C::mask(j);
+            out[(4 * d + 0) * C::F + j] = ubyte_f<0>(m);
+            out[(4 * d + 1) * C::F + j] = ubyte_f<1>(m);
+            out[(4 * d + 2) * C::F + j] = ubyte_f<2>(m);
+            out[(4 * d + 3) * C::F + j] = ubyte_f<3>(m);
+        }
+    }
+}
+
+// 128-bit global load.
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// ------------------------------------------------------------ launch interfaces
+
+struct ExpertArgs {
+    const uint8_t* w_gate;
+    const uint8_t* w_up;
+    const uint8_t* w_down;
+    const float* s_gate;
+    const float* s_up;
+    const float* s_down;
+    const int32_t* n_active;
+    const int32_t* expert_id;
+    const int32_t* seg;
+    const int32_t* assign;
+    int T, H, I, top_k, slots, max_active;
+};
+
+hipError_t launch_route(const float* x, const float* router_w, const float* bias, int T, int H,
+                        int E, int n_group, int topk_group, int top_k, int n_shared, float rsf,
+                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                        hipStream_t stream);
+
+hipError_t launch_gate_up(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t stream);
+
+hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
+                       hipStream_t stream);
+
+hipError_t launch_pack(int bits, const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len,
+                       hipStream_t stream);
+hipError_t launch_unpack(int bits, const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len,
+                         hipStream_t stream);
+
+hipError_t launch_residual_rmsnorm(float* x, const float* y, float* xn, int T, int H, float eps,
+                                   hipStream_t stream);
+
+}  // namespace moedec

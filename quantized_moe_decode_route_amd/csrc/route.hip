@@ -1,0 +1,234 @@
+// Router: sigmoid scores, noaux_tc-corrected group-limited top-k, weights, and
+// the batch union (worklist) of the selected experts.
+//
+// Show HN page "धीमे कंप्यूटर पर GLM 5.2 चलाना", section "implemented features":
+// DeepSeek-V3-style sigmoid router with noaux_tc correction,
+// routed_scaling_factor and a shared expert; batch-union MoE.  The
+// group-score rule (top-2 sum), the use of the corrected score for selection
+// only and the tie-breaking (lower index) are this library's reading.
+//
+// Kernel 1 (router_gemv): one workgroup per expert row streams the fp32 router
+// row once per token with 16-byte loads and writes s = sigmoid(W_r[e] . x_t).
+// Kernel 2 (route_select): one workgroup; each wave routes one token at a time
+// (group top-2 sums, topk_group rounds of a wave arg-max over groups, top_k
+// rounds over the kept experts, weights), then the workgroup builds the
+// expert-ascending worklist with a counting sort.
+#include "common.h"
+
+namespace moedec {
+
+namespace {
+
+constexpr int kGemvThreads = 256;
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxEPL = MOEDEC_MAX_EXPERTS / kWave;   // experts per lane
+
+__global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* __restrict__ x,
+                                                                   const float* __restrict__ W, int T, int H,
+                                                                   int E, float* __restrict__ scores) {
+    __shared__ float red[MOEDEC_MAX_TOKENS][kGemvThreads / kWave];
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const float4* w4 = reinterpret_cast<const float4*>(W + (size_t)e * H);
+    const int n4 = H >> 2;
+    for (int t = 0; t < T; ++t) {
+        const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * H);
+        float acc = 0.f;
+        for (int i = threadIdx.x; i < n4; i += kGemvThreads) {
+            const float4 w = w4[i], v = x4[i];
+            acc += (w.x * v.x + w.y * v.y) + (w.z * v.z + w.w * v.w);
+        }
+        acc = group_sum<kWave>(acc);
+        if (lane == 0) red[t][wave] = acc;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < T; t += kGemvThreads) {
+        const float z = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
+        scores[(size_t)t * E + e] = 1.0f / (1.0f + expf(-z));
+    }
+}
+
+// (v, i) beats (u, j) if v > u, or v == u and i < j.
+__device__ __forceinline__ bool beats(float v, int i, float u, int j) { return v > u || (v == u && i < j); }
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float u = __shfl_xor(v, off, kWave);
+        const int j = __shfl_xor(i, off, kWave);
+        if (beats(u, j, v, i)) { v = u; i = j; }
+    }
+}
+
+// Exclusive scan of `v` over the workgroup; returns the prefix, writes the total.
+__device__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += u;
+    }
+    if (lane == kWave - 1) wave_tot[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+        if (w < wave) before += wave_tot[w];
+        total += wave_tot[w];
+    }
+    __syncthreads();
+    return before + inc - v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void route_select_kernel(
+    const float* __restrict__ scores, const float* __restrict__ bias, int T, int E, int n_group, int topk_group,
+    int top_k, int n_shared, float rsf, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ wl_n_active, int32_t* __restrict__ wl_expert_id, int32_t* __restrict__ wl_seg,
+    int32_t* __restrict__ wl_assign) {
+    __shared__ float cs[kSelWaves][MOEDEC_MAX_EXPERTS];
+    __shared__ int sel[MOEDEC_MAX_TOKENS * 32];
+    __shared__ int cnt[MOEDEC_MAX_EXPERTS + 8];
+    __shared__ int ea[MOEDEC_MAX_TOKENS * 40];
+    __shared__ int start[MOEDEC_MAX_EXPERTS + 8];
+    __shared__ int wave_tot[kSelWaves];
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int per = E / n_group;
+    const int epl = (E + kWave - 1) / kWave;
+
+    for (int t = wave; t < T; t += kSelWaves) {
+        const float* st = scores + (size_t)t * E;
+        float cand[kMaxEPL];
+#pragma unroll
+        for (int i = 0; i < kMaxEPL; ++i) {
+            const int e = lane + i * kWave;
+            cand[i] = -INFINITY;
+            if (i < epl && e < E) {
+                const float c = st[e] + bias[e];
+                cand[i] = c;
+                cs[wave][e] = c;
+            }
+        }
+        __threadfence_block();   // this wave's LDS writes before its lanes read each other's
+        // group score: largest plus second largest corrected score in the group
+        float gs = -INFINITY;
+        if (lane < n_group) {
+            float m1 = -INFINITY, m2 = -INFINITY;
+            for (int k = 0; k < per; ++k) {
+                const float c = cs[wave][lane * per + k];
+                if (c > m1) { m2 = m1; m1 = c; }
+                else if (c > m2) { m2 = c; }
+            }
+            gs = m1 + m2;
+        }
+        // keep topk_group groups
+        uint64_t kept = 0;
+        for (int r = 0; r < topk_group; ++r) {
+            float v = gs;
+            int g = lane < n_group ? lane : 0x7fffffff;
+            wave_argmax(v, g);
+            kept |= 1ull << g;
+            if (lane == g) gs = -INFINITY;
+        }
+        // candidates outside the kept groups drop out
+#pragma unroll
+        for (int i = 0; i < kMaxEPL; ++i) {
+            const int e = lane + i * kWave;
+            if (i < epl && e < E && !((kept >> (e / per)) & 1ull)) cand[i] = -INFINITY;
+        }
+        // top_k rounds of an arg-max over (c, -index)
+        int mine = -1;
+        for (int k = 0; k < top_k; ++k) {
+            float v = -INFINITY;
+            int ie = 0x7fffffff;
+#pragma unroll
+            for (int i = 0; i < kMaxEPL; ++i) {
+                const int e = lane + i * kWave;
+                if (i < epl && e < E && beats(cand[i], e, v, ie)) { v = cand[i]; ie = e; }
+            }
+            wave_argmax(v, ie);
+            if (lane == k) mine = ie;
+            if ((ie & (kWave - 1)) == lane) {
+#pragma unroll
+                for (int i = 0; i < kMaxEPL; ++i)
+                    if (i == (ie >> 6)) cand[i] = -INFINITY;
+            }
+        }
+        // weights: unbiased scores renormalised in slot order, times rsf
+        float total = 0.f;
+        for (int k = 0; k < top_k; ++k) {
+            const int ek = __shfl(mine, k, kWave);
+            total += st[ek];
+        }
+        if (lane < top_k) {
+            const float wv = st[mine] / total;
+            topk_idx[t * top_k + lane] = mine;
+            topk_w[t * top_k + lane] = wv * rsf;
+            sel[t * top_k + lane] = mine;
+        }
+    }
+    if (wl_n_active == nullptr) return;
+    __syncthreads();
+
+    // batch union: counting sort of the assignments by expert
+    const int slots = top_k + n_shared;
+    const int A = T * slots;
+    const int NE = E + n_shared;
+    for (int i = threadIdx.x; i < NE; i += kSelThreads) cnt[i] = 0;
+    for (int a = threadIdx.x; a < A; a += kSelThreads) {
+        const int t = a / slots, s = a - t * slots;
+        ea[a] = s < top_k ? sel[t * top_k + s] : E + (s - top_k);
+    }
+    __syncthreads();
+    for (int a = threadIdx.x; a < A; a += kSelThreads) atomicAdd(&cnt[ea[a]], 1);
+    __syncthreads();
+    // per-thread contiguous chunk of experts, then a workgroup scan
+    const int chunk = (NE + kSelThreads - 1) / kSelThreads;
+    const int e0 = threadIdx.x * chunk;
+    int my_cnt = 0, my_act = 0;
+    for (int e = e0; e < min(NE, e0 + chunk); ++e) {
+        my_cnt += cnt[e];
+        my_act += cnt[e] > 0;
+    }
+    int tot_cnt, tot_act;
+    int cnt_before = block_exclusive_scan(my_cnt, wave_tot, tot_cnt);
+    int act_before = block_exclusive_scan(my_act, wave_tot, tot_act);
+    for (int e = e0; e < min(NE, e0 + chunk); ++e) {
+        start[e] = cnt_before;
+        if (cnt[e] > 0) {
+            wl_expert_id[act_before] = e;
+            wl_seg[act_before] = cnt_before;
+            ++act_before;
+        }
+        cnt_before += cnt[e];
+    }
+    if (threadIdx.x == 0) {
+        *wl_n_active = tot_act;
+        wl_seg[tot_act] = tot_cnt;
+    }
+    __syncthreads();
+    for (int a = threadIdx.x; a < A; a += kSelThreads) {
+        const int e = ea[a];
+        int r = 0;
+        for (int b = 0; b < a; ++b) r += ea[b] == e;
+        wl_assign[start[e] + r] = a;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* x, const float* router_w, const float* bias, int T, int H, int E,
+                        int n_group, int topk_group, int top_k, int n_shared, float rsf, float* scores,
+                        int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, hipStream_t st) {
+    hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_select_kernel, dim3(1), dim3(kSelThreads), 0, st, scores, bias, T, E, n_group,
+                       topk_group, top_k, n_shared, rsf, topk_idx, topk_w, wl ? wl->n_active : nullptr,
+                       wl ? wl->expert_id : nullptr, wl ? wl->seg : nullptr, wl ? wl->assign : nullptr);
+    return hipGetLastError();
+}
+
+}  // namespace moedec

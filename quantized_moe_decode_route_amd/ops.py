@@ -1,0 +1,300 @@
+"""Python binding of libmoedec: argument marshalling only.
+
+Every function here checks that its torch tensors live on the GPU with the
+dtype and layout the C ABI (include/moedec.h) expects, passes their device
+pointers and the current HIP stream to the library, and raises MoedecError on
+a non-zero status.  All arithmetic runs in the library's kernels; there is no
+fallback: if libmoedec.so is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoedec.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moedec.h")
+
+MAX_TOKENS = 64
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "device error"}
+
+
+class MoedecError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class _Worklist(ctypes.Structure):
+    _fields_ = [("n_active", ctypes.c_void_p), ("expert_id", ctypes.c_void_p),
+                ("seg", ctypes.c_void_p), ("assign", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+
+_SIGS = {
+    "moedec_status_string": ([_I], ctypes.c_char_p),
+    "moedec_abi_version": ([], _I),
+    "moe_route_topk": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P], _I),
+    "moe_residual_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
+}
+for _b in ("q4", "q8", "q2"):
+    _SIGS[f"moe_expert_gate_up_silu_{_b}"] = ([_P, _P, _P, _I, _I, _P, _P], _I)
+    _SIGS[f"moe_expert_down_combine_{_b}"] = ([_P, _P, _P, _P, _I, _I, _P, _P], _I)
+    _SIGS[f"moe_pack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
+    _SIGS[f"moe_unpack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_moe_decode_route_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moedec.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:moe|moedec)_\w+)\s*\(", text)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoedecError(fn, status, lib().moedec_status_string(status).decode())
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+# ------------------------------------------------------------------- types
+
+@dataclass
+class Worklist:
+    """Batch union written by route_topk (device tensors, see moedec_worklist)."""
+    n_active: torch.Tensor   # int32 [1]
+    expert_id: torch.Tensor  # int32 [max_active]
+    seg: torch.Tensor        # int32 [max_active + 1]
+    assign: torch.Tensor     # int32 [T * (K + S)]
+
+    @staticmethod
+    def empty(T: int, top_k: int, n_experts: int, n_shared: int, device) -> "Worklist":
+        max_active = min(n_experts, T * top_k) + n_shared
+        z = dict(dtype=torch.int32, device=device)
+        return Worklist(torch.zeros(1, **z), torch.zeros(max_active, **z), torch.zeros(max_active + 1, **z),
+                        torch.zeros(T * (top_k + n_shared), **z))
+
+    def struct(self) -> _Worklist:
+        return _Worklist(_dev(self.n_active, torch.int32, "n_active"),
+                         _dev(self.expert_id, torch.int32, "expert_id"),
+                         _dev(self.seg, torch.int32, "seg"), _dev(self.assign, torch.int32, "assign"))
+
+
+@dataclass
+class Experts:
+    """One layer's experts as device tensors (see moedec_experts)."""
+    q_gate: torch.Tensor   # uint8 [(E+S), I, H*bits/8]
+    q_up: torch.Tensor     # uint8 [(E+S), I, H*bits/8]
+    q_down: torch.Tensor   # uint8 [(E+S), H, I*bits/8]
+    s_gate: torch.Tensor   # fp32 [(E+S), I]
+    s_up: torch.Tensor     # fp32 [(E+S), I]
+    s_down: torch.Tensor   # fp32 [(E+S), H]
+    n_experts: int
+    n_shared: int
+    bits: int
+
+    @property
+    def hidden(self) -> int:
+        return self.q_down.shape[1]
+
+    @property
+    def inter(self) -> int:
+        return self.q_gate.shape[1]
+
+    def struct(self) -> _Experts:
+        n = self.n_experts + self.n_shared
+        H, I, b = self.hidden, self.inter, self.bits
+        shapes = {"q_gate": (n, I, H * b // 8), "q_up": (n, I, H * b // 8), "q_down": (n, H, I * b // 8),
+                  "s_gate": (n, I), "s_up": (n, I), "s_down": (n, H)}
+        for k, shp in shapes.items():
+            if tuple(getattr(self, k).shape) != shp:
+                raise ValueError(f"{k} has shape {tuple(getattr(self, k).shape)}, expected {shp}")
+        return _Experts(H, I, self.n_experts, self.n_shared, b,
+                        _dev(self.q_gate, torch.uint8, "q_gate"), _dev(self.q_up, torch.uint8, "q_up"),
+                        _dev(self.q_down, torch.uint8, "q_down"), _dev(self.s_gate, torch.float32, "s_gate"),
+                        _dev(self.s_up, torch.float32, "s_up"), _dev(self.s_down, torch.float32, "s_down"))
+
+    @staticmethod
+    def from_layer(layer: dict, n_experts: int, n_shared: int, bits: int) -> "Experts":
+        return Experts(layer["q_gate"], layer["q_up"], layer["q_down"], layer["s_gate"], layer["s_up"],
+                       layer["s_down"], n_experts, n_shared, bits)
+
+
+@dataclass
+class Route:
+    scores: torch.Tensor     # fp32 [T, E]
+    topk_idx: torch.Tensor   # int32 [T, K]
+    topk_w: torch.Tensor     # fp32 [T, K]
+    worklist: Worklist
+
+
+# ------------------------------------------------------------------- calls
+
+def route_topk(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, *, n_group: int, topk_group: int,
+               top_k: int, n_shared: int, rsf: float, out: Route | None = None) -> Route:
+    """moe_route_topk: sigmoid scores, group-limited top-k, weights, worklist."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    if router_w.shape != (E, H) or bias.shape != (E,):
+        raise ValueError("router_w must be [E, H] and bias [E]")
+    if out is None:
+        dev = x.device
+        out = Route(torch.empty((T, E), dtype=torch.float32, device=dev),
+                    torch.empty((T, top_k), dtype=torch.int32, device=dev),
+                    torch.empty((T, top_k), dtype=torch.float32, device=dev),
+                    Worklist.empty(T, top_k, E, n_shared, dev))
+    wl = out.worklist.struct()
+    st = lib().moe_route_topk(_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"),
+                              _dev(bias, torch.float32, "bias"), T, H, E, n_group, topk_group, top_k, n_shared,
+                              float(rsf), _dev(out.scores, torch.float32, "scores"),
+                              _dev(out.topk_idx, torch.int32, "topk_idx"), _dev(out.topk_w, torch.float32, "topk_w"),
+                              ctypes.byref(wl), _stream(x))
+    _check("moe_route_topk", st)
+    return out
+
+
+def _suffix(bits: int) -> str:
+    if bits not in (4, 8, 2):
+        raise ValueError("bits must be 4, 8 or 2")
+    return f"q{bits}"
+
+
+def gate_up_silu(x: torch.Tensor, ex: Experts, wl: Worklist, top_k: int, out: torch.Tensor | None = None):
+    """moe_expert_gate_up_silu_q{bits}: h[a] = silu(Wg x_t) * (Wu x_t) per assignment a."""
+    T = x.shape[0]
+    A = T * (top_k + ex.n_shared)
+    if out is None:
+        out = torch.empty((A, ex.inter), dtype=torch.float32, device=x.device)
+    if out.shape != (A, ex.inter):
+        raise ValueError("h must be [T*(K+S), I]")
+    s_ex, s_wl = ex.struct(), wl.struct()
+    fn = getattr(lib(), f"moe_expert_gate_up_silu_{_suffix(ex.bits)}")
+    st = fn(_dev(x, torch.float32, "x"), ctypes.byref(s_ex), ctypes.byref(s_wl), T, top_k,
+            _dev(out, torch.float32, "h"), _stream(x))
+    _check(fn.__name__, st)
+    return out
+
+
+def down_combine(h: torch.Tensor, ex: Experts, wl: Worklist, topk_w: torch.Tensor, top_k: int,
+                 out: torch.Tensor | None = None):
+    """moe_expert_down_combine_q{bits}: y[t] = sum_k w[t,k] o(t,k) + sum_shared o."""
+    T = topk_w.shape[0]
+    if out is None:
+        out = torch.empty((T, ex.hidden), dtype=torch.float32, device=h.device)
+    if out.shape != (T, ex.hidden) or h.shape != (T * (top_k + ex.n_shared), ex.inter):
+        raise ValueError("shape mismatch between h, topk_w and y")
+    s_ex, s_wl = ex.struct(), wl.struct()
+    fn = getattr(lib(), f"moe_expert_down_combine_{_suffix(ex.bits)}")
+    st = fn(_dev(h, torch.float32, "h"), ctypes.byref(s_ex), ctypes.byref(s_wl),
+            _dev(topk_w, torch.float32, "topk_w"), T, top_k, _dev(out, torch.float32, "y"), _stream(h))
+    _check(fn.__name__, st)
+    return out
+
+
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_pack_q{bits}: int8 codes [rows, n] -> uint8 [rows, n*bits/8]."""
+    rows, n = codes.shape
+    if out is None:
+        out = torch.empty((rows, n * bits // 8), dtype=torch.uint8, device=codes.device)
+    fn = getattr(lib(), f"moe_pack_{_suffix(bits)}")
+    st = fn(_dev(codes, torch.int8, "codes"), _dev(out, torch.uint8, "packed"), rows, n, _stream(codes))
+    _check(fn.__name__, st)
+    return out
+
+
+def unpack(packed: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_unpack_q{bits}: uint8 [rows, nb] -> int8 codes [rows, nb*8/bits]."""
+    rows, nb = packed.shape
+    n = nb * 8 // bits
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.int8, device=packed.device)
+    fn = getattr(lib(), f"moe_unpack_{_suffix(bits)}")
+    st = fn(_dev(packed, torch.uint8, "packed"), _dev(out, torch.int8, "codes"), rows, n, _stream(packed))
+    _check(fn.__name__, st)
+    return out
+
+
+def residual_rmsnorm(x: torch.Tensor, y: torch.Tensor | None, xn: torch.Tensor, eps: float = 1e-6) -> None:
+    """moe_residual_rmsnorm: x += y (if given), xn = x / sqrt(mean(x^2) + eps)."""
+    T, H = x.shape
+    yp = _dev(y, torch.float32, "y") if y is not None else None
+    st = lib().moe_residual_rmsnorm(_dev(x, torch.float32, "x"), yp, _dev(xn, torch.float32, "xn"), T, H,
+                                    float(eps), _stream(x))
+    _check("moe_residual_rmsnorm", st)
+
+
+# ------------------------------------------------------------- a whole layer
+
+@dataclass
+class LayerBuffers:
+    """Every intermediate of one layer call, allocated once and reused."""
+    route: Route
+    h: torch.Tensor
+    y: torch.Tensor
+
+    @staticmethod
+    def allocate(T: int, H: int, I: int, E: int, top_k: int, n_shared: int, device) -> "LayerBuffers":
+        f = dict(dtype=torch.float32, device=device)
+        route = Route(torch.empty((T, E), **f), torch.empty((T, top_k), dtype=torch.int32, device=device),
+                      torch.empty((T, top_k), **f), Worklist.empty(T, top_k, E, n_shared, device))
+        return LayerBuffers(route, torch.empty((T * (top_k + n_shared), I), **f), torch.empty((T, H), **f))
+
+
+def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
+              topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None) -> LayerBuffers:
+    """route_topk -> gate_up_silu -> down_combine on one stream; returns the buffers (y in .y)."""
+    T = x.shape[0]
+    if buf is None:
+        buf = LayerBuffers.allocate(T, ex.hidden, ex.inter, ex.n_experts, top_k, ex.n_shared, x.device)
+    route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
+               rsf=rsf, out=buf.route)
+    gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)
+    down_combine(buf.h, ex, buf.route.worklist, buf.route.topk_w, top_k, out=buf.y)
+    return buf

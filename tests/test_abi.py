@@ -1,0 +1,128 @@
+"""The C-ABI library: it loads, exports every function include/moedec.h
+declares, and rejects bad arguments before anything reaches a device (these
+calls return from host-side validation, so they run without a GPU)."""
+import ctypes
+import os
+
+import pytest
+
+from quantized_moe_decode_route_amd import ops
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from quantized_moe_decode_route_amd import build
+        build.build()
+    return ops.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = ops.header_functions()
+    assert len(names) == 16
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(ops._Experts) == 72
+    assert ops._Experts.w_gate.offset == 24
+    assert ctypes.sizeof(ops._Worklist) == 32
+
+
+def test_status_strings(lib):
+    assert lib.moedec_status_string(0) == b"ok"
+    assert lib.moedec_status_string(1) == b"invalid argument"
+    assert lib.moedec_status_string(99) == b"unknown status"
+    assert lib.moedec_abi_version() == 1
+
+
+FAKE = 1 << 20       # an aligned, never-dereferenced address
+
+
+def _route(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, b=FAKE, T=1, H=256, E=16, G=4, TG=2, K=4, S=1, rsf=2.5,
+             scores=FAKE, idx=FAKE, wts=FAKE, wl=None)
+    a.update(kw)
+    return lib.moe_route_topk(a["x"], a["w"], a["b"], a["T"], a["H"], a["E"], a["G"], a["TG"], a["K"], a["S"],
+                              a["rsf"], a["scores"], a["idx"], a["wts"], a["wl"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(scores=None), 1), (dict(T=0), 1), (dict(H=250), 1), (dict(E=15), 1),
+    (dict(G=16), 1),                       # one expert per group
+    (dict(TG=5), 1), (dict(K=9), 1),       # more experts than two kept groups hold
+    (dict(K=0), 1), (dict(S=-1), 1), (dict(rsf=float("nan")), 1), (dict(x=FAKE + 4), 1),
+    (dict(T=65), 2), (dict(E=2048, G=8, TG=4), 2), (dict(K=33, E=256, G=1, TG=1), 2),
+])
+def test_route_rejects(lib, kw, status):
+    assert _route(lib, **kw) == status
+
+
+def _experts(**kw):
+    d = dict(hidden=256, inter=128, n_experts=16, n_shared=1, bits=4,
+             w_gate=FAKE, w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE)
+    d.update(kw)
+    return ops._Experts(**d)
+
+
+def _wl(**kw):
+    d = dict(n_active=FAKE, expert_id=FAKE, seg=FAKE, assign=FAKE)
+    d.update(kw)
+    return ops._Worklist(**d)
+
+
+@pytest.mark.parametrize("suffix,bits", [("q4", 4), ("q8", 8), ("q2", 2)])
+@pytest.mark.parametrize("kw,wkw,call,status", [
+    (dict(bits=0), {}, {}, 1),                     # bits do not match the suffix
+    (dict(w_up=None), {}, {}, 1),
+    ({}, dict(seg=None), {}, 1),
+    (dict(hidden=250), {}, {}, 1),                 # not a whole 16-byte group
+    (dict(inter=100), {}, {}, 1),
+    ({}, {}, dict(T=0), 1), ({}, {}, dict(K=0), 1), ({}, {}, dict(K=17), 1),
+    (dict(w_down=FAKE + 8), {}, {}, 1),            # misaligned codes
+    ({}, {}, dict(T=65), 2), (dict(hidden=32768), {}, {}, 2), (dict(n_shared=9), {}, {}, 2),
+])
+def test_expert_calls_reject(lib, suffix, bits, kw, wkw, call, status):
+    if "bits" not in kw:
+        kw = dict(kw, bits=bits)
+    else:
+        kw = dict(kw, bits=(bits + 1) if bits != 8 else 4)
+    ex, wl = _experts(**kw), _wl(**wkw)
+    T, K = call.get("T", 1), call.get("K", 4)
+    gu = getattr(lib, f"moe_expert_gate_up_silu_{suffix}")
+    dn = getattr(lib, f"moe_expert_down_combine_{suffix}")
+    assert gu(FAKE, ctypes.byref(ex), ctypes.byref(wl), T, K, FAKE, None) == status
+    assert dn(FAKE, ctypes.byref(ex), ctypes.byref(wl), FAKE, T, K, FAKE, None) == status
+
+
+def test_expert_calls_reject_null_structs(lib):
+    assert lib.moe_expert_gate_up_silu_q4(FAKE, None, ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
+    assert lib.moe_expert_down_combine_q4(FAKE, ctypes.byref(_experts()), None, FAKE, 1, 4, FAKE, None) == 1
+    assert lib.moe_expert_gate_up_silu_q4(None, ctypes.byref(_experts()), ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+def test_pack_validation(lib, bits):
+    pk = getattr(lib, f"moe_pack_q{bits}")
+    up = getattr(lib, f"moe_unpack_q{bits}")
+    assert pk(FAKE, FAKE, -1, 8, None) == 1
+    assert up(FAKE, FAKE, 2, -8, None) == 1
+    assert pk(None, FAKE, 2, 8, None) == 1
+    assert pk(None, None, 0, 8, None) == 0        # empty: nothing to do
+    assert up(None, None, 4, 0, None) == 0
+    if bits != 8:
+        assert pk(FAKE, FAKE, 2, 8 // bits + 1, None) == 1   # row of a partial byte
+
+
+def test_rmsnorm_validation(lib):
+    assert lib.moe_residual_rmsnorm(None, None, FAKE, 1, 8, 1e-6, None) == 1
+    assert lib.moe_residual_rmsnorm(FAKE, None, FAKE, 0, 8, 1e-6, None) == 1
+    assert lib.moe_residual_rmsnorm(FAKE, None, FAKE, 1, 8, -1.0, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 256)
+    with pytest.raises(ValueError):
+        ops._dev(x, torch.float32, "x")

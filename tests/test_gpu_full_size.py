@@ -1,0 +1,86 @@
+"""GPU parity at the full GLM-5.2 layer sizes, in the launch configuration the
+benchmark times: every expert of the layer resident on the device, the path
+run through the C ABI, and the oracle run on the host on the tokens it checks
+(every output of those tokens)."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+from quantized_moe_decode_route_amd import ops, synth
+
+from _parity import MARGIN, TOL, check_all, rel_err, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,steps", [("glm_t1", (0, 1)), ("glm_t3", (0,)), ("glm_t1_q8", (0,)),
+                                        ("glm_t1_q2", (0,))])
+def test_glm_layer(name, steps):
+    cfg = synth.CONFIGS[name]
+    say(f"case {name}: T={cfg.tokens} bits={cfg.bits} steps={steps}")
+    lay = synth.layer_device(cfg, 0, DEV)
+    rw, b = synth.router_weight(cfg, 0), synth.router_bias(cfg, 0)
+    for step in steps:
+        x = synth.batch_tokens(cfg, step)
+        g = run_layer(cfg, lay, x)
+        say(f"  step {step}: {g['n_active']} active experts")
+        check_all(cfg, g, x, rw, b, synth.expert_loader(cfg, 0))
+    del lay
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_glm_stack16_sampled_token():
+    """16 resident layers, 16 tokens, Zipf-skewed bias: the device runs the
+    whole batch through x <- x + MoE(rmsnorm(x)); the oracle follows one token
+    through all 16 layers (tokens are independent in this step)."""
+    cfg = synth.CONFIGS["glm_stack16"]
+    T, H = cfg.tokens, cfg.hidden
+    say(f"case glm_stack16: {cfg.layers} layers, T={T}")
+    layers = [synth.layer_device(cfg, l, DEV) for l in range(cfg.layers)]
+    x0 = synth.batch_tokens(cfg, 0)
+    x = torch.from_numpy(x0).to(DEV)
+    xn = torch.empty_like(x)
+    ops.residual_rmsnorm(x, None, xn)
+    idxs, ys, active = [], [], []
+    for l, lay in enumerate(layers):
+        ex = ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits)
+        buf = ops.moe_layer(xn, lay["router_w"], lay["bias"], ex, n_group=cfg.n_group,
+                            topk_group=cfg.topk_group, top_k=cfg.top_k, rsf=cfg.rsf)
+        ops.residual_rmsnorm(x, buf.y, xn)
+        idxs.append(buf.route.topk_idx.cpu().numpy())
+        active.append(int(buf.route.worklist.n_active.item()))
+        ys.append(x.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    say(f"  unique experts per layer: {active}")
+    del layers
+    _free()
+    t = 5
+    xo = x0[t:t + 1].astype(np.float64)
+    compared = 0
+    for l in range(cfg.layers):
+        rw, b = synth.router_weight(cfg, l), synth.router_bias(cfg, l)
+        xin = orc.rmsnorm(xo).astype(np.float32)
+        r = orc.moe_layer(xin, rw, b, synth.expert_loader(cfg, l), n_group=cfg.n_group,
+                          topk_group=cfg.topk_group, top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf,
+                          bits=cfg.bits)
+        if r.margin[0] < MARGIN:
+            say(f"  layer {l}: selection margin {r.margin[0]:.1e} below {MARGIN}; stop following token {t}")
+            break
+        assert sorted(idxs[l][t]) == sorted(r.idx[0])
+        xo = xo + r.y
+        e = rel_err(ys[l][t], xo[0])
+        say(f"  layer {l}: x err {e:.2e}")
+        assert e <= TOL
+        compared += 1
+    assert compared >= 8
