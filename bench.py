@@ -1,0 +1,251 @@
+"""Benchmark of the routed-MoE decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload glm_t1]
+
+A step is one pass of the whole path (route -> gate/up + SwiGLU -> down +
+combine) over one batch of synthetic tokens; the default workload is one
+GLM-5.2-shaped layer (hidden 6144, expert intermediate 2048, 256 routed experts
+in 8 groups, top-4 groups, top-8, one shared expert, int4 codes with fp32 row
+scales) decoding one token.  Several such layers are resident in HBM and the
+steps rotate over them and over a pool of 64 tokens, so no step finds the
+previous steps' weights in the 256 MB Infinity Cache; steps are replayed from
+HIP graphs.  Prints one JSON line.
+
+Bytes per step (the metric's count) = the unique selected experts' packed
+codes and row scales + the input and output activations; the router weight is
+excluded and reported apart.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) and tokens/s for one int4 256-expert MoE layer"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc", "experts.hip")
+
+
+def step_bytes(cfg, n_active: int) -> int:
+    return n_active * cfg.expert_bytes() + 2 * cfg.tokens * cfg.hidden * 4
+
+
+def gate_up_bytes(cfg, n_active: int) -> int:
+    """Algorithmic bytes of one gate/up launch: gate and up codes and scales of
+    the active experts, the activations read and h written."""
+    per = 2 * cfg.inter * (cfg.hidden * cfg.bits // 8 + 4)
+    return n_active * per + cfg.tokens * cfg.hidden * 4 + cfg.tokens * cfg.slots * cfg.inter * 4
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per gate/up launch measured with rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as orc
+    from quantized_moe_decode_route_amd import synth
+
+    layers = 4
+    data = {}
+    elapsed, nbytes, ntok, steps = 0.0, 0, 0, 0
+    with threadpool_limits(limits=1):
+        while steps < 64 and (elapsed < budget_s or steps == 0):
+            l = steps % layers
+            if l not in data:
+                data[l] = (synth.router_weight(cfg, l), synth.router_bias(cfg, l), {})
+            rw, b, cache = data[l]
+            x = synth.batch_tokens(cfg, steps)
+            # the layer is resident: fetch the experts this step needs before timing
+            s64 = orc.router_scores(x, rw)
+            idx, _ = orc.select_experts(s64.astype(np.float32), b, cfg.n_group, cfg.topk_group, cfg.top_k,
+                                        cfg.rsf)
+            need = set(idx.ravel().tolist()) | set(range(cfg.n_experts, cfg.n_experts + cfg.n_shared))
+            for e in need:
+                if e not in cache:
+                    cache[e] = synth.expert_arrays(cfg, l, e)
+            t0 = time.perf_counter()
+            r = orc.moe_layer(x, rw, b, cache.__getitem__, n_group=cfg.n_group, topk_group=cfg.topk_group,
+                              top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits)
+            elapsed += time.perf_counter() - t0
+            nbytes += step_bytes(cfg, len(r.worklist.expert_id))
+            ntok += cfg.tokens
+            steps += 1
+            if len(cache) > 40:
+                cache.clear()
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(ntok / elapsed, 4),
+            "sample": f"{steps} steps ({ntok} tokens) of {cfg.name} on {layers} rotating layers, "
+                      f"{elapsed:.1f} s of oracle time, 1 thread"}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="glm_t1")
+    ap.add_argument("--layers", type=int, default=4, help="resident layers the steps rotate over")
+    ap.add_argument("--graph-steps", type=int, default=8)
+    ap.add_argument("--kernel-steps", type=int, default=100, help="eager steps timing the gate/up kernel")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_moe_decode_route_amd import ops, synth
+
+    cfg = synth.CONFIGS[args.workload]
+    if cfg.layers != 1:
+        raise SystemExit("bench.py times single-layer workloads; the 16-layer stack is a parity case")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, T, G = args.layers, cfg.tokens, args.graph_steps
+    layers = [synth.layer_device(cfg, l, dev) for l in range(L)]
+    experts = [ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits) for lay in layers]
+    pool = torch.from_numpy(synth.token_pool(cfg)).to(dev)
+    n_pool = cfg.pool
+    period = int(np.lcm(L, n_pool))
+    kw = dict(n_group=cfg.n_group, topk_group=cfg.topk_group, top_k=cfg.top_k, rsf=cfg.rsf)
+    bufs = [ops.LayerBuffers.allocate(T, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared, dev)
+            for _ in range(L)]
+
+    def tokens(i):
+        b = i % n_pool
+        return pool[b * T:(b + 1) * T]
+
+    def step(i):
+        l = i % L
+        ops.moe_layer(tokens(i), layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], **kw)
+
+    # unique experts of every step of the period (routing is a function of (layer, token))
+    n_active = np.zeros(period, np.int64)
+    for i in range(period):
+        step(i)
+        torch.cuda.synchronize()
+        n_active[i] = int(bufs[i % L].route.worklist.n_active.item())
+    sbytes = np.array([step_bytes(cfg, int(n)) for n in n_active])
+
+    # graphs: one per block of G consecutive steps of the period, one per single step
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    blocks, singles = {}, {}
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            step(i)
+    stream.synchronize()
+    for i0 in range(0, period, G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(i0, i0 + G):
+                step(i)
+        blocks[i0] = g
+    for i in range(period):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(i)
+        singles[i] = g
+
+    def run(first, count):
+        i = first
+        while i < first + count:
+            p = i % period
+            if p % G == 0 and i + G <= first + count:
+                blocks[p].replay()
+                i += G
+            else:
+                singles[p].replay()
+                i += 1
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    first = args.warmup
+    t0 = time.perf_counter()
+    run(first, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx = (np.arange(first, first + args.steps) % period)
+    total_bytes = int(sbytes[idx].sum())
+    gbs = total_bytes / wall / 1e9
+    ms_per_step = wall / args.steps * 1e3
+    tok_s = args.steps * T / wall
+    print(f"[bench] {args.steps} steps in {wall * 1e3:.1f} ms: {ms_per_step * 1e3:.2f} us/step, "
+          f"{gbs:.0f} GB/s, {tok_s:.0f} tok/s", file=sys.stderr, flush=True)
+
+    # the dominant kernel (gate/up) timed live with HIP events on the launch stream,
+    # caches flushed before every step
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
+    kb = []
+    for k in range(args.kernel_steps):
+        i = first + args.steps + k
+        l = i % L
+        flush.fill_(float(k))
+        x = tokens(i)
+        ops.route_topk(x, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route, **kw)
+        ev0[k].record()
+        ops.gate_up_silu(x, experts[l], bufs[l].route.worklist, cfg.top_k, out=bufs[l].h)
+        ev1[k].record()
+        ops.down_combine(bufs[l].h, experts[l], bufs[l].route.worklist, bufs[l].route.topk_w, cfg.top_k,
+                         out=bufs[l].y)
+        kb.append(gate_up_bytes(cfg, int(n_active[i % period])))
+    torch.cuda.synchronize()
+    dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
+    achieved = float(np.mean(kb) / dur.mean() / 1e9)
+    traffic = traffic_from_profile(cfg.name)
+    roofline = {"bound": "hbm", "kernel": "gate_up_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "avg_us": round(float(dur.mean() * 1e6), 2),
+                "bytes_per_launch": int(np.mean(kb))}
+    print(f"[bench] gate_up avg {dur.mean() * 1e6:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    base = cpu_baseline(cfg, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "tokens_per_s": round(tok_s, 1),
+        "bytes_per_step": int(sbytes[idx].mean()), "router_bytes_per_step": cfg.n_experts * cfg.hidden * 4,
+        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "routed_experts": cfg.n_experts, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
+                   "top_k": cfg.top_k, "shared_experts": cfg.n_shared, "bits": cfg.bits,
+                   "resident_layers": L, "unique_experts_per_step": float(n_active[idx].mean())},
+        "roofline": roofline, "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moedec.h"
+#include "moedec.h"   // include/ is on the include path
 
 namespace moedec {
 
@@ -145,6 +145,9 @@ hipError_t launch_route(const float* x, const float* router_w, const float* bias
                         hipStream_t stream);
 
 hipError_t launch_gate_up(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t stream);
+hipError_t launch_gate_up_valu(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t stream);
+hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
+                            hipStream_t stream);
 
 hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                        hipStream_t stream);

@@ -1,0 +1,575 @@
+// Expert kernels on the vector ALUs: gate/up + SwiGLU, and down + weighted
+// combine, over row-scaled int8 / packed int4 / packed int2 codes (dequantised
+// on use).  The matrix-core kernels (experts_mfma.hip) are the default; these
+// serve the batches they do not take (more than 16 tokens for down).
+//
+// Both kernels are persistent: one workgroup of 8 waves per compute unit, each
+// taking an equal contiguous share of the work, so every selected expert's
+// packed rows are streamed exactly once per token batch (the batch union of
+// the worklist) and every CU streams the same number of bytes.  Rows are split
+// into 16-byte groups and the lanes of a lane group take consecutive groups,
+// so one wave-wide load covers a contiguous 1 KB.  Each wave keeps W such loads
+// in flight in a register ring while it decodes earlier ones.  The worklist is
+// copied to LDS first so no weight load waits behind a global lookup.
+// Activations (x for gate/up, h for down) are staged in LDS in a
+// group-transposed layout [token][column-in-group][group], so the lanes of a
+// wave read consecutive LDS words (no bank conflicts).
+#include "common.h"
+
+namespace moedec {
+
+constexpr int kPThreads = 512;
+constexpr int kPWaves = kPThreads / kWave;
+constexpr int kMaxActive = MOEDEC_MAX_EXPERTS + 8;
+constexpr int kNcMax = 4;                      // tokens per gate/up segment
+
+// Copy n_active, expert_id[] and seg[] of the worklist to LDS (whole workgroup).
+__device__ __forceinline__ int load_worklist(const ExpertArgs& a, int* eid, int* seg) {
+    __shared__ int n_s;
+    if (threadIdx.x == 0) n_s = *a.n_active;
+    __syncthreads();
+    const int n = n_s;
+    for (int j = threadIdx.x; j <= n; j += blockDim.x) {
+        if (j < n) eid[j] = a.expert_id[j];
+        seg[j] = a.seg[j];
+    }
+    __syncthreads();
+    return n;
+}
+
+// Largest j in [0, n) with v[j] <= q (v ascending, v[0] <= q).
+__device__ __forceinline__ int upper_index(const int* v, int n, int q) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (v[mid] <= q) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// cpre[j] = number of token chunks (of up to kNcMax) of experts 0..j-1, for
+// j in [0, n]; each thread scans a contiguous run of entries.
+__device__ void chunk_prefix(const int* seg, int n, int* cpre) {
+    __shared__ int wtot[kPWaves];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int per = (n + 1 + kPThreads - 1) / kPThreads;
+    const int j0 = threadIdx.x * per, j1 = min(j0 + per, n);
+    int local = 0;
+    for (int j = j0; j < j1; ++j) local += (seg[j + 1] - seg[j] + kNcMax - 1) / kNcMax;
+    int inc = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += u;
+    }
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    int run = inc - local;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+    for (int j = j0; j < min(j0 + per, n + 1); ++j) {
+        cpre[j] = run;
+        if (j < n) run += (seg[j + 1] - seg[j] + kNcMax - 1) / kNcMax;
+    }
+    __syncthreads();
+}
+
+// Stage n token rows of x into LDS slots: xs[(slot*CW + c)*P + p] and the
+// per-group sums xsum[slot*P + p].
+template <int BITS>
+__device__ __forceinline__ void stage_tokens(const float* __restrict__ x, int H, const int* tok, const int* slot,
+                                             int n, float* xs, float* xsum) {
+    constexpr int CW = 16 * Codec<BITS>::F;
+    const int P = (H * BITS / 8) >> 4;
+    for (int idx = threadIdx.x; idx < n * P; idx += blockDim.x) {
+        const int k = idx / P, p = idx - k * P;
+        const int sl = slot ? slot[k] : k;
+        const int t = tok ? tok[k] : k;
+        const float4* s4 = reinterpret_cast<const float4*>(x + (size_t)t * H + p * CW);
+        float sum = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < CW / 4; ++c4) {
+            const float4 v = s4[c4];
+            xs[(sl * CW + 4 * c4 + 0) * P + p] = v.x;
+            xs[(sl * CW + 4 * c4 + 1) * P + p] = v.y;
+            xs[(sl * CW + 4 * c4 + 2) * P + p] = v.z;
+            xs[(sl * CW + 4 * c4 + 3) * P + p] = v.w;
+            sum += (v.x + v.y) + (v.z + v.w);
+        }
+        xsum[sl * P + p] = sum;
+    }
+}
+
+// ------------------------------------------------------------------ gate / up
+//
+// Work units are (segment, row) with segment = (active expert j, chunk of up
+// to kNcMax of its tokens); segments are enumerated expert-ascending and each
+// workgroup takes an equal contiguous range of the units.  When the batch's
+// tokens fit in LDS they are staged once at kernel start (slot = token index);
+// otherwise each segment stages its own tokens.  h[a][r] = silu(g) * v.
+
+template <int BITS, int NC, int LPR, int W>
+__device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, const float* xs,
+                                             const float* xsum, const int* slot, const int* asg, int e,
+                                             int rlo, int rhi, int lpr) {
+    using C = Codec<BITS>;
+    constexpr int F = C::F;
+    constexpr int CW = 16 * F;
+    const int H = a.H, I = a.I;
+    const int row_bytes = H * BITS / 8;
+    const int P = row_bytes >> 4;
+    const int spl = P / lpr;
+    const int gpw = kWave / lpr;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int grp = lane / lpr, li = lane - grp * lpr;
+    const int rows_per_iter = kPWaves * gpw;
+    const int n_iter = (rhi - rlo + rows_per_iter - 1) / rows_per_iter;
+    const int n_items = n_iter * spl;
+    const uint8_t* gb = a.w_gate + (size_t)e * I * row_bytes;
+    const uint8_t* ub = a.w_up + (size_t)e * I * row_bytes;
+    const float* sg = a.s_gate + (size_t)e * I;
+    const float* su = a.s_up + (size_t)e * I;
+    int sl[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) sl[k] = slot[k];
+
+    auto row_of = [&](int it) { return rlo + it * rows_per_iter + wave * gpw + grp; };
+    uint4 bg[W], bu[W];
+    float bsg[W], bsu[W];
+    auto issue = [&](int i, int w) {
+        const int it = i / spl, s = i - it * spl;
+        const int r = min(row_of(it), rhi - 1);
+        const size_t off = (size_t)r * row_bytes + (li + s * lpr) * 16;
+        bg[w] = ld16(gb + off);
+        bu[w] = ld16(ub + off);
+        bsg[w] = sg[r];
+        bsu[w] = su[r];
+    };
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        if (w < n_items) issue(w, w);
+
+    // this lane's share of 2^(BITS-1) * sum(x) over its groups
+    float xoff[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        float v = 0.f;
+        for (int s = 0; s < spl; ++s) v += xsum[sl[k] * P + li + s * lpr];
+        xoff[k] = C::kOffset * v;
+    }
+
+    float ag[NC][F], au[NC][F];
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+#pragma unroll
+        for (int f = 0; f < F; ++f) ag[k][f] = au[k][f] = 0.f;
+
+    for (int base = 0; base < n_items; base += W) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int i = base + w;
+            if (i >= n_items) break;
+            const uint4 cg = bg[w], cu = bu[w];
+            const float csg = bsg[w], csu = bsu[w];
+            if (i + W < n_items) issue(i + W, w);
+            const int it = i / spl, s = i - it * spl;
+            const int p = li + s * lpr;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float xv[NC][4 * F];
+#pragma unroll
+                for (int k = 0; k < NC; ++k)
+#pragma unroll
+                    for (int m = 0; m < 4 * F; ++m) xv[k][m] = xs[(sl[k] * CW + 4 * d * F + m) * P + p];
+                const uint32_t wgd = (d == 0 ? cg.x : d == 1 ? cg.y : d == 2 ? cg.z : cg.w) ^ C::kFlip;
+                const uint32_t wud = (d == 0 ? cu.x : d == 1 ? cu.y : d == 2 ? cu.z : cu.w) ^ C::kFlip;
+#pragma unroll
+                for (int f = 0; f < F; ++f) {
+                    const uint32_t mg = wgd & C::mask(f), mu = wud & C::mask(f);
+                    const float g0 = ubyte_f<0>(mg), g1 = ubyte_f<1>(mg), g2 = ubyte_f<2>(mg), g3 = ubyte_f<3>(mg);
+                    const float u0 = ubyte_f<0>(mu), u1 = ubyte_f<1>(mu), u2 = ubyte_f<2>(mu), u3 = ubyte_f<3>(mu);
+#pragma unroll
+                    for (int k = 0; k < NC; ++k) {
+                        ag[k][f] = fmaf(g0, xv[k][0 * F + f], ag[k][f]);
+                        ag[k][f] = fmaf(g1, xv[k][1 * F + f], ag[k][f]);
+                        ag[k][f] = fmaf(g2, xv[k][2 * F + f], ag[k][f]);
+                        ag[k][f] = fmaf(g3, xv[k][3 * F + f], ag[k][f]);
+                        au[k][f] = fmaf(u0, xv[k][0 * F + f], au[k][f]);
+                        au[k][f] = fmaf(u1, xv[k][1 * F + f], au[k][f]);
+                        au[k][f] = fmaf(u2, xv[k][2 * F + f], au[k][f]);
+                        au[k][f] = fmaf(u3, xv[k][3 * F + f], au[k][f]);
+                    }
+                }
+            }
+            if (s == spl - 1) {
+                const int r = row_of(it);
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    float g = -xoff[k], v = -xoff[k];
+#pragma unroll
+                    for (int f = 0; f < F; ++f) {
+                        g += C::scale(f) * ag[k][f];
+                        v += C::scale(f) * au[k][f];
+                        ag[k][f] = au[k][f] = 0.f;
+                    }
+                    if constexpr (LPR > 0) {
+                        g = group_sum<LPR>(g);
+                        v = group_sum<LPR>(v);
+                    } else {
+                        g = group_sum_rt(g, lpr);
+                        v = group_sum_rt(v, lpr);
+                    }
+                    if (li == 0 && r < rhi) {
+                        g *= csg;
+                        v *= csu;
+                        h[(size_t)asg[k] * I + r] = g / (1.0f + __expf(-g)) * v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BITS, int LPR, int W>
+__global__ __launch_bounds__(kPThreads) void gate_up_kernel(const float* __restrict__ x, const ExpertArgs a,
+                                                            float* __restrict__ h, int lpr_rt, int ns) {
+    using C = Codec<BITS>;
+    constexpr int CW = 16 * C::F;
+    extern __shared__ float lds[];
+    __shared__ int eid[kMaxActive];
+    __shared__ int seg[kMaxActive + 1];
+    __shared__ int cpre[kMaxActive + 1];
+    __shared__ int tok_s[kNcMax], slot_s[kNcMax], asg_s[kNcMax], staged_s[kNcMax];
+
+    const int H = a.H, I = a.I, T = a.T;
+    const int P = (H * BITS / 8) >> 4;
+    const int lpr = LPR > 0 ? LPR : lpr_rt;
+    float* xs = lds;                            // [ns][CW][P]
+    float* xsum = lds + (size_t)ns * CW * P;    // [ns][P]
+    const bool stage_all = T <= ns;
+
+    if (threadIdx.x < kNcMax) staged_s[threadIdx.x] = -1;
+    if (stage_all) stage_tokens<BITS>(x, H, nullptr, nullptr, T, xs, xsum);   // slot = token
+    const int n_act = load_worklist(a, eid, seg);
+    chunk_prefix(seg, n_act, cpre);
+
+    const int n_seg = cpre[n_act];
+    const long long n_units = (long long)n_seg * I;
+    const long long u0 = n_units * blockIdx.x / gridDim.x;
+    const long long u1 = n_units * (blockIdx.x + 1) / gridDim.x;
+    if (u0 >= u1) return;
+
+    for (int sidx = (int)(u0 / I); (long long)sidx * I < u1; ++sidx) {
+        const int rlo = (int)max(u0 - (long long)sidx * I, 0LL);
+        const int rhi = (int)min(u1 - (long long)sidx * I, (long long)I);
+        const int j = upper_index(cpre, n_act, sidx);
+        const int c = sidx - cpre[j];
+        const int e = eid[j];
+        const int first = seg[j] + c * kNcMax;
+        const int nc = min(kNcMax, seg[j + 1] - first);
+        __syncthreads();   // readers of the previous segment's tokens are done
+        if ((int)threadIdx.x < nc) {
+            const int as = a.assign[first + threadIdx.x];
+            asg_s[threadIdx.x] = as;
+            tok_s[threadIdx.x] = as / a.slots;
+            slot_s[threadIdx.x] = stage_all ? as / a.slots : (int)threadIdx.x;
+        }
+        __syncthreads();
+        if (!stage_all) {
+            bool same = true;
+            for (int k = 0; k < nc; ++k) same = same && staged_s[k] == tok_s[k];
+            if (!same) {
+                stage_tokens<BITS>(x, H, tok_s, slot_s, nc, xs, xsum);
+                __syncthreads();
+                if (threadIdx.x < kNcMax) staged_s[threadIdx.x] = (int)threadIdx.x < nc ? tok_s[threadIdx.x] : -1;
+                __syncthreads();
+            }
+        }
+        switch (nc) {
+            case 1: gate_up_rows<BITS, 1, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
+            case 2: gate_up_rows<BITS, 2, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
+            case 3: gate_up_rows<BITS, 3, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
+            default: gate_up_rows<BITS, 4, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
+        }
+    }
+}
+
+// ------------------------------------------------------------ down + combine
+//
+// Each workgroup owns a contiguous block of output rows for the whole batch.
+// It walks the worklist (experts ascending) in chunks of up to `qc`
+// assignments, stages those assignments' h (pre-multiplied by their routing
+// weight) in LDS, and adds every expert's contribution to its rows in a fixed
+// order, so the sum needs no atomics and is deterministic.  DEFER (one
+// token): lanes accumulate over all experts of a row before one reduction;
+// otherwise each (row, assignment) partial is reduced and added to the row's
+// per-token accumulator in LDS by the row's owning lane.
+
+template <int BITS, bool DEFER, int LPR, int W>
+__global__ __launch_bounds__(kPThreads) void down_kernel(const float* __restrict__ h,
+                                                         const float* __restrict__ topk_w, const ExpertArgs a,
+                                                         float* __restrict__ y, int lpr_rt, int qc, int rows_per_wg) {
+    using C = Codec<BITS>;
+    constexpr int F = C::F;
+    constexpr int CW = 16 * F;
+    extern __shared__ float lds[];
+    __shared__ int eid[kMaxActive];
+    __shared__ int seg[kMaxActive + 1];
+
+    const int H = a.H, I = a.I, T = a.T, K = a.top_k, slots = a.slots;
+    const int row_bytes = I * BITS / 8;
+    const int P = row_bytes >> 4;
+    const int lpr = LPR > 0 ? LPR : lpr_rt;
+    const int spl = P / lpr;
+    const int gpw = kWave / lpr;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int grp = lane / lpr, li = lane - grp * lpr;
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int r1 = min(r0 + rows_per_wg, H);
+    if (r0 >= r1) return;
+    const int nrows = r1 - r0;
+    const int rows_per_iter = kPWaves * gpw;
+    const int n_iter = (nrows + rows_per_iter - 1) / rows_per_iter;
+
+    float* hs = lds;                          // [qc][CW][P]
+    float* hsum = hs + (size_t)qc * CW * P;   // [qc][P]
+    float* yacc = hsum + (size_t)qc * P;      // [rows_per_wg][T]
+    int* qtok = reinterpret_cast<int*>(yacc + (size_t)rows_per_wg * T);  // [qc]
+
+    for (int i = threadIdx.x; i < rows_per_wg * T; i += kPThreads) yacc[i] = 0.f;
+    const int n_act = load_worklist(a, eid, seg);
+    const int A = seg[n_act];
+    const uint8_t* wd_base = a.w_down + (size_t)r0 * row_bytes;
+
+    for (int q0 = 0; q0 < A; q0 += qc) {
+        const int q1 = min(A, q0 + qc);
+        const int nq = q1 - q0;
+        const int j_first = upper_index(seg, n_act, q0);
+        const int j_last = upper_index(seg, n_act, q1 - 1);
+        const int ipr = (j_last - j_first + 1) * spl;          // items per row iteration
+        const int n_items = n_iter * ipr;
+
+        auto row_of = [&](int it) { return it * rows_per_iter + wave * gpw + grp; };   // relative to r0
+        uint4 buf[W];
+        float bsd[W];
+        auto issue = [&](int i, int w) {
+            const int it = i / ipr, rem = i - it * ipr;
+            const int jq = rem / spl, s = rem - jq * spl;
+            const int rl = min(row_of(it), nrows - 1);
+            const int ex = eid[j_first + jq];
+            buf[w] = ld16(wd_base + ((size_t)ex * H + rl) * row_bytes + (li + s * lpr) * 16);
+            bsd[w] = a.s_down[(size_t)ex * H + r0 + rl];
+        };
+        // weights first: these loads fly while h is staged
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (w < n_items) issue(w, w);
+
+        __syncthreads();   // previous chunk's readers are done with hs
+        for (int ql = threadIdx.x; ql < nq; ql += kPThreads) qtok[ql] = a.assign[q0 + ql] / slots;
+        for (int idx = threadIdx.x; idx < nq * P; idx += kPThreads) {
+            const int ql = idx / P, p = idx - ql * P;
+            const int as = a.assign[q0 + ql];
+            const int t = as / slots, slot = as - t * slots;
+            const float wq = slot < K ? topk_w[t * K + slot] : 1.0f;
+            const float4* s4 = reinterpret_cast<const float4*>(h + (size_t)as * I + p * CW);
+            float sum = 0.f;
+#pragma unroll
+            for (int c4 = 0; c4 < CW / 4; ++c4) {
+                const float4 v = s4[c4];
+                const float v0 = wq * v.x, v1 = wq * v.y, v2 = wq * v.z, v3 = wq * v.w;
+                hs[(ql * CW + 4 * c4 + 0) * P + p] = v0;
+                hs[(ql * CW + 4 * c4 + 1) * P + p] = v1;
+                hs[(ql * CW + 4 * c4 + 2) * P + p] = v2;
+                hs[(ql * CW + 4 * c4 + 3) * P + p] = v3;
+                sum += (v0 + v1) + (v2 + v3);
+            }
+            hsum[ql * P + p] = sum;
+        }
+        __syncthreads();
+
+        float acc = 0.f;
+        for (int base = 0; base < n_items; base += W) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const int i = base + w;
+                if (i >= n_items) break;
+                const uint4 cq = buf[w];
+                const float sd = bsd[w];
+                if (i + W < n_items) issue(i + W, w);
+                const int it = i / ipr, rem = i - it * ipr;
+                const int jq = rem / spl, s = rem - jq * spl;
+                const int jj = j_first + jq;
+                const int rl = row_of(it);
+                const int p = li + s * lpr;
+                const int qa = max(seg[jj], q0) - q0, qb = min(seg[jj + 1], q1) - q0;
+                for (int ql = qa; ql < qb; ++ql) {
+                    float pr[F];
+#pragma unroll
+                    for (int f = 0; f < F; ++f) pr[f] = 0.f;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        float hv[4 * F];
+#pragma unroll
+                        for (int m = 0; m < 4 * F; ++m) hv[m] = hs[(ql * CW + 4 * d * F + m) * P + p];
+                        const uint32_t wdw = (d == 0 ? cq.x : d == 1 ? cq.y : d == 2 ? cq.z : cq.w) ^ C::kFlip;
+#pragma unroll
+                        for (int f = 0; f < F; ++f) {
+                            const uint32_t m = wdw & C::mask(f);
+                            pr[f] = fmaf(ubyte_f<0>(m), hv[0 * F + f], pr[f]);
+                            pr[f] = fmaf(ubyte_f<1>(m), hv[1 * F + f], pr[f]);
+                            pr[f] = fmaf(ubyte_f<2>(m), hv[2 * F + f], pr[f]);
+                            pr[f] = fmaf(ubyte_f<3>(m), hv[3 * F + f], pr[f]);
+                        }
+                    }
+                    float v = -C::kOffset * hsum[ql * P + p];
+#pragma unroll
+                    for (int f = 0; f < F; ++f) v += C::scale(f) * pr[f];
+                    if constexpr (DEFER) {
+                        acc = fmaf(sd, v, acc);
+                    } else {
+                        if constexpr (LPR > 0) v = group_sum<LPR>(v);
+                        else v = group_sum_rt(v, lpr);
+                        if (li == 0 && rl < nrows) yacc[rl * T + qtok[ql]] += sd * v;
+                    }
+                }
+                if constexpr (DEFER) {
+                    if (rem == ipr - 1) {
+                        float v = acc;
+                        acc = 0.f;
+                        if constexpr (LPR > 0) v = group_sum<LPR>(v);
+                        else v = group_sum_rt(v, lpr);
+                        if (li == 0 && rl < nrows) yacc[rl * T] += v;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows * T; i += kPThreads) {
+        const int t = i / nrows, rl = i - t * nrows;
+        y[(size_t)t * H + r0 + rl] = yacc[rl * T + t];
+    }
+}
+
+// --------------------------------------------------------------------- launch
+
+namespace {
+
+constexpr int kGuW = 4;   // gate/up items in flight per wave (2 loads each)
+constexpr int kDnW = 8;   // down items in flight per wave
+constexpr size_t kLdsMax = 160 * 1024;
+// Static LDS of the persistent kernels (worklist copies) plus headroom.
+constexpr size_t kStaticLds = 16 * 1024;
+// Dynamic LDS a persistent workgroup asks for at least, so that no two of
+// them share a compute unit.
+constexpr size_t kLdsOnePerCu = 84 * 1024;
+
+// Lanes sharing one row: the largest power of two dividing the row's group
+// count, at most a wave; each lane then takes P / lanes groups.
+int lanes_per_row(int P) {
+    const int pow2 = P & (-P);
+    return pow2 >= kWave ? kWave : pow2;
+}
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <typename Kern>
+hipError_t allow_lds(Kern k, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+template <int BITS>
+hipError_t gate_up_bits(const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
+    constexpr int CW = 16 * Codec<BITS>::F;
+    const int P = (a.H * BITS / 8) / 16;
+    const int lpr = lanes_per_row(P);
+    const size_t per_tok = (size_t)(CW * P + P) * sizeof(float);
+    int fit = (int)((kLdsMax - kStaticLds) / per_tok);     // token rows LDS can hold
+    if (fit < kNcMax) return hipErrorInvalidValue;
+    const int ns = a.T <= fit ? a.T : kNcMax;              // all tokens once, else one segment's
+    size_t lds = ns * per_tok;
+    if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
+    const dim3 grid(cu_count());
+#define MOEDEC_GU(L)                                                              \
+    do {                                                                          \
+        auto k = gate_up_kernel<BITS, L, kGuW>;                                     \
+        hipError_t err = allow_lds(k, lds);                                       \
+        if (err != hipSuccess) return err;                                        \
+        hipLaunchKernelGGL(k, grid, dim3(kPThreads), lds, st, x, a, h, lpr, ns); \
+    } while (0)
+    if (lpr == kWave) MOEDEC_GU(kWave);
+    else MOEDEC_GU(0);
+#undef MOEDEC_GU
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t down_bits(const float* h, const float* topk_w, const ExpertArgs& a, float* y, hipStream_t st) {
+    constexpr int CW = 16 * Codec<BITS>::F;
+    const int P = (a.I * BITS / 8) / 16;
+    const int lpr = lanes_per_row(P);
+    const int n_wg = cu_count();
+    const int rows = (a.H + n_wg - 1) / n_wg;
+    const int A = a.T * a.slots;
+    const size_t fixed = (size_t)rows * a.T * sizeof(float);
+    const size_t per_q = (size_t)(CW * P + P) * sizeof(float) + sizeof(int);
+    int qc = (int)((kLdsMax - kStaticLds - fixed) / per_q);
+    if (qc < 1) return hipErrorInvalidValue;
+    if (qc > A) qc = A;
+    size_t lds = fixed + (size_t)qc * per_q;
+    if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
+    const dim3 grid((a.H + rows - 1) / rows);
+    const bool defer = a.T == 1;
+#define MOEDEC_DOWN(DEF, L)                                                                     \
+    do {                                                                                        \
+        auto k = down_kernel<BITS, DEF, L, kDnW>;                                                 \
+        hipError_t err = allow_lds(k, lds);                                                     \
+        if (err != hipSuccess) return err;                                                      \
+        hipLaunchKernelGGL(k, grid, dim3(kPThreads), lds, st, h, topk_w, a, y, lpr, qc, rows); \
+    } while (0)
+    if (lpr == kWave) {
+        if (defer) MOEDEC_DOWN(true, kWave);
+        else MOEDEC_DOWN(false, kWave);
+    } else {
+        if (defer) MOEDEC_DOWN(true, 0);
+        else MOEDEC_DOWN(false, 0);
+    }
+#undef MOEDEC_DOWN
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_valu(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
+    switch (bits) {
+        case 4: return gate_up_bits<4>(x, a, h, st);
+        case 8: return gate_up_bits<8>(x, a, h, st);
+        case 2: return gate_up_bits<2>(x, a, h, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
+                            hipStream_t st) {
+    switch (bits) {
+        case 4: return down_bits<4>(h, topk_w, a, y, st);
+        case 8: return down_bits<8>(h, topk_w, a, y, st);
+        case 2: return down_bits<2>(h, topk_w, a, y, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moedec

@@ -7,11 +7,14 @@
 // group-score rule (top-2 sum), the use of the corrected score for selection
 // only and the tie-breaking (lower index) are this library's reading.
 //
-// Kernel 1 (router_gemv): one workgroup per expert row streams the fp32 router
-// row once per token with 16-byte loads and writes s = sigmoid(W_r[e] . x_t).
+// Kernel 1 (router_gemv): one workgroup per expert row; every thread issues all
+// of its 16-byte loads of the row before using them, then the row is dotted
+// with each token and s = sigmoid(W_r[e] . x_t) is written.
 // Kernel 2 (route_select): one workgroup; each wave routes one token at a time
-// (group top-2 sums, topk_group rounds of a wave arg-max over groups, top_k
-// rounds over the kept experts, weights), then the workgroup builds the
+// with the token's scores in registers (a lane holds a contiguous run of
+// experts): group top-2 sums by a lane butterfly, topk_group rounds of a wave
+// arg-max over groups, top_k rounds over the kept experts, weights from the
+// winners' scores passed by lane shuffles; then the workgroup builds the
 // expert-ascending worklist with a counting sort.
 #include "common.h"
 
@@ -20,9 +23,10 @@ namespace moedec {
 namespace {
 
 constexpr int kGemvThreads = 256;
+constexpr int kGemvMaxF4 = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 per thread
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kMaxEPL = MOEDEC_MAX_EXPERTS / kWave;   // experts per lane
+constexpr int kMaxEPL = MOEDEC_MAX_EXPERTS / kWave;              // experts per lane
 
 __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* __restrict__ x,
                                                                    const float* __restrict__ W, int T, int H,
@@ -32,12 +36,22 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const float4* w4 = reinterpret_cast<const float4*>(W + (size_t)e * H);
     const int n4 = H >> 2;
+    float4 wr[kGemvMaxF4];
+#pragma unroll
+    for (int k = 0; k < kGemvMaxF4; ++k) {
+        const int i = threadIdx.x + k * kGemvThreads;
+        wr[k] = i < n4 ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     for (int t = 0; t < T; ++t) {
         const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * H);
         float acc = 0.f;
-        for (int i = threadIdx.x; i < n4; i += kGemvThreads) {
-            const float4 w = w4[i], v = x4[i];
-            acc += (w.x * v.x + w.y * v.y) + (w.z * v.z + w.w * v.w);
+#pragma unroll
+        for (int k = 0; k < kGemvMaxF4; ++k) {
+            const int i = threadIdx.x + k * kGemvThreads;
+            if (i < n4) {
+                const float4 v = x4[i];
+                acc += (wr[k].x * v.x + wr[k].y * v.y) + (wr[k].z * v.z + wr[k].w * v.w);
+            }
         }
         acc = group_sum<kWave>(acc);
         if (lane == 0) red[t][wave] = acc;
@@ -59,6 +73,13 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
         const int j = __shfl_xor(i, off, kWave);
         if (beats(u, j, v, i)) { v = u; i = j; }
     }
+}
+
+// Merge the top-2 pair (b1 >= b2) into (m1 >= m2).
+__device__ __forceinline__ void top2_merge(float& m1, float& m2, float b1, float b2) {
+    const float lo = fminf(m1, b1);
+    m1 = fmaxf(m1, b1);
+    m2 = fmaxf(lo, fmaxf(m2, b2));
 }
 
 // Exclusive scan of `v` over the workgroup; returns the prefix, writes the total.
@@ -97,75 +118,88 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int per = E / n_group;
     const int epl = (E + kWave - 1) / kWave;
+    const int lpg = per / epl;            // lanes per group on the butterfly path
+    const bool butterfly = (per % epl == 0) && ((lpg & (lpg - 1)) == 0) && lpg <= kWave;
+    const int e0 = lane * epl;            // this lane's experts: e0 .. e0 + epl - 1
 
     for (int t = wave; t < T; t += kSelWaves) {
         const float* st = scores + (size_t)t * E;
-        float cand[kMaxEPL];
+        float sv[kMaxEPL], cv[kMaxEPL];
 #pragma unroll
         for (int i = 0; i < kMaxEPL; ++i) {
-            const int e = lane + i * kWave;
-            cand[i] = -INFINITY;
-            if (i < epl && e < E) {
-                const float c = st[e] + bias[e];
-                cand[i] = c;
-                cs[wave][e] = c;
-            }
+            const int e = e0 + i;
+            const bool ok = i < epl && e < E;
+            sv[i] = ok ? st[e] : 0.f;
+            cv[i] = ok ? sv[i] + bias[e] : -INFINITY;
         }
-        __threadfence_block();   // this wave's LDS writes before its lanes read each other's
-        // group score: largest plus second largest corrected score in the group
+        // group score: largest plus second largest corrected score of the group
         float gs = -INFINITY;
-        if (lane < n_group) {
+        int gid = 0x7fffffff;
+        if (butterfly) {
             float m1 = -INFINITY, m2 = -INFINITY;
-            for (int k = 0; k < per; ++k) {
-                const float c = cs[wave][lane * per + k];
-                if (c > m1) { m2 = m1; m1 = c; }
-                else if (c > m2) { m2 = c; }
+#pragma unroll
+            for (int i = 0; i < kMaxEPL; ++i) top2_merge(m1, m2, cv[i], -INFINITY);
+            for (int off = 1; off < lpg; off <<= 1) {
+                const float b1 = __shfl_xor(m1, off, kWave), b2 = __shfl_xor(m2, off, kWave);
+                top2_merge(m1, m2, b1, b2);
             }
-            gs = m1 + m2;
+            if (e0 < E && (lane % lpg) == 0) {
+                gs = m1 + m2;
+                gid = e0 / per;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMaxEPL; ++i)
+                if (i < epl && e0 + i < E) cs[wave][e0 + i] = cv[i];
+            __threadfence_block();
+            if (lane < n_group) {
+                float m1 = -INFINITY, m2 = -INFINITY;
+                for (int k = 0; k < per; ++k) top2_merge(m1, m2, cs[wave][lane * per + k], -INFINITY);
+                gs = m1 + m2;
+                gid = lane;
+            }
         }
-        // keep topk_group groups
+        // keep topk_group groups (ties: lower group)
         uint64_t kept = 0;
         for (int r = 0; r < topk_group; ++r) {
             float v = gs;
-            int g = lane < n_group ? lane : 0x7fffffff;
+            int g = gid;
             wave_argmax(v, g);
             kept |= 1ull << g;
-            if (lane == g) gs = -INFINITY;
+            if (gid == g) gs = -INFINITY;
         }
-        // candidates outside the kept groups drop out
 #pragma unroll
         for (int i = 0; i < kMaxEPL; ++i) {
-            const int e = lane + i * kWave;
-            if (i < epl && e < E && !((kept >> (e / per)) & 1ull)) cand[i] = -INFINITY;
+            const int e = e0 + i;
+            if (i < epl && e < E && !((kept >> (e / per)) & 1ull)) cv[i] = -INFINITY;
         }
-        // top_k rounds of an arg-max over (c, -index)
-        int mine = -1;
+        // top_k rounds of an arg-max over (c, -index); weights from unbiased scores
+        int mine = 0;
+        float mine_s = 0.f, total = 0.f;
         for (int k = 0; k < top_k; ++k) {
             float v = -INFINITY;
             int ie = 0x7fffffff;
 #pragma unroll
-            for (int i = 0; i < kMaxEPL; ++i) {
-                const int e = lane + i * kWave;
-                if (i < epl && e < E && beats(cand[i], e, v, ie)) { v = cand[i]; ie = e; }
-            }
+            for (int i = 0; i < kMaxEPL; ++i)
+                if (i < epl && beats(cv[i], e0 + i, v, ie)) { v = cv[i]; ie = e0 + i; }
             wave_argmax(v, ie);
-            if (lane == k) mine = ie;
-            if ((ie & (kWave - 1)) == lane) {
+            const int owner = ie / epl, slot = ie - owner * epl;
+            float s_here = 0.f;
+#pragma unroll
+            for (int i = 0; i < kMaxEPL; ++i)
+                if (i == slot) s_here = sv[i];
+            const float s_win = __shfl(s_here, owner, kWave);
+            if (lane == owner) {
 #pragma unroll
                 for (int i = 0; i < kMaxEPL; ++i)
-                    if (i == (ie >> 6)) cand[i] = -INFINITY;
+                    if (i == slot) cv[i] = -INFINITY;
             }
-        }
-        // weights: unbiased scores renormalised in slot order, times rsf
-        float total = 0.f;
-        for (int k = 0; k < top_k; ++k) {
-            const int ek = __shfl(mine, k, kWave);
-            total += st[ek];
+            total += s_win;                      // slot order
+            if (lane == k) { mine = ie; mine_s = s_win; }
         }
         if (lane < top_k) {
-            const float wv = st[mine] / total;
             topk_idx[t * top_k + lane] = mine;
-            topk_w[t * top_k + lane] = wv * rsf;
+            topk_w[t * top_k + lane] = (mine_s / total) * rsf;
             sel[t * top_k + lane] = mine;
         }
     }
@@ -184,18 +218,18 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     __syncthreads();
     for (int a = threadIdx.x; a < A; a += kSelThreads) atomicAdd(&cnt[ea[a]], 1);
     __syncthreads();
-    // per-thread contiguous chunk of experts, then a workgroup scan
+    // per-thread contiguous run of experts, then a workgroup scan
     const int chunk = (NE + kSelThreads - 1) / kSelThreads;
-    const int e0 = threadIdx.x * chunk;
+    const int x0 = threadIdx.x * chunk;
     int my_cnt = 0, my_act = 0;
-    for (int e = e0; e < min(NE, e0 + chunk); ++e) {
+    for (int e = x0; e < min(NE, x0 + chunk); ++e) {
         my_cnt += cnt[e];
         my_act += cnt[e] > 0;
     }
     int tot_cnt, tot_act;
     int cnt_before = block_exclusive_scan(my_cnt, wave_tot, tot_cnt);
     int act_before = block_exclusive_scan(my_act, wave_tot, tot_act);
-    for (int e = e0; e < min(NE, e0 + chunk); ++e) {
+    for (int e = x0; e < min(NE, x0 + chunk); ++e) {
         start[e] = cnt_before;
         if (cnt[e] > 0) {
             wl_expert_id[act_before] = e;

@@ -27,6 +27,11 @@ SHAPES = {
     "t7_odd_groups_q4": (7, 2144, 96, 24, 3, 2, 5, 1, 4),
     "t1_q2_small": (1, 256, 128, 16, 4, 2, 4, 1, 2),
     "t2_q8_small": (2, 256, 128, 16, 4, 2, 4, 1, 8),
+    # group sizes the selection's lane butterfly cannot take (LDS fallback)
+    "t2_group_of_3": (2, 256, 128, 12, 4, 2, 3, 1, 4),
+    "t1_e100": (1, 512, 128, 100, 4, 2, 6, 1, 4),
+    # more tokens than LDS holds at H = 6144: tokens staged per segment
+    "t8_h6144_segments": (8, 6144, 256, 64, 8, 4, 8, 1, 4),
 }
 
 
