@@ -32,6 +32,9 @@ Readings (the pages are silent on these):
  R4  ties go to the lower group index, then the lower expert index.
  R5  weights: w_k = (s_k / sum_j s_j) * routed_scaling_factor, the sum taken in
      slot order; slot order = c descending, ties to the lower index.
+ R6  a NaN corrected score (from a NaN activation or bias) ranks below every
+     number, as -inf does, with ties to the lower index: the selection stays
+     a well-defined set of distinct experts.
  R7  expert FFN = SwiGLU without biases: h = silu(Wg x) * (Wu x), o = Wd h,
      silu(g) = g / (1 + exp(-g)).
  R8  int4 code = two's-complement nibble; byte j of a row holds column 2j in
@@ -153,6 +156,7 @@ def select_experts(scores: np.ndarray, bias: np.ndarray, n_group: int, topk_grou
     rsf32 = np.float32(rsf)
     for t in range(T):
         c = s[t] + b                                         # fp32 (R2)
+        c = np.where(np.isnan(c), np.float32(-np.inf), c)    # R6
         gs = [_top2_sum32(c[g * per:(g + 1) * per]) for g in range(n_group)]  # R1
         kept = sorted(range(n_group), key=lambda g: (-gs[g], g))[:topk_group]  # R4
         cand = [e for e in range(E) if e // per in kept]      # R3

@@ -104,6 +104,25 @@ def test_selection_matches_subset_enumeration(seed):
         np.testing.assert_allclose(w[t], ww, rtol=3e-7)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_nan_scores_rank_last(seed):
+    """Reading R6: a NaN corrected score selects as -inf does (ties by index);
+    the brute-force enumerator, given -inf there, is the reference."""
+    g = np.random.default_rng(100 + seed)
+    G, per, TG, K = 4, 4, 2, 4
+    s = expit(g.standard_normal((2, G * per))).astype(np.float32)
+    b = g.uniform(-0.1, 0.1, G * per).astype(np.float32)
+    holes = g.choice(G * per, size=5 + seed, replace=False)
+    b_nan, b_inf = b.copy(), b.copy()
+    b_nan[holes] = np.nan
+    b_inf[holes] = -np.inf
+    idx, _ = orc.select_experts(s, b_nan, G, TG, K, 2.5)
+    for t in range(2):
+        order, _ = _brute_select(s[t], b_inf, G, TG, K, 2.5)
+        assert idx[t].tolist() == order
+        assert len(set(idx[t].tolist())) == K
+
+
 def test_single_group_is_plain_topk():
     """n_group = topk_group = 1 reduces to a stable top-k of s + b."""
     g = np.random.default_rng(3)
