@@ -1,275 +1,49 @@
 // Expert kernels on the matrix cores: gate/up + SwiGLU, and down + weighted
-// combine, over row-scaled int8 / packed int4 / packed int2 codes.
+// combine, over row-scaled int8 / packed int4 / packed int2 codes (the row
+// loops, the code -> f16 conversion and the operand layouts are in mfma.h).
 //
 // The codes of each selected expert are streamed from HBM exactly once per
-// token batch (the batch union of the worklist).  The vector ALUs only turn
-// codes into exact f16 integers; the dot products run on
-// v_mfma_f32_16x16x32_f16 with 16 weight rows as the M dimension, the batch's
-// tokens as the N dimension (up to 16, so a verify batch costs no more ALU
-// work than one token) and 32 input columns per call as K.  Activations enter
-// as an f16 hi/lo pair (x ~= hi + lo to about 22 bits), so each product is
-// two MFMAs accumulated in fp32.
-//
-// Code -> f16: a field q of b bits sits in bits [s, s+b) of a 32-bit word w.
-// ((w >> s) & mask) ^ magic puts field s in the low half and field s+16/b*...
-// (the field 16 bits higher) in the high half of a half2, flips each field's
-// sign bit (two's complement -> q + 2^(b-1)) and ORs in the exponent of 1024,
-// so each half is the f16 value 1024 + 2^(b-1) + q; one packed f16 subtract
-// of that bias leaves q exactly.  The pairs come out in the column order
-// (s, s + 16/b): the staged activations use the same order, so the products
-// line up.
-//
-// Layout of one MFMA A operand: lane l supplies row l % 16 and the 8 K-values
-// 8*(l/16) .. +7, so the 4 lanes of a row read 4 consecutive 16-byte groups of
-// it (64 bytes, a "chunk") and one wave-wide load covers 16 rows x 64 bytes.
-// Each workgroup (8 waves, one per compute unit) owns a contiguous share of
-// the rows; its waves split the K dimension into chunks and their partial
-// sums meet in LDS in a fixed order (deterministic).
-#include "common.h"
+// token batch (the batch union of the worklist): one persistent 8-wave
+// workgroup per compute unit, each owning a contiguous share of the rows.
+#include "mfma.h"
 
 namespace moedec {
 
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace mfma;
 
-constexpr int kMT = 512;                 // threads of a persistent workgroup
-constexpr int kMW = kMT / kWave;         // its waves
-constexpr int kNBMax = 5;                // 16-row blocks per gate/up group at most
-constexpr int kNBD = 2;                  // 16-row blocks per down workgroup at most
-constexpr int kCols = 16;                // MFMA N: tokens per segment at most
-constexpr int kMaxActive = MOEDEC_MAX_EXPERTS + 8;
-constexpr size_t kLdsMax = 160 * 1024;
-constexpr size_t kStatic = 16 * 1024;    // static LDS of these kernels, rounded up
-
-// Per code width: MFMA calls per 16-byte group, mask / magic / bias of the
-// conversion, and the column (within the group) of element e of call c.
-template <int BITS>
-struct MfmaCodec;
-
-template <>
-struct MfmaCodec<4> {
-    static constexpr int NCALL = 4;
-    static constexpr int NB = 5;          // 16-row blocks per gate/up group
-    static constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64086408u, kBias = 0x64086408u;   // 1032
-    __device__ static int col(int c, int e) { return 8 * c + (e >> 1) + 4 * (e & 1); }
-};
-template <>
-struct MfmaCodec<8> {
-    static constexpr int NCALL = 2;
-    static constexpr int NB = 5;
-    static constexpr uint32_t kMask = 0x00FF00FFu, kMagic = 0x64806480u, kBias = 0x64806480u;   // 1152
-    __device__ static int col(int c, int e) { return 8 * c + 4 * (e >> 2) + ((e >> 1) & 1) + 2 * (e & 1); }
-};
-template <>
-struct MfmaCodec<2> {
-    static constexpr int NCALL = 8;
-    static constexpr int NB = 3;          // wider B operands: fewer blocks fit in registers
-    static constexpr uint32_t kMask = 0x00030003u, kMagic = 0x64026402u, kBias = 0x64026402u;   // 1026
-    // call c = 2*dword + half; element e = 2*s + t is field 4*half + s + 8*t of the dword
-    __device__ static int col(int c, int e) { return 16 * (c >> 1) + 4 * (c & 1) + (e >> 1) + 8 * (e & 1); }
-};
-
-__device__ __forceinline__ uint32_t q_pair(uint32_t w, int sh, uint32_t mask, uint32_t magic, uint32_t bias) {
-    const half2v v = __builtin_bit_cast(half2v, ((w >> sh) & mask) ^ magic) - __builtin_bit_cast(half2v, bias);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ uint32_t dword(const uint4& q, int d) {
-    return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
-}
-
-// A operand of call c (0 <= c < NCALL) from this lane's 16-byte group.
-template <int BITS>
-__device__ __forceinline__ half8 a_operand(const uint4& q, int c) {
-    using M = MfmaCodec<BITS>;
-    u32x4 p;
-    if constexpr (BITS == 4) {
-        const uint32_t w = dword(q, c);
-        p = u32x4{q_pair(w, 0, M::kMask, M::kMagic, M::kBias), q_pair(w, 4, M::kMask, M::kMagic, M::kBias),
-                  q_pair(w, 8, M::kMask, M::kMagic, M::kBias), q_pair(w, 12, M::kMask, M::kMagic, M::kBias)};
-    } else if constexpr (BITS == 8) {
-        const uint32_t w0 = dword(q, 2 * c), w1 = dword(q, 2 * c + 1);
-        p = u32x4{q_pair(w0, 0, M::kMask, M::kMagic, M::kBias), q_pair(w0, 8, M::kMask, M::kMagic, M::kBias),
-                  q_pair(w1, 0, M::kMask, M::kMagic, M::kBias), q_pair(w1, 8, M::kMask, M::kMagic, M::kBias)};
-    } else {
-        const uint32_t w = dword(q, c >> 1);
-        const int s0 = 8 * (c & 1);
-        p = u32x4{q_pair(w, s0 + 0, M::kMask, M::kMagic, M::kBias), q_pair(w, s0 + 2, M::kMask, M::kMagic, M::kBias),
-                  q_pair(w, s0 + 4, M::kMask, M::kMagic, M::kBias), q_pair(w, s0 + 6, M::kMask, M::kMagic, M::kBias)};
-    }
-    return __builtin_bit_cast(half8, p);
-}
-
-__device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// ------------------------------------------------------------ small helpers
-
-__device__ __forceinline__ int mw_load_worklist(const ExpertArgs& a, int* eid, int* seg) {
-    __shared__ int n_s;
-    if (threadIdx.x == 0) n_s = *a.n_active;
-    __syncthreads();
-    const int n = n_s;
-    for (int j = threadIdx.x; j <= n; j += kMT) {
-        if (j < n) eid[j] = a.expert_id[j];
-        seg[j] = a.seg[j];
-    }
-    __syncthreads();
-    return n;
-}
-
-// Largest j in [0, n) with v[j] <= q (v ascending, v[0] <= q).
-__device__ __forceinline__ int mw_upper_index(const int* v, int n, int q) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (v[mid] <= q) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Maximum over the workgroup.
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    float m = scratch[0];
-    for (int w = 1; w < kMW; ++w) m = fmaxf(m, scratch[w]);
-    return m;
-}
-
-// Power-of-two exponent k with max|v| * 2^k in [2^14, 2^15): the activations
-// then use the upper part of the f16 range without overflow.
-__device__ __forceinline__ int f16_exponent(float m) {
-    if (!(m > 0.f) || !isfinite(m)) return 0;
-    int e;
-    frexpf(m, &e);
-    int k = 15 - e;
-    return k > 100 ? 100 : k < -100 ? -100 : k;
-}
-
-// cpre[j] = segments (chunks of up to `cmax` tokens) of experts 0..j-1, j in [0, n].
-__device__ void mw_segment_prefix(const int* seg, int n, int cmax, int* cpre) {
-    __shared__ int wtot[kMW];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int per = (n + 1 + kMT - 1) / kMT;
-    const int j0 = threadIdx.x * per, j1 = min(j0 + per, n);
-    int local = 0;
-    for (int j = j0; j < j1; ++j) local += (seg[j + 1] - seg[j] + cmax - 1) / cmax;
-    int inc = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int u = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += u;
-    }
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    int run = inc - local;
-    for (int w = 0; w < wave; ++w) run += wtot[w];
-    for (int j = j0; j < min(j0 + per, n + 1); ++j) {
-        cpre[j] = run;
-        if (j < n) run += (seg[j + 1] - seg[j] + cmax - 1) / cmax;
-    }
-    __syncthreads();
-}
-
-// Stage n activation rows (row k of src = src + row_off[k] * ld, times mul[k])
-// into the B-operand layout: hi/lo[((ch*4 + q)*ldn + k)*NCALL + c] (half8),
-// with one power-of-two scale 2^kexp for all of them; groups past the row end
-// are zero.  Returns kexp.
-template <int BITS>
-__device__ int stage_b(const float* __restrict__ src, int ld, int ncols, const int* row_off, const float* mul,
-                       int n, int ldn, half8* hi, half8* lo, float* scratch) {
-    using M = MfmaCodec<BITS>;
-    constexpr int CW = 16 * (8 / BITS);
-    const int P = ncols / CW;                    // 16-byte groups of a row
-    const int NCH = (P + 3) / 4;
-    float m = 0.f;
-    for (int idx = threadIdx.x; idx < n * (ncols / 4); idx += kMT) {
-        const int k = idx / (ncols / 4), c4 = idx - k * (ncols / 4);
-        const float4 v = reinterpret_cast<const float4*>(src + (size_t)row_off[k] * ld)[c4];
-        const float s = mul ? fabsf(mul[k]) : 1.f;
-        m = fmaxf(m, s * fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    const int kexp = f16_exponent(block_max(m, scratch));
-    const float sc = ldexpf(1.0f, kexp);
-    const int units = NCH * 4 * n * M::NCALL;
-    for (int u = threadIdx.x; u < units; u += kMT) {
-        const int c = u % M::NCALL;
-        const int k = (u / M::NCALL) % n;
-        const int g = u / (M::NCALL * n);        // group = ch * 4 + q
-        half8 vh, vl;
-        if (g < P) {
-            const float* row = src + (size_t)row_off[k] * ld + g * CW;
-            const float s = (mul ? mul[k] : 1.f) * sc;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = row[M::col(c, e)] * s;
-                const _Float16 h = (_Float16)v;
-                vh[e] = h;
-                vl[e] = (_Float16)(v - (float)h);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vh[e] = vl[e] = (_Float16)0.f;
-        }
-        const int dst = (g * ldn + k) * M::NCALL + c;
-        hi[dst] = vh;
-        lo[dst] = vl;
-    }
-    return kexp;
-}
-
-// ------------------------------------------------------------------ gate / up
-//
-// Work units are (segment, row): segment = (active expert j, a chunk of up to
-// `ns` of its tokens), enumerated expert-ascending; workgroup b takes the
-// b-th equal contiguous share.  Rows are taken in groups of up to kNB
-// 16-row blocks; for each group the waves walk their K-chunks (gate and up
-// codes of all the group's blocks per chunk, the next chunk's loads in flight
-// during the current one's MFMAs), then reduce over waves in LDS and write
-// h[a][r] = silu(g) * v.
-
+// Gate/up work units are (segment, row): segment = (active expert j, a chunk
+// of up to `ns` of its tokens), enumerated expert-ascending; workgroup b takes
+// the b-th equal contiguous share.  With T <= ns all tokens are staged once and
+// a segment's columns point at their tokens' slots; otherwise each segment
+// stages its own tokens (skipped when they are the ones already staged).
 template <int BITS>
 __global__ __launch_bounds__(kMT) void gate_up_mfma_kernel(const float* __restrict__ x, const ExpertArgs a,
                                                            float* __restrict__ h, int ns) {
     using M = MfmaCodec<BITS>;
     constexpr int NCALL = M::NCALL;
-    constexpr int kNB = M::NB;
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ int eid[kMaxActive];
     __shared__ int seg[kMaxActive + 1];
     __shared__ int cpre[kMaxActive + 1];
-    __shared__ int tok_s[kCols], asg_s[kCols], row_s[kCols], staged_s[kCols];
+    __shared__ int tok_s[kCols], asg_s[kCols], col_s[kCols], staged_s[kCols];
     __shared__ float scratch[kMW];
     __shared__ int kexp_s;
     __shared__ float sg_s[kNBMax * 16], su_s[kNBMax * 16];
 
     const int H = a.H, I = a.I, T = a.T;
-    const int row_bytes = H * BITS / 8;
-    const int P = row_bytes >> 4;
-    const int NCH = (P + 3) / 4;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int ln = lane & 15, lq = lane >> 4;       // MFMA column (token) and K-slice of this lane
+    const int NCH = ((H * BITS / 8) / 16 + 3) / 4;
     half8* xhi = reinterpret_cast<half8*>(dyn);
     half8* xlo = xhi + (size_t)NCH * 4 * ns * NCALL;
-    float* red = reinterpret_cast<float*>(xlo + (size_t)NCH * 4 * ns * NCALL);   // [kMW][kNB][2][16][ns]
+    float* red = reinterpret_cast<float*>(xlo + (size_t)NCH * 4 * ns * NCALL);
     const bool stage_all = T <= ns;
 
     if (threadIdx.x < kCols) staged_s[threadIdx.x] = -1;
     if (stage_all) {   // all tokens once: slot = token index
-        if (threadIdx.x < kCols) row_s[threadIdx.x] = threadIdx.x;
+        if (threadIdx.x < kCols) tok_s[threadIdx.x] = threadIdx.x;
         __syncthreads();
-        const int k = stage_b<BITS>(x, H, H, row_s, nullptr, T, ns, xhi, xlo, scratch);
+        const int k = stage_b<BITS>(x, H, H, tok_s, nullptr, T, ns, xhi, xlo, scratch);
         if (threadIdx.x == 0) kexp_s = k;
     }
     const int n_act = mw_load_worklist(a, eid, seg);
@@ -280,7 +54,6 @@ __global__ __launch_bounds__(kMT) void gate_up_mfma_kernel(const float* __restri
     const long long u0 = n_units * blockIdx.x / gridDim.x;
     const long long u1 = n_units * (blockIdx.x + 1) / gridDim.x;
     if (u0 >= u1) return;
-    const int cw0 = wave * NCH / kMW, cw1 = (wave + 1) * NCH / kMW;   // this wave's K-chunks
 
     for (int sidx = (int)(u0 / I); (long long)sidx * I < u1; ++sidx) {
         const int rlo = (int)max(u0 - (long long)sidx * I, 0LL);
@@ -294,6 +67,7 @@ __global__ __launch_bounds__(kMT) void gate_up_mfma_kernel(const float* __restri
             const int as = a.assign[first + threadIdx.x];
             asg_s[threadIdx.x] = as;
             tok_s[threadIdx.x] = as / a.slots;
+            col_s[threadIdx.x] = stage_all ? as / a.slots : (int)threadIdx.x;
         }
         __syncthreads();
         if (!stage_all) {
@@ -306,305 +80,31 @@ __global__ __launch_bounds__(kMT) void gate_up_mfma_kernel(const float* __restri
                 __syncthreads();
             }
         }
-        // B-operand slot of this lane's token column, or -1
-        const int bslot = ln < nc ? (stage_all ? tok_s[ln] : ln) : -1;
-        const float unscale = ldexpf(1.0f, -kexp_s);
-        const uint8_t* gb = a.w_gate + (size_t)e * I * row_bytes;
-        const uint8_t* ub = a.w_up + (size_t)e * I * row_bytes;
-
-        for (int g0 = rlo; g0 < rhi; g0 += kNB * 16) {
-            const int gn = min(rhi - g0, kNB * 16);          // rows in this group
-            const int nb = (gn + 15) >> 4;
-            if ((int)threadIdx.x < gn) {                      // row scales, read at the end
-                sg_s[threadIdx.x] = a.s_gate[(size_t)e * I + g0 + threadIdx.x];
-                su_s[threadIdx.x] = a.s_up[(size_t)e * I + g0 + threadIdx.x];
-            }
-            floatx4 accg[kNB], accu[kNB];
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) accg[b] = accu[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-            // Every load is issued unconditionally at a clamped (valid) address,
-            // so the wait counts before each use are static: rows past the group
-            // re-read its last row (their outputs are never written) and groups
-            // past the row end meet zero activations.
-            auto issue = [&](int ch, uint4* dg, uint4* du) {
-                const int grp = min(ch * 4 + lq, P - 1);
-#pragma unroll
-                for (int b = 0; b < kNB; ++b) {
-                    const int r = min(g0 + b * 16 + ln, rhi - 1);
-                    const size_t off = (size_t)r * row_bytes + grp * 16;
-                    dg[b] = ld16(gb + off);
-                    du[b] = ld16(ub + off);
-                }
-            };
-            auto compute = [&](int ch, const uint4* dg, const uint4* du) {
-                half8 bh[NCALL], bl[NCALL];
-#pragma unroll
-                for (int c = 0; c < NCALL; ++c) {
-                    if (bslot >= 0) {
-                        const int src = ((ch * 4 + lq) * ns + bslot) * NCALL + c;
-                        bh[c] = xhi[src];
-                        bl[c] = xlo[src];
-                    } else {
-#pragma unroll
-                        for (int e2 = 0; e2 < 8; ++e2) bh[c][e2] = bl[c][e2] = (_Float16)0.f;
-                    }
-                }
-#pragma unroll
-                for (int b = 0; b < kNB; ++b) {
-                    if (b < nb) {
-#pragma unroll
-                        for (int c = 0; c < NCALL; ++c) {
-                            const half8 ag = a_operand<BITS>(dg[b], c);
-                            accg[b] = mfma(ag, bh[c], accg[b]);
-                            accg[b] = mfma(ag, bl[c], accg[b]);
-                            const half8 au = a_operand<BITS>(du[b], c);
-                            accu[b] = mfma(au, bh[c], accu[b]);
-                            accu[b] = mfma(au, bl[c], accu[b]);
-                        }
-                    }
-                }
-            };
-            const int nk = cw1 - cw0;
-            if (nk > 0) {
-                uint4 g0b[kNB], u0b[kNB], g1b[kNB], u1b[kNB];
-                issue(cw0, g0b, u0b);
-                for (int t = 0; t < nk; t += 2) {          // two register buffers, alternating
-                    issue(cw0 + min(t + 1, nk - 1), g1b, u1b);
-                    compute(cw0 + t, g0b, u0b);
-                    issue(cw0 + min(t + 2, nk - 1), g0b, u0b);
-                    if (t + 1 < nk) compute(cw0 + t + 1, g1b, u1b);
-                }
-            }
-            // partial sums of this wave's K-chunks -> LDS; lane holds rows 4*lq + i, column ln
-            if (ln < nc) {
-#pragma unroll
-                for (int b = 0; b < kNB; ++b) {
-                    if (b < nb) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = 4 * lq + i;
-                            red[(((wave * kNB + b) * 2 + 0) * 16 + r) * ns + ln] = accg[b][i];
-                            red[(((wave * kNB + b) * 2 + 1) * 16 + r) * ns + ln] = accu[b][i];
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < gn * nc; idx += kMT) {
-                const int r = idx / nc, n = idx - r * nc;
-                const int b = r >> 4, rr = r & 15;
-                float gs = 0.f, vs = 0.f;
-                for (int w = 0; w < kMW; ++w) {
-                    gs += red[(((w * kNB + b) * 2 + 0) * 16 + rr) * ns + n];
-                    vs += red[(((w * kNB + b) * 2 + 1) * 16 + rr) * ns + n];
-                }
-                const int row = g0 + r;
-                const float gv = gs * unscale * sg_s[r];
-                const float uv = vs * unscale * su_s[r];
-                h[(size_t)asg_s[n] * I + row] = gv / (1.0f + __expf(-gv)) * uv;
-            }
-            __syncthreads();
-        }
+        gate_up_rows<BITS>(a, h, e, rlo, rhi, nc, col_s, asg_s, xhi, xlo, ns, ldexpf(1.0f, -kexp_s), red, sg_s,
+                           su_s);
     }
 }
 
-// ------------------------------------------------------------ down + combine
-//
-// Workgroup b owns output rows [b*rows, (b+1)*rows) (at most kNBD blocks of 16)
-// for the whole batch, at most 16 tokens (one MFMA column each).  It walks the
-// worklist (experts ascending) in chunks of up to `qc` assignments, stages
-// those assignments' h times their routing weight as f16 hi/lo in LDS, and for
-// every expert accumulates Qd . h' over its waves' K-chunks, scales the result
-// by the expert's row scales and adds it to the running sum; after the last
-// chunk the waves' sums meet in LDS in a fixed order and y is written.  No
-// atomics: the result is deterministic.
-
+// Down: workgroup b owns output rows [b*rows, (b+1)*rows) for the whole batch.
 template <int BITS>
 __global__ __launch_bounds__(kMT) void down_mfma_kernel(const float* __restrict__ h,
                                                         const float* __restrict__ topk_w, const ExpertArgs a,
                                                         float* __restrict__ y, int qc, int rows_per_wg) {
-    using M = MfmaCodec<BITS>;
-    constexpr int NCALL = M::NCALL;
-    constexpr int W = 4;                        // items (expert, chunk) in flight per wave
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ int eid[kMaxActive];
     __shared__ int seg[kMaxActive + 1];
     __shared__ float scratch[kMW];
-
-    const int H = a.H, I = a.I, T = a.T, K = a.top_k, slots = a.slots;
-    const int row_bytes = I * BITS / 8;
-    const int P = row_bytes >> 4;
-    const int NCH = (P + 3) / 4;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int ln = lane & 15, lq = lane >> 4;
     const int r0 = blockIdx.x * rows_per_wg;
-    const int r1 = min(r0 + rows_per_wg, H);
+    const int r1 = min(r0 + rows_per_wg, a.H);
     if (r0 >= r1) return;
-    const int nrows = r1 - r0;
-    const int nb = (nrows + 15) >> 4;
-
-    half8* hhi = reinterpret_cast<half8*>(dyn);                 // [NCH*4][qc][NCALL]
-    half8* hlo = hhi + (size_t)NCH * 4 * qc * NCALL;
-    float* red = reinterpret_cast<float*>(hlo + (size_t)NCH * 4 * qc * NCALL);   // [kMW][kNBD][16][16]
-    int* qrow = reinterpret_cast<int*>(red + (size_t)kMW * kNBD * 256);          // [qc] assignment
-    float* qmul = reinterpret_cast<float*>(qrow + qc);                            // [qc] routing weight
-    int* amap = reinterpret_cast<int*>(qmul + qc);                                // [qc][16] expert x token -> slot
-    float* sd_s = reinterpret_cast<float*>(amap + (size_t)qc * kCols);           // [qc][32] row scales
-
     const int n_act = mw_load_worklist(a, eid, seg);
-    const int A = seg[n_act];
-    const int cw0 = wave * NCH / kMW, cw1 = (wave + 1) * NCH / kMW;
-    const int nk = cw1 - cw0;                    // this wave's K-chunks
-    floatx4 tot[kNBD];
-#pragma unroll
-    for (int b = 0; b < kNBD; ++b) tot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* wbase = a.w_down + (size_t)r0 * row_bytes;
-
-    for (int q0 = 0; q0 < A; q0 += qc) {
-        const int q1 = min(A, q0 + qc);
-        const int nq = q1 - q0;
-        const int j_first = mw_upper_index(seg, n_act, q0);
-        const int j_last = mw_upper_index(seg, n_act, q1 - 1);
-        const int nj = j_last - j_first + 1;
-        const int n_items = nj * nk;
-
-        uint4 ring[W][kNBD];
-        // every load unconditional at a clamped address (static wait counts):
-        // rows past the block re-read the last row, items past the end the last item
-        auto issue = [&](int i, uint4* dst) {
-            i = min(i, n_items - 1);
-            const int jj = j_first + i / nk, ch = cw0 + i % nk;
-            const int grp = min(ch * 4 + lq, P - 1);
-            const uint8_t* base = wbase + (size_t)eid[jj] * H * row_bytes + grp * 16;
-#pragma unroll
-            for (int b = 0; b < kNBD; ++b) dst[b] = ld16(base + (size_t)min(b * 16 + ln, nrows - 1) * row_bytes);
-        };
-        // weights first: these loads fly while h is staged
-        if (n_items > 0) {
-#pragma unroll
-            for (int w = 0; w < W; ++w) issue(w, ring[w]);
-        }
-
-        __syncthreads();   // the previous chunk's readers are done with LDS
-        for (int ql = threadIdx.x; ql < nq; ql += kMT) {
-            const int as = a.assign[q0 + ql];
-            const int t = as / slots, slot = as - t * slots;
-            qrow[ql] = as;
-            qmul[ql] = slot < K ? topk_w[t * K + slot] : 1.0f;
-        }
-        for (int i = threadIdx.x; i < nj * kCols; i += kMT) amap[i] = -1;
-        for (int i = threadIdx.x; i < nj * 32; i += kMT) {        // row scales of the chunk's experts
-            const int jq = i >> 5, rl = min(i & 31, nrows - 1);
-            sd_s[i] = a.s_down[(size_t)eid[j_first + jq] * H + r0 + rl];
-        }
-        __syncthreads();
-        for (int ql = threadIdx.x; ql < nq; ql += kMT) {
-            const int jj = mw_upper_index(seg, n_act, q0 + ql);
-            amap[(jj - j_first) * kCols + qrow[ql] / slots] = ql;
-        }
-        const int kexp = stage_b<BITS>(h, I, I, qrow, qmul, nq, qc, hhi, hlo, scratch);
-        __syncthreads();
-        const float unscale = ldexpf(1.0f, -kexp);
-
-        floatx4 acc[kNBD];
-#pragma unroll
-        for (int b = 0; b < kNBD; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int base = 0; base < n_items; base += W) {
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const int i = base + w;
-                uint4 cq[kNBD];
-#pragma unroll
-                for (int b = 0; b < kNBD; ++b) cq[b] = ring[w][b];
-                issue(i + W, ring[w]);
-                if (i < n_items) {
-                    const int jq = i / nk, ch = cw0 + i % nk;
-                    const int bq = amap[jq * kCols + ln];                 // this lane's token column
-                    half8 bh[NCALL], bl[NCALL];
-#pragma unroll
-                    for (int c = 0; c < NCALL; ++c) {
-                        if (bq >= 0) {
-                            const int src = ((ch * 4 + lq) * qc + bq) * NCALL + c;
-                            bh[c] = hhi[src];
-                            bl[c] = hlo[src];
-                        } else {
-#pragma unroll
-                            for (int e2 = 0; e2 < 8; ++e2) bh[c][e2] = bl[c][e2] = (_Float16)0.f;
-                        }
-                    }
-#pragma unroll
-                    for (int b = 0; b < kNBD; ++b) {
-                        if (b < nb) {
-#pragma unroll
-                            for (int c = 0; c < NCALL; ++c) {
-                                const half8 av = a_operand<BITS>(cq[b], c);
-                                acc[b] = mfma(av, bh[c], acc[b]);
-                                acc[b] = mfma(av, bl[c], acc[b]);
-                            }
-                        }
-                    }
-                    if (i % nk == nk - 1) {          // expert done for this wave: scale rows, add
-#pragma unroll
-                        for (int b = 0; b < kNBD; ++b) {
-#pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2)
-                                tot[b][i2] += (sd_s[jq * 32 + b * 16 + 4 * lq + i2] * unscale) * acc[b][i2];
-                            acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
-                }
-            }
-        }
-    }
-    // the waves' partial sums -> LDS -> y, summed in wave order
-    if (ln < T) {
-#pragma unroll
-        for (int b = 0; b < kNBD; ++b)
-            if (b < nb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) red[((wave * kNBD + b) * 16 + 4 * lq + i) * 16 + ln] = tot[b][i];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nrows * T; idx += kMT) {
-        const int t = idx / nrows, r = idx - t * nrows;
-        const int b = r >> 4, rr = r & 15;
-        float s = 0.f;
-        for (int w = 0; w < kMW; ++w) s += red[((w * kNBD + b) * 16 + rr) * 16 + t];
-        y[(size_t)t * H + r0 + r] = s;
-    }
-}
-
-// --------------------------------------------------------------------- launch
-
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-// Dynamic LDS a persistent workgroup asks for at least, so that no two of them
-// share a compute unit.
-constexpr size_t kLdsOnePerCu = 84 * 1024;
-
-template <typename Kern>
-hipError_t allow_lds(Kern k, size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
+    down_rows<BITS>(h, topk_w, a, y, r0, r1, qc, dyn, eid, seg, a.assign, n_act, scratch);
 }
 
 template <int BITS>
 hipError_t gate_up_mfma_bits(const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
-    const int P = (a.H * BITS / 8) / 16;
-    const int NCH = (P + 3) / 4;
     // per staged token: hi + lo B operands and the reduction buffer
-    const size_t per_tok = (size_t)NCH * 4 * MfmaCodec<BITS>::NCALL * 2 * sizeof(half8) +
-                           (size_t)kMW * MfmaCodec<BITS>::NB * 2 * 16 * sizeof(float);
+    const size_t per_tok = staged_row_bytes<BITS>(a.H) + gate_up_red_bytes_per_token<BITS>();
     int fit = (int)((kLdsMax - kStatic) / per_tok);
     if (fit > kCols) fit = kCols;
     if (fit < 1) return hipErrorInvalidValue;
@@ -620,16 +120,13 @@ hipError_t gate_up_mfma_bits(const float* x, const ExpertArgs& a, float* h, hipS
 
 template <int BITS>
 hipError_t down_mfma_bits(const float* h, const float* topk_w, const ExpertArgs& a, float* y, hipStream_t st) {
-    const int P = (a.I * BITS / 8) / 16;
-    const int NCH = (P + 3) / 4;
     const int n_wg = cu_count();
     int rows = (a.H + n_wg - 1) / n_wg;
     if (rows > kNBD * 16) rows = kNBD * 16;          // then more workgroups than CUs
     if (a.T > kCols) return hipErrorInvalidValue;
     const int A = a.T * a.slots;
-    const size_t fixed = (size_t)kMW * kNBD * 256 * sizeof(float);
-    const size_t per_q = (size_t)NCH * 4 * MfmaCodec<BITS>::NCALL * 2 * sizeof(half8) + sizeof(int) +
-                         sizeof(float) + kCols * sizeof(int) + 32 * sizeof(float);
+    const size_t fixed = down_lds_fixed_bytes();
+    const size_t per_q = down_lds_bytes_per_assignment<BITS>(a.I);
     int qc = (int)((kLdsMax - kStatic - fixed) / per_q);
     if (qc < 1) return hipErrorInvalidValue;
     if (qc > A) qc = A;
