@@ -32,9 +32,10 @@ Readings (the pages are silent on these):
  R4  ties go to the lower group index, then the lower expert index.
  R5  weights: w_k = (s_k / sum_j s_j) * routed_scaling_factor, the sum taken in
      slot order; slot order = c descending, ties to the lower index.
- R6  a NaN corrected score (from a NaN activation or bias) ranks below every
-     number, as -inf does, with ties to the lower index: the selection stays
-     a well-defined set of distinct experts.
+ R6  a NaN corrected score (from a NaN activation or bias), or a NaN group
+     score (+inf and -inf in one group), ranks below every number, as -inf
+     does, with ties to the lower index: the selection stays a well-defined
+     set of distinct experts.
  R7  expert FFN = SwiGLU without biases: h = silu(Wg x) * (Wu x), o = Wd h,
      silu(g) = g / (1 + exp(-g)).
  R8  int4 code = two's-complement nibble; byte j of a row holds column 2j in
@@ -137,7 +138,9 @@ def router_scores(x: np.ndarray, router_w: np.ndarray) -> np.ndarray:
 
 def _top2_sum32(vals: np.ndarray) -> np.float32:
     order = sorted(range(len(vals)), key=lambda j: (-vals[j], j))
-    return np.float32(vals[order[0]] + vals[order[1]])
+    with np.errstate(invalid="ignore"):
+        g = np.float32(vals[order[0]] + vals[order[1]])
+    return np.float32(-np.inf) if np.isnan(g) else g          # R6
 
 
 def select_experts(scores: np.ndarray, bias: np.ndarray, n_group: int, topk_group: int,

@@ -123,6 +123,23 @@ def test_nan_scores_rank_last(seed):
         assert len(set(idx[t].tolist())) == K
 
 
+def test_inf_minus_inf_group_ranks_last():
+    """Reading R6: a group whose top two corrected scores are +inf and -inf has
+    a NaN sum, ranked as -inf: with three finite groups and two kept, it is
+    never kept, as if all its members were -inf."""
+    g = np.random.default_rng(7)
+    s = expit(g.standard_normal((3, 16))).astype(np.float32)
+    b = g.uniform(-0.1, 0.1, 16).astype(np.float32)
+    b_odd, b_ref = b.copy(), b.copy()
+    b_odd[4:8] = [np.inf, -np.inf, -np.inf, -np.inf]
+    b_ref[4:8] = -np.inf
+    idx, _ = orc.select_experts(s, b_odd, 4, 2, 4, 2.5)
+    for t in range(3):
+        order, _ = _brute_select(s[t], b_ref, 4, 2, 4, 2.5)
+        assert idx[t].tolist() == order
+        assert not any(4 <= e < 8 for e in idx[t])
+
+
 def test_single_group_is_plain_topk():
     """n_group = topk_group = 1 reduces to a stable top-k of s + b."""
     g = np.random.default_rng(3)
