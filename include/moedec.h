@@ -160,6 +160,47 @@ int moe_expert_down_combine_q2(const float* h, const moedec_experts* ex, const m
                                const float* topk_w, int T, int top_k, float* y, void* stream);
 
 /*
+ * The whole layer step in one launch: moe_route_topk (with the worklist),
+ * then the gate/up and down calls, fused (same passages as those three calls;
+ * Show HN page, "implemented features").  Arguments and outputs are those of
+ * the three calls; E = ex->n_experts, H = ex->hidden, S = ex->n_shared.
+ *   x, router_w, bias          : as for moe_route_topk
+ *   scores, topk_idx, topk_w   : as for moe_route_topk
+ *   wl                         : required; filled as moe_route_topk fills it
+ *   h                          : fp32 [T*(top_k+S), inter] (the gate/up result)
+ *   y                          : fp32 [T, H] (the layer output)
+ *   workspace : int32 [MOEDEC_FUSED_WORKSPACE_INTS], device memory the caller
+ *       zeroes once before the first call and then leaves to the library; it
+ *       holds the state of the launch's grid-wide barriers, so launches that
+ *       may run at the same time need separate workspaces.  After the call
+ *       (once the stream has reached it) workspace[2] != 0 means a barrier
+ *       wait timed out: not every workgroup could be resident at once (the
+ *       GPU was shared with other work); that call's outputs are invalid and
+ *       the workspace must be zeroed again.  workspace[3] > 0 caps the
+ *       barrier wait at that many polling rounds (0: about two seconds).
+ * The scores may differ from moe_route_topk's in the last bits (another
+ * summation order); routing and results are otherwise those of the separate
+ * calls given the same scores.  Limits: T <= MOEDEC_FUSED_MAX_TOKENS,
+ * n_experts <= MOEDEC_FUSED_MAX_EXPERTS, else MOEDEC_ERR_UNSUPPORTED (use the
+ * separate calls).
+ */
+#define MOEDEC_FUSED_WORKSPACE_INTS 16
+#define MOEDEC_FUSED_MAX_TOKENS 16
+#define MOEDEC_FUSED_MAX_EXPERTS 512
+int moe_layer_fused_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                       int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                       float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                       float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                       int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                       float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                       float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                       int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                       float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                       float* h, float* y, int32_t* workspace, void* stream);
+
+/*
  * Packing of codes (ideipro.ru: packing checked bit for bit; Show HN page,
  * "implemented features": int8, packed int4, packed int2).
  *   codes  : int8  [rows, row_len]                 one code per int8

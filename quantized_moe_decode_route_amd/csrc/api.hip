@@ -74,6 +74,55 @@ int down(int bits, const float* h, const moedec_experts* ex, const moedec_workli
     return device_status(launch_down(bits, h, topk_w, a, y, static_cast<hipStream_t>(stream)));
 }
 
+int route_args_ok(int T, int H, int E, int n_group, int topk_group, int top_k, int n_shared, float rsf) {
+    if (T < 1 || H < 4 || H % 4 || E < 2 || n_group < 1 || E % n_group || E / n_group < 2)
+        return MOEDEC_ERR_INVALID_ARG;
+    if (topk_group < 1 || topk_group > n_group || top_k < 1 || top_k > topk_group * (E / n_group))
+        return MOEDEC_ERR_INVALID_ARG;
+    if (n_shared < 0 || !isfinite(rsf)) return MOEDEC_ERR_INVALID_ARG;
+    if (T > MOEDEC_MAX_TOKENS || E > MOEDEC_MAX_EXPERTS || n_group > 64 || top_k > 32 || n_shared > 8 ||
+        H > MOEDEC_MAX_DIM)
+        return MOEDEC_ERR_UNSUPPORTED;
+    return MOEDEC_OK;
+}
+
+int layer_fused(int bits, const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                int T, int n_group, int topk_group, int top_k, float rsf, float* scores, int32_t* topk_idx,
+                float* topk_w, const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream) {
+    if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w || !h || !y || !workspace)
+        return MOEDEC_ERR_INVALID_ARG;
+    FusedLayerArgs f{};
+    int st = check_experts(ex, wl, bits, T, top_k, f.ex);
+    if (st != MOEDEC_OK) return st;
+    st = route_args_ok(T, ex->hidden, ex->n_experts, n_group, topk_group, top_k, ex->n_shared, rsf);
+    if (st != MOEDEC_OK) return st;
+    if (!aligned16(x) || !aligned16(router_w) || !aligned16(h) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MOEDEC_ERR_INVALID_ARG;
+    if (T > MOEDEC_FUSED_MAX_TOKENS || ex->n_experts > MOEDEC_FUSED_MAX_EXPERTS) return MOEDEC_ERR_UNSUPPORTED;
+    f.x = x;
+    f.router_w = router_w;
+    f.bias = bias;
+    f.scores = scores;
+    f.topk_idx = topk_idx;
+    f.topk_w = topk_w;
+    f.wl_n_active = wl->n_active;
+    f.wl_expert_id = wl->expert_id;
+    f.wl_seg = wl->seg;
+    f.wl_assign = wl->assign;
+    f.h = h;
+    f.y = y;
+    f.workspace = workspace;
+    f.T = T;
+    f.E = ex->n_experts;
+    f.n_group = n_group;
+    f.topk_group = topk_group;
+    f.n_shared = ex->n_shared;
+    f.rsf = rsf;
+    const hipError_t err = launch_layer_fused(bits, f, static_cast<hipStream_t>(stream));
+    if (err == hipErrorInvalidValue) return MOEDEC_ERR_UNSUPPORTED;   // shapes the LDS plan cannot hold
+    return device_status(err);
+}
+
 int pack(int bits, const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len, void* stream) {
     if (rows < 0 || row_len < 0 || row_len % (8 / bits)) return MOEDEC_ERR_INVALID_ARG;
     if (rows * row_len == 0) return MOEDEC_OK;
@@ -108,14 +157,9 @@ MOEDEC_API int moe_route_topk(const float* x, const float* router_w, const float
                               void* stream) {
     if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w) return MOEDEC_ERR_INVALID_ARG;
     if (wl && (!wl->n_active || !wl->expert_id || !wl->seg || !wl->assign)) return MOEDEC_ERR_INVALID_ARG;
-    if (T < 1 || H < 4 || H % 4 || E < 2 || n_group < 1 || E % n_group || E / n_group < 2) return MOEDEC_ERR_INVALID_ARG;
-    if (topk_group < 1 || topk_group > n_group || top_k < 1 || top_k > topk_group * (E / n_group))
-        return MOEDEC_ERR_INVALID_ARG;
-    if (n_shared < 0 || !isfinite(routed_scaling_factor)) return MOEDEC_ERR_INVALID_ARG;
+    const int st = route_args_ok(T, H, E, n_group, topk_group, top_k, n_shared, routed_scaling_factor);
+    if (st != MOEDEC_OK) return st;
     if (!aligned16(x) || !aligned16(router_w)) return MOEDEC_ERR_INVALID_ARG;
-    if (T > MOEDEC_MAX_TOKENS || E > MOEDEC_MAX_EXPERTS || n_group > 64 || top_k > 32 || n_shared > 8 ||
-        H > MOEDEC_MAX_DIM)
-        return MOEDEC_ERR_UNSUPPORTED;
     return device_status(launch_route(x, router_w, bias, T, H, E, n_group, topk_group, top_k, n_shared,
                                       routed_scaling_factor, scores, topk_idx, topk_w, wl,
                                       static_cast<hipStream_t>(stream)));
@@ -169,4 +213,26 @@ MOEDEC_API int moe_unpack_q2(const uint8_t* packed, int8_t* codes, int64_t rows,
 MOEDEC_API int moe_residual_rmsnorm(float* x, const float* y, float* xn, int T, int H, float eps, void* stream) {
     if (!x || !xn || T < 1 || H < 1 || !(eps >= 0.0f)) return MOEDEC_ERR_INVALID_ARG;
     return device_status(launch_residual_rmsnorm(x, y, xn, T, H, eps, static_cast<hipStream_t>(stream)));
+}
+
+MOEDEC_API int moe_layer_fused_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                                  int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                                  float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                  float* h, float* y, int32_t* workspace, void* stream) {
+    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
+                       topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                                  int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                                  float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                  float* h, float* y, int32_t* workspace, void* stream) {
+    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
+                       topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                                  int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                                  float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                  float* h, float* y, int32_t* workspace, void* stream) {
+    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
+                       topk_idx, topk_w, wl, h, y, workspace, stream);
 }

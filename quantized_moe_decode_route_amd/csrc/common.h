@@ -152,6 +152,28 @@ hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const
 hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                        hipStream_t stream);
 
+// Everything the fused layer launch needs (the worklist fields of `ex` unused).
+struct FusedLayerArgs {
+    ExpertArgs ex;
+    const float* x;
+    const float* router_w;
+    const float* bias;
+    float* scores;
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* wl_n_active;
+    int32_t* wl_expert_id;
+    int32_t* wl_seg;
+    int32_t* wl_assign;
+    float* h;
+    float* y;
+    int32_t* workspace;
+    int T, E, n_group, topk_group, n_shared;
+    float rsf;
+};
+
+hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);
+
 hipError_t launch_pack(int bits, const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len,
                        hipStream_t stream);
 hipError_t launch_unpack(int bits, const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len,

@@ -13,76 +13,24 @@ namespace {
 
 using namespace mfma;
 
-// Gate/up work units are (segment, row): segment = (active expert j, a chunk
-// of up to `ns` of its tokens), enumerated expert-ascending; workgroup b takes
-// the b-th equal contiguous share.  With T <= ns all tokens are staged once and
-// a segment's columns point at their tokens' slots; otherwise each segment
-// stages its own tokens (skipped when they are the ones already staged).
+// Gate/up: all tokens staged once when they fit (T <= ns), then this
+// workgroup's share of the (segment, row) units.
 template <int BITS>
 __global__ __launch_bounds__(kMT) void gate_up_mfma_kernel(const float* __restrict__ x, const ExpertArgs a,
                                                            float* __restrict__ h, int ns) {
-    using M = MfmaCodec<BITS>;
-    constexpr int NCALL = M::NCALL;
+    constexpr int NCALL = MfmaCodec<BITS>::NCALL;
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ int eid[kMaxActive];
     __shared__ int seg[kMaxActive + 1];
-    __shared__ int cpre[kMaxActive + 1];
-    __shared__ int tok_s[kCols], asg_s[kCols], col_s[kCols], staged_s[kCols];
-    __shared__ float scratch[kMW];
-    __shared__ int kexp_s;
-    __shared__ float sg_s[kNBMax * 16], su_s[kNBMax * 16];
-
-    const int H = a.H, I = a.I, T = a.T;
-    const int NCH = ((H * BITS / 8) / 16 + 3) / 4;
+    __shared__ GateUpLds s;
+    const int NCH = ((a.H * BITS / 8) / 16 + 3) / 4;
     half8* xhi = reinterpret_cast<half8*>(dyn);
     half8* xlo = xhi + (size_t)NCH * 4 * ns * NCALL;
     float* red = reinterpret_cast<float*>(xlo + (size_t)NCH * 4 * ns * NCALL);
-    const bool stage_all = T <= ns;
-
-    if (threadIdx.x < kCols) staged_s[threadIdx.x] = -1;
-    if (stage_all) {   // all tokens once: slot = token index
-        if (threadIdx.x < kCols) tok_s[threadIdx.x] = threadIdx.x;
-        __syncthreads();
-        const int k = stage_b<BITS>(x, H, H, tok_s, nullptr, T, ns, xhi, xlo, scratch);
-        if (threadIdx.x == 0) kexp_s = k;
-    }
+    const bool stage_all = a.T <= ns;
+    if (stage_all) stage_tokens<BITS>(x, a.T, a.H, ns, xhi, xlo, s);
     const int n_act = mw_load_worklist(a, eid, seg);
-    mw_segment_prefix(seg, n_act, ns, cpre);
-
-    const int n_seg = cpre[n_act];
-    const long long n_units = (long long)n_seg * I;
-    const long long u0 = n_units * blockIdx.x / gridDim.x;
-    const long long u1 = n_units * (blockIdx.x + 1) / gridDim.x;
-    if (u0 >= u1) return;
-
-    for (int sidx = (int)(u0 / I); (long long)sidx * I < u1; ++sidx) {
-        const int rlo = (int)max(u0 - (long long)sidx * I, 0LL);
-        const int rhi = (int)min(u1 - (long long)sidx * I, (long long)I);
-        const int j = mw_upper_index(cpre, n_act, sidx);
-        const int e = eid[j];
-        const int first = seg[j] + (sidx - cpre[j]) * ns;
-        const int nc = min(ns, seg[j + 1] - first);
-        __syncthreads();   // everyone is done with the previous segment's LDS
-        if ((int)threadIdx.x < nc) {
-            const int as = a.assign[first + threadIdx.x];
-            asg_s[threadIdx.x] = as;
-            tok_s[threadIdx.x] = as / a.slots;
-            col_s[threadIdx.x] = stage_all ? as / a.slots : (int)threadIdx.x;
-        }
-        __syncthreads();
-        if (!stage_all) {
-            bool same = true;
-            for (int k = 0; k < nc; ++k) same = same && staged_s[k] == tok_s[k];
-            if (!same) {
-                const int k = stage_b<BITS>(x, H, H, tok_s, nullptr, nc, ns, xhi, xlo, scratch);
-                if (threadIdx.x == 0) kexp_s = k;
-                if (threadIdx.x < kCols) staged_s[threadIdx.x] = (int)threadIdx.x < nc ? tok_s[threadIdx.x] : -1;
-                __syncthreads();
-            }
-        }
-        gate_up_rows<BITS>(a, h, e, rlo, rhi, nc, col_s, asg_s, xhi, xlo, ns, ldexpf(1.0f, -kexp_s), red, sg_s,
-                           su_s);
-    }
+    gate_up_units<BITS>(a, x, h, eid, seg, a.assign, n_act, ns, stage_all, blockIdx.x, gridDim.x, xhi, xlo, red, s);
 }
 
 // Down: workgroup b owns output rows [b*rows, (b+1)*rows) for the whole batch.
@@ -98,13 +46,14 @@ __global__ __launch_bounds__(kMT) void down_mfma_kernel(const float* __restrict_
     const int r1 = min(r0 + rows_per_wg, a.H);
     if (r0 >= r1) return;
     const int n_act = mw_load_worklist(a, eid, seg);
-    down_rows<BITS>(h, topk_w, a, y, r0, r1, qc, dyn, eid, seg, a.assign, n_act, scratch);
+    NoGate gate;
+    down_rows<BITS>(h, topk_w, a, y, r0, r1, qc, dyn, eid, seg, a.assign, n_act, scratch, gate);
 }
 
 template <int BITS>
 hipError_t gate_up_mfma_bits(const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
     // per staged token: hi + lo B operands and the reduction buffer
-    const size_t per_tok = staged_row_bytes<BITS>(a.H) + gate_up_red_bytes_per_token<BITS>();
+    const size_t per_tok = gate_up_lds_per_token<BITS>(a.H);
     int fit = (int)((kLdsMax - kStatic) / per_tok);
     if (fit > kCols) fit = kCols;
     if (fit < 1) return hipErrorInvalidValue;

@@ -350,6 +350,76 @@ __device__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, 
     }
 }
 
+// Per-workgroup LDS of gate_up_units (besides the dynamic staging).
+struct GateUpLds {
+    int cpre[kMaxActive + 1];                // segments of experts 0..j-1
+    int tok[kCols], asg[kCols], col[kCols], staged[kCols];
+    float scratch[kMW];
+    float sg[kNBMax * 16], su[kNBMax * 16];
+    int kexp;
+};
+
+// Stage all T tokens of x once (B slot = token index); sets s.kexp and
+// s.staged.  Used when T <= ns.
+template <int BITS>
+__device__ void stage_tokens(const float* __restrict__ x, int T, int H, int ns, half8* xhi, half8* xlo,
+                             GateUpLds& s) {
+    if (threadIdx.x < kCols) s.tok[threadIdx.x] = threadIdx.x;
+    __syncthreads();
+    const int k = stage_b<BITS>(x, H, H, s.tok, nullptr, T, ns, xhi, xlo, s.scratch);
+    if (threadIdx.x == 0) s.kexp = k;
+    __syncthreads();
+}
+
+// Gate/up + SwiGLU over the experts j < n_exp of a worklist (eid ascending,
+// seg offsets into assign; LDS or global).  Work units are (segment, row):
+// segment = (expert j, a chunk of up to ns of its tokens), enumerated
+// expert-ascending; this workgroup takes share `part` of `nparts` equal
+// contiguous shares.  With stage_all the tokens were staged by stage_tokens
+// and a segment's columns point at their tokens' slots; otherwise each
+// segment stages its own tokens (skipped when they are already staged).
+template <int BITS>
+__device__ void gate_up_units(const ExpertArgs& a, const float* __restrict__ x, float* __restrict__ h,
+                              const int* eid, const int* seg, const int* assign, int n_exp, int ns, bool stage_all,
+                              int part, int nparts, half8* xhi, half8* xlo, float* red, GateUpLds& s) {
+    const int H = a.H, I = a.I;
+    if (threadIdx.x < kCols && !stage_all) s.staged[threadIdx.x] = -1;
+    mw_segment_prefix(seg, n_exp, ns, s.cpre);
+    const int n_seg = s.cpre[n_exp];
+    const long long n_units = (long long)n_seg * I;
+    const long long u0 = n_units * part / nparts;
+    const long long u1 = n_units * (part + 1) / nparts;
+    if (u0 >= u1) return;                        // uniform over the workgroup
+    for (int sidx = (int)(u0 / I); (long long)sidx * I < u1; ++sidx) {
+        const int rlo = (int)max(u0 - (long long)sidx * I, 0LL);
+        const int rhi = (int)min(u1 - (long long)sidx * I, (long long)I);
+        const int j = mw_upper_index(s.cpre, n_exp, sidx);
+        const int e = eid[j];
+        const int first = seg[j] + (sidx - s.cpre[j]) * ns;
+        const int nc = min(ns, seg[j + 1] - first);
+        __syncthreads();   // everyone is done with the previous segment's LDS
+        if ((int)threadIdx.x < nc) {
+            const int as = assign[first + threadIdx.x];
+            s.asg[threadIdx.x] = as;
+            s.tok[threadIdx.x] = as / a.slots;
+            s.col[threadIdx.x] = stage_all ? as / a.slots : (int)threadIdx.x;
+        }
+        __syncthreads();
+        if (!stage_all) {
+            bool same = true;
+            for (int k = 0; k < nc; ++k) same = same && s.staged[k] == s.tok[k];
+            if (!same) {
+                const int k = stage_b<BITS>(x, H, H, s.tok, nullptr, nc, ns, xhi, xlo, s.scratch);
+                if (threadIdx.x == 0) s.kexp = k;
+                if (threadIdx.x < kCols) s.staged[threadIdx.x] = (int)threadIdx.x < nc ? s.tok[threadIdx.x] : -1;
+                __syncthreads();
+            }
+        }
+        gate_up_rows<BITS>(a, h, e, rlo, rhi, nc, s.col, s.asg, xhi, xlo, ns, ldexpf(1.0f, -s.kexp), red, s.sg,
+                           s.su);
+    }
+}
+
 // LDS bytes gate_up_rows needs besides the staged activations, per staged token.
 template <int BITS>
 constexpr size_t gate_up_red_bytes_per_token() {
@@ -360,6 +430,12 @@ constexpr size_t gate_up_red_bytes_per_token() {
 template <int BITS>
 __host__ __device__ constexpr size_t staged_row_bytes(int ncols) {
     return (size_t)((ncols * BITS / 8 / 16 + 3) / 4) * 4 * MfmaCodec<BITS>::NCALL * 2 * 16;
+}
+
+// LDS per staged token of gate_up_units: hi + lo B operands and the reduction.
+template <int BITS>
+__host__ __device__ constexpr size_t gate_up_lds_per_token(int H) {
+    return staged_row_bytes<BITS>(H) + gate_up_red_bytes_per_token<BITS>();
 }
 
 // ------------------------------------------------------------ down + combine
@@ -373,6 +449,15 @@ __host__ __device__ constexpr size_t staged_row_bytes(int ncols) {
 // add to a running sum; at the end the waves' sums meet in LDS in a fixed order
 // and y is written.  No atomics: deterministic.  `dyn` holds the chunk's
 // staging (down_lds_bytes).  Returns with the workgroup synchronised.
+//
+// `gate` lets a caller overlap a wait for h with the first weight loads:
+// gate.arrive() runs before the first chunk's weight loads are issued and
+// gate.wait() after, before h is first read (both once, by the whole
+// workgroup).  NoGate does nothing.
+struct NoGate {
+    __device__ void arrive() {}
+    __device__ void wait() {}
+};
 constexpr int kDownW = 4;                      // items (expert, chunk) in flight per wave
 
 template <int BITS>
@@ -381,10 +466,10 @@ __host__ __device__ constexpr size_t down_lds_bytes_per_assignment(int I) {
 }
 __host__ __device__ constexpr size_t down_lds_fixed_bytes() { return (size_t)kMW * kNBD * 256 * sizeof(float); }
 
-template <int BITS>
-__device__ void down_rows(const float* __restrict__ h, const float* topk_w, const ExpertArgs& a,
-                          float* __restrict__ y, int r0, int r1, int qc, unsigned char* dyn, const int* eid,
-                          const int* seg, const int* assign, int n_act, float* scratch) {
+template <int BITS, typename Gate>
+__device__ void down_rows(const float* h, const float* topk_w, const ExpertArgs& a, float* __restrict__ y, int r0,
+                          int r1, int qc, unsigned char* dyn, const int* eid, const int* seg, const int* assign,
+                          int n_act, float* scratch, Gate& gate) {
     using M = MfmaCodec<BITS>;
     constexpr int NCALL = M::NCALL;
     constexpr int W = kDownW;
@@ -433,10 +518,12 @@ __device__ void down_rows(const float* __restrict__ h, const float* topk_w, cons
             for (int b = 0; b < kNBD; ++b) dst[b] = ld16(base + (size_t)min(b * 16 + ln, nrows - 1) * row_bytes);
         };
         // weights first: these loads fly while h is staged
+        if (q0 == 0) gate.arrive();
         if (n_items > 0) {
 #pragma unroll
             for (int w = 0; w < W; ++w) issue(w, ring[w]);
         }
+        if (q0 == 0) gate.wait();
 
         __syncthreads();   // the previous chunk's readers are done with LDS
         for (int ql = threadIdx.x; ql < nq; ql += kMT) {
@@ -508,6 +595,10 @@ __device__ void down_rows(const float* __restrict__ h, const float* topk_w, cons
                 }
             }
         }
+    }
+    if (A == 0) {          // no chunk ran: the gate still opens once
+        gate.arrive();
+        gate.wait();
     }
     // the waves' partial sums -> LDS -> y, summed in wave order
     if (ln < T) {

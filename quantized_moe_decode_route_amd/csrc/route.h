@@ -52,8 +52,9 @@ __device__ __forceinline__ bool beats(float v, int i, float u, int j) { return v
 //   5. thread per candidate: rank among all candidates = its slot if < top_k;
 //   6. thread per slot: weight = s / (sum of the chosen s in slot order) * rsf.
 // The worklist is then a rank sort of the assignments by (expert, assignment).
-// A NaN corrected score ranks below every number (as -inf, ties by index), so
-// the ranks are always a permutation and every slot gets an expert.
+// A NaN corrected score or group score ranks below every number (as -inf,
+// ties by index), so the ranks are always permutations and every slot gets a
+// valid expert whatever the inputs hold.
 template <int TM, int EM>
 __device__ void route_select_block(const float* scores, const float* __restrict__ bias, int T, int E,
                                    int n_group, int topk_group, int top_k, int n_shared, float rsf,
@@ -80,7 +81,8 @@ __device__ void route_select_block(const float* scores, const float* __restrict_
                 m2 = fmaxf(m2, fminf(m1, v));
                 m1 = fmaxf(m1, v);
             }
-            r.gs[g] = m1 + m2;
+            const float gsum = m1 + m2;                 // NaN only from +inf + -inf
+            r.gs[g] = gsum == gsum ? gsum : -INFINITY;
         }
         __syncthreads();
         for (int g = threadIdx.x; g < n_group; g += nthr) {

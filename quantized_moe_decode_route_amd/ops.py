@@ -58,6 +58,12 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_expert_down_combine_{_b}"] = ([_P, _P, _P, _P, _I, _I, _P, _P], _I)
     _SIGS[f"moe_pack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_unpack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
+    _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
+
+# limits of the fused layer call (include/moedec.h)
+FUSED_MAX_TOKENS = 16
+FUSED_MAX_EXPERTS = 512
+FUSED_WORKSPACE_INTS = 16
 
 
 def lib() -> ctypes.CDLL:
@@ -274,25 +280,66 @@ def residual_rmsnorm(x: torch.Tensor, y: torch.Tensor | None, xn: torch.Tensor, 
 
 @dataclass
 class LayerBuffers:
-    """Every intermediate of one layer call, allocated once and reused."""
+    """Every intermediate of one layer call, allocated once and reused; the
+    workspace (zeroed here, once) holds the fused launch's barrier state."""
     route: Route
     h: torch.Tensor
     y: torch.Tensor
+    workspace: torch.Tensor   # int32 [FUSED_WORKSPACE_INTS]
 
     @staticmethod
     def allocate(T: int, H: int, I: int, E: int, top_k: int, n_shared: int, device) -> "LayerBuffers":
         f = dict(dtype=torch.float32, device=device)
         route = Route(torch.empty((T, E), **f), torch.empty((T, top_k), dtype=torch.int32, device=device),
                       torch.empty((T, top_k), **f), Worklist.empty(T, top_k, E, n_shared, device))
-        return LayerBuffers(route, torch.empty((T * (top_k + n_shared), I), **f), torch.empty((T, H), **f))
+        return LayerBuffers(route, torch.empty((T * (top_k + n_shared), I), **f), torch.empty((T, H), **f),
+                            torch.zeros(FUSED_WORKSPACE_INTS, dtype=torch.int32, device=device))
+
+    def fused_error(self) -> bool:
+        """True if a fused launch's barrier timed out (synchronises)."""
+        return bool(self.workspace[2].item() != 0)
+
+
+def fused_supported(T: int, ex: Experts) -> bool:
+    return T <= FUSED_MAX_TOKENS and ex.n_experts <= FUSED_MAX_EXPERTS
+
+
+def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
+                topk_group: int, top_k: int, rsf: float, buf: LayerBuffers) -> LayerBuffers:
+    """moe_layer_fused_q{bits}: the whole layer in one launch (outputs in buf)."""
+    T, H = x.shape
+    E = ex.n_experts
+    if router_w.shape != (E, H) or bias.shape != (E,) or H != ex.hidden:
+        raise ValueError("router_w must be [E, H], bias [E], x [T, hidden]")
+    r = buf.route
+    if r.scores.shape != (T, E) or r.topk_idx.shape != (T, top_k) or buf.y.shape != (T, H) or \
+            buf.h.shape != (T * (top_k + ex.n_shared), ex.inter) or buf.workspace.numel() < FUSED_WORKSPACE_INTS:
+        raise ValueError("buffers do not match the call's shapes")
+    s_ex, s_wl = ex.struct(), r.worklist.struct()
+    fn = getattr(lib(), f"moe_layer_fused_{_suffix(ex.bits)}")
+    st = fn(_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"), _dev(bias, torch.float32, "bias"),
+            ctypes.byref(s_ex), T, n_group, topk_group, top_k, float(rsf),
+            _dev(r.scores, torch.float32, "scores"), _dev(r.topk_idx, torch.int32, "topk_idx"),
+            _dev(r.topk_w, torch.float32, "topk_w"), ctypes.byref(s_wl), _dev(buf.h, torch.float32, "h"),
+            _dev(buf.y, torch.float32, "y"), _dev(buf.workspace, torch.int32, "workspace"), _stream(x))
+    _check(fn.__name__, st)
+    return buf
 
 
 def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
-              topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None) -> LayerBuffers:
-    """route_topk -> gate_up_silu -> down_combine on one stream; returns the buffers (y in .y)."""
+              topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None,
+              fused: bool | None = None) -> LayerBuffers:
+    """One layer on x's stream; returns the buffers (y in .y).  fused=None takes
+    the single-launch path where its limits allow, else route_topk ->
+    gate_up_silu -> down_combine; True / False force one of them."""
     T = x.shape[0]
     if buf is None:
         buf = LayerBuffers.allocate(T, ex.hidden, ex.inter, ex.n_experts, top_k, ex.n_shared, x.device)
+    if fused is None:
+        fused = fused_supported(T, ex)
+    if fused:
+        return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
+                           buf=buf)
     route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
                rsf=rsf, out=buf.route)
     gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)

@@ -42,14 +42,16 @@ def experts_dev(cfg, lay) -> ops.Experts:
     return ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits)
 
 
-def run_layer(cfg, lay, x: np.ndarray) -> dict:
-    """route + gate/up + down on the GPU; every result back on the host."""
+def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None) -> dict:
+    """One layer on the GPU (fused: the single-launch call; False: route +
+    gate/up + down; None: whichever moe_layer picks); results on the host."""
     dev = lay["router_w"].device
     xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
     ex = experts_dev(cfg, lay)
     buf = ops.moe_layer(xt, lay["router_w"], lay["bias"], ex, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                        top_k=cfg.top_k, rsf=cfg.rsf)
+                        top_k=cfg.top_k, rsf=cfg.rsf, fused=fused)
     torch.cuda.synchronize()
+    assert not buf.fused_error(), "a grid barrier of the fused launch timed out"
     wl = buf.route.worklist
     n = int(wl.n_active.item())
     return dict(scores=buf.route.scores.cpu().numpy(), idx=buf.route.topk_idx.cpu().numpy(),

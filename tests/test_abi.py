@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
 
@@ -100,6 +100,35 @@ def test_expert_calls_reject_null_structs(lib):
     assert lib.moe_expert_gate_up_silu_q4(FAKE, None, ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
     assert lib.moe_expert_down_combine_q4(FAKE, ctypes.byref(_experts()), None, FAKE, 1, 4, FAKE, None) == 1
     assert lib.moe_expert_gate_up_silu_q4(None, ctypes.byref(_experts()), ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
+
+
+def _fused(lib, suffix, ex, wl, **kw):
+    a = dict(x=FAKE, w=FAKE, b=FAKE, T=1, G=4, TG=2, K=4, rsf=2.5, scores=FAKE, idx=FAKE, wts=FAKE,
+             h=FAKE, y=FAKE, ws=FAKE)
+    a.update(kw)
+    fn = getattr(lib, f"moe_layer_fused_{suffix}")
+    return fn(a["x"], a["w"], a["b"], ctypes.byref(ex) if ex else None, a["T"], a["G"], a["TG"], a["K"], a["rsf"],
+              a["scores"], a["idx"], a["wts"], ctypes.byref(wl) if wl else None, a["h"], a["y"], a["ws"], None)
+
+
+@pytest.mark.parametrize("suffix,bits", [("q4", 4), ("q8", 8), ("q2", 2)])
+@pytest.mark.parametrize("ekw,kw,status", [
+    ({}, dict(ws=None), 1), ({}, dict(ws=FAKE + 2), 1),          # workspace missing or misaligned
+    ({}, dict(h=None), 1), ({}, dict(y=None), 1), ({}, dict(x=FAKE + 4), 1),
+    ({}, dict(K=9), 1), ({}, dict(G=16), 1), ({}, dict(rsf=float("inf")), 1),
+    (dict(bits=0), {}, 1),
+    ({}, dict(T=17), 2),                                          # past the fused token limit
+    (dict(n_experts=1024), dict(G=8, TG=4), 2),                   # past the fused expert limit
+    ({}, dict(T=65), 2),
+])
+def test_fused_call_rejects(lib, suffix, bits, ekw, kw, status):
+    ekw = dict(ekw, bits=ekw.get("bits", bits))
+    assert _fused(lib, suffix, _experts(**ekw), _wl(), **kw) == status
+
+
+def test_fused_call_requires_structs(lib):
+    assert _fused(lib, "q4", None, _wl()) == 1
+    assert _fused(lib, "q4", _experts(), None) == 1
 
 
 @pytest.mark.parametrize("bits", [4, 8, 2])

@@ -23,16 +23,18 @@ def _free():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name,steps", [("glm_t1", (0, 1)), ("glm_t3", (0,)), ("glm_t1_q8", (0,)),
-                                        ("glm_t1_q2", (0,))])
-def test_glm_layer(name, steps):
+# fused: the single-launch call the benchmark times; split: the three separate calls
+@pytest.mark.parametrize("name,steps,fused", [("glm_t1", (0, 1), True), ("glm_t1", (2,), False),
+                                              ("glm_t3", (0,), True), ("glm_t3", (1,), False),
+                                              ("glm_t1_q8", (0,), True), ("glm_t1_q2", (0,), True)])
+def test_glm_layer(name, steps, fused):
     cfg = synth.CONFIGS[name]
-    say(f"case {name}: T={cfg.tokens} bits={cfg.bits} steps={steps}")
+    say(f"case {name} {'fused' if fused else 'split'}: T={cfg.tokens} bits={cfg.bits} steps={steps}")
     lay = synth.layer_device(cfg, 0, DEV)
     rw, b = synth.router_weight(cfg, 0), synth.router_bias(cfg, 0)
     for step in steps:
         x = synth.batch_tokens(cfg, step)
-        g = run_layer(cfg, lay, x)
+        g = run_layer(cfg, lay, x, fused=fused)
         say(f"  step {step}: {g['n_active']} active experts")
         check_all(cfg, g, x, rw, b, synth.expert_loader(cfg, 0))
     del lay

@@ -40,42 +40,54 @@ def _cfg(name, seed=11):
     return synth.MoEConfig(name, T, H, I, E, G, TG, K, S, b, seed=seed)
 
 
-@pytest.mark.parametrize("name", list(SHAPES))
-def test_layer_matches_oracle(name):
+def _fits_fused(name):
+    T, H, I, E, G, TG, K, S, b = SHAPES[name]
+    return T <= ops.FUSED_MAX_TOKENS and E <= ops.FUSED_MAX_EXPERTS
+
+
+# every shape through the separate calls; those within its limits also through the fused call
+CASES = [(n, False) for n in SHAPES] + [(n, True) for n in SHAPES if _fits_fused(n)]
+
+
+@pytest.mark.parametrize("name,fused", CASES, ids=[f"{n}-{'fused' if f else 'split'}" for n, f in CASES])
+def test_layer_matches_oracle(name, fused):
     cfg = _cfg(name)
-    say(f"case {name}: {SHAPES[name]}")
+    say(f"case {name} {'fused' if fused else 'split'}: {SHAPES[name]}")
     lay = synth.layer_device(cfg, 0, DEV)
     x = synth.token_pool(cfg, cfg.tokens)
-    g = run_layer(cfg, lay, x)
+    g = run_layer(cfg, lay, x, fused=fused)
     rw, b = synth.router_weight(cfg, 0), synth.router_bias(cfg, 0)
     check_all(cfg, g, x, rw, b, synth.expert_loader(cfg, 0))
 
 
-def test_repeat_runs_are_bit_identical():
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+def test_repeat_runs_are_bit_identical(fused):
     cfg = _cfg("t3_ragged_rows_s2", seed=5)
     lay = synth.layer_device(cfg, 0, DEV)
     x = synth.token_pool(cfg, cfg.tokens)
-    a = run_layer(cfg, lay, x)
-    b = run_layer(cfg, lay, x)
+    a = run_layer(cfg, lay, x, fused=fused)
+    b = run_layer(cfg, lay, x, fused=fused)
     for k in ("scores", "idx", "w", "h", "y"):
         np.testing.assert_array_equal(a[k], b[k])
 
 
-def test_all_tied_router():
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+def test_all_tied_router(fused):
     """x = 0 and zero bias: every score is exactly 0.5; the lowest groups and
     indices are chosen and every weight is rsf / K exactly."""
     cfg = _cfg("tiny")
     lay = synth.layer_device(cfg, 0, DEV)
     lay["bias"].zero_()
     x = np.zeros((3, cfg.hidden), np.float32)
-    g = run_layer(synth.scaled(cfg, tokens=3), lay, x)
+    g = run_layer(synth.scaled(cfg, tokens=3), lay, x, fused=fused)
     assert np.all(g["scores"] == 0.5)
     assert g["idx"].tolist() == [[0, 1, 2, 3]] * 3
     assert np.all(g["w"] == np.float32(2.5 / 4))
     assert g["expert_id"].tolist() == [0, 1, 2, 3, 16]
 
 
-def test_one_hot_expert_closed_form():
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+def test_one_hot_expert_closed_form(fused):
     """K = 1, one group, +10 bias on one expert, zero shared down-scales, a
     one-hot token: the output is the closed form of that single expert."""
     cfg = synth.MoEConfig("onehot", 1, 256, 128, 16, 1, 1, 1, 1, 4, seed=3)
@@ -85,7 +97,7 @@ def test_one_hot_expert_closed_form():
     lay["s_down"][16].zero_()
     x = np.zeros((1, 256), np.float32)
     x[0, 77] = 1.25
-    g = run_layer(cfg, lay, x)
+    g = run_layer(cfg, lay, x, fused=fused)
     assert g["idx"].tolist() == [[9]]
     d = synth.expert_arrays(cfg, 0, 9)
     qg = orc.unpack_rows(d["q_gate"], 4)[:, 77].astype(np.float64)
