@@ -1,6 +1,6 @@
 """Benchmark of the routed-MoE decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload glm_t1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload glm_t1] [--split]
 
 A step is one pass of the whole path (route -> gate/up + SwiGLU -> down +
 combine) over one batch of synthetic tokens; the default workload is one
@@ -9,11 +9,15 @@ in 8 groups, top-4 groups, top-8, one shared expert, int4 codes with fp32 row
 scales) decoding one token.  Several such layers are resident in HBM and the
 steps rotate over them and over a pool of 64 tokens, so no step finds the
 previous steps' weights in the 256 MB Infinity Cache; steps are replayed from
-HIP graphs.  Prints one JSON line.
+HIP graphs.  The step is the single-launch fused call where its limits allow
+(--split: the three separate calls).  Prints one JSON line.
 
 Bytes per step (the metric's count) = the unique selected experts' packed
 codes and row scales + the input and output activations; the router weight is
-excluded and reported apart.
+excluded and reported apart.  The roofline object prices the dominant kernel
+(the fused launch; with --split, gate/up) by its algorithmic bytes: for the
+fused launch the step bytes + the router weight and bias + the scores and h
+it writes.
 """
 from __future__ import annotations
 
@@ -31,12 +35,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) and tokens/s for one int4 256-expert MoE layer"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc", "experts.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc")
+# sources each timed kernel is built from (the traffic counters are void once any changes)
+KERNEL_SRCS = {"fused": ["layer_fused.hip", "mfma.h", "route.h", "common.h"],
+               "gate_up": ["experts_mfma.hip", "mfma.h", "common.h"]}
 
 
 def step_bytes(cfg, n_active: int) -> int:
     return n_active * cfg.expert_bytes() + 2 * cfg.tokens * cfg.hidden * 4
+
+
+def router_bytes(cfg) -> int:
+    return cfg.n_experts * cfg.hidden * 4
+
+
+def fused_bytes(cfg, n_active: int) -> int:
+    """Algorithmic bytes of one fused launch: the step bytes, the router weight
+    and bias read, the scores and h written."""
+    return (step_bytes(cfg, n_active) + router_bytes(cfg) + cfg.n_experts * 4 + cfg.tokens * cfg.n_experts * 4
+            + cfg.tokens * cfg.slots * cfg.inter * 4)
 
 
 def gate_up_bytes(cfg, n_active: int) -> int:
@@ -46,20 +64,23 @@ def gate_up_bytes(cfg, n_active: int) -> int:
     return n_active * per + cfg.tokens * cfg.hidden * 4 + cfg.tokens * cfg.slots * cfg.inter * 4
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per gate/up launch measured with rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def traffic_from_profile(kind: str, workload: str):
+    """HBM bytes per launch of the timed kernel measured with rocprofv3
+    counters, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            d = json.load(f)
+            d = json.load(f).get(kind, {})
     except (OSError, ValueError):
         return None
-    if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
+    if d.get("kernel_sha") != kernel_hash(kind) or d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -112,7 +133,8 @@ def main() -> None:
     ap.add_argument("--workload", default="glm_t1")
     ap.add_argument("--layers", type=int, default=4, help="resident layers the steps rotate over")
     ap.add_argument("--graph-steps", type=int, default=8)
-    ap.add_argument("--kernel-steps", type=int, default=100, help="eager steps timing the gate/up kernel")
+    ap.add_argument("--kernel-steps", type=int, default=100, help="eager steps timing the dominant kernel")
+    ap.add_argument("--split", action="store_true", help="time the three separate calls instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
     args = ap.parse_args()
 
@@ -144,9 +166,19 @@ def main() -> None:
         b = i % n_pool
         return pool[b * T:(b + 1) * T]
 
+    fused = (not args.split) and ops.fused_supported(T, experts[0])
+    if fused:
+        try:
+            ops.layer_fused(tokens(0), layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0], **kw)
+        except ops.MoedecError as err:
+            if err.status != ops.MOEDEC_ERR_UNSUPPORTED:
+                raise
+            fused = False            # the batch does not fit the fused call's LDS plan
+
     def step(i):
         l = i % L
-        ops.moe_layer(tokens(i), layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], **kw)
+        ops.moe_layer(tokens(i), layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], fused=fused,
+                      **kw)
 
     # unique experts of every step of the period (routing is a function of (layer, token))
     n_active = np.zeros(period, np.int64)
@@ -202,33 +234,46 @@ def main() -> None:
     print(f"[bench] {args.steps} steps in {wall * 1e3:.1f} ms: {ms_per_step * 1e3:.2f} us/step, "
           f"{gbs:.0f} GB/s, {tok_s:.0f} tok/s", file=sys.stderr, flush=True)
 
-    # the dominant kernel (gate/up) timed live with HIP events on the launch stream,
-    # caches flushed before every step
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # the dominant kernel timed live with HIP events on the stream it is launched
+    # on (torch's current stream), the caches emptied of its data before every
+    # launch by reading (not writing) a 1 GiB buffer
+    kind = "fused" if fused else "gate_up"
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
     kb = []
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
     for k in range(args.kernel_steps):
         i = first + args.steps + k
         l = i % L
-        flush.fill_(float(k))
+        sink += flush.sum()
         x = tokens(i)
-        ops.route_topk(x, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route, **kw)
-        ev0[k].record()
-        ops.gate_up_silu(x, experts[l], bufs[l].route.worklist, cfg.top_k, out=bufs[l].h)
-        ev1[k].record()
-        ops.down_combine(bufs[l].h, experts[l], bufs[l].route.worklist, bufs[l].route.topk_w, cfg.top_k,
-                         out=bufs[l].y)
-        kb.append(gate_up_bytes(cfg, int(n_active[i % period])))
+        if fused:
+            ev0[k].record()
+            ops.layer_fused(x, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], **kw)
+            ev1[k].record()
+            kb.append(fused_bytes(cfg, int(n_active[i % period])))
+        else:
+            ops.route_topk(x, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route,
+                           **kw)
+            ev0[k].record()
+            ops.gate_up_silu(x, experts[l], bufs[l].route.worklist, cfg.top_k, out=bufs[l].h)
+            ev1[k].record()
+            ops.down_combine(bufs[l].h, experts[l], bufs[l].route.worklist, bufs[l].route.topk_w, cfg.top_k,
+                             out=bufs[l].y)
+            kb.append(gate_up_bytes(cfg, int(n_active[i % period])))
     torch.cuda.synchronize()
+    if fused and any(b.fused_error() for b in bufs):
+        raise SystemExit("a grid barrier of the fused launch timed out: results invalid")
     dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
-    traffic = traffic_from_profile(cfg.name)
-    roofline = {"bound": "hbm", "kernel": "gate_up_kernel", "achieved": round(achieved, 1),
+    traffic = traffic_from_profile(kind, cfg.name)
+    kname = f"layer_fused_kernel<{cfg.bits}>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_us": round(float(dur.mean() * 1e6), 2),
                 "bytes_per_launch": int(np.mean(kb))}
-    print(f"[bench] gate_up avg {dur.mean() * 1e6:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] {kname} avg {dur.mean() * 1e6:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
     base = cpu_baseline(cfg, args.cpu_budget) if args.cpu_budget > 0 else None
 
@@ -237,8 +282,8 @@ def main() -> None:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "tokens_per_s": round(tok_s, 1),
-        "bytes_per_step": int(sbytes[idx].mean()), "router_bytes_per_step": cfg.n_experts * cfg.hidden * 4,
-        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
+        "bytes_per_step": int(sbytes[idx].mean()), "router_bytes_per_step": router_bytes(cfg),
+        "config": {"workload": cfg.name, "path": "fused" if fused else "split", "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
                    "routed_experts": cfg.n_experts, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
                    "top_k": cfg.top_k, "shared_experts": cfg.n_shared, "bits": cfg.bits,
                    "resident_layers": L, "unique_experts_per_step": float(n_active[idx].mean())},

@@ -96,7 +96,7 @@ int layer_fused(int bits, const float* x, const float* router_w, const float* bi
     if (st != MOEDEC_OK) return st;
     st = route_args_ok(T, ex->hidden, ex->n_experts, n_group, topk_group, top_k, ex->n_shared, rsf);
     if (st != MOEDEC_OK) return st;
-    if (!aligned16(x) || !aligned16(router_w) || !aligned16(h) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    if (!aligned16(x) || !aligned16(router_w) || !aligned16(h) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
         return MOEDEC_ERR_INVALID_ARG;
     if (T > MOEDEC_FUSED_MAX_TOKENS || ex->n_experts > MOEDEC_FUSED_MAX_EXPERTS) return MOEDEC_ERR_UNSUPPORTED;
     f.x = x;

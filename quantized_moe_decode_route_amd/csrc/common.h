@@ -35,6 +35,34 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Largest value / smallest int over the wave, returned in every lane: DPP
+// inside each row of 16 lanes, then the four rows' results read as scalars.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    const int b = f_bits(v);
+    const float r0 = bits_f(__builtin_amdgcn_readlane(b, 0)), r1 = bits_f(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = bits_f(__builtin_amdgcn_readlane(b, 32)), r3 = bits_f(__builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+    v = min(v, dpp_i<0xB1>(v));
+    v = min(v, dpp_i<0x4E>(v));
+    v = min(v, dpp_i<0x141>(v));
+    v = min(v, dpp_i<0x140>(v));
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return min(min(r0, r1), min(r2, r3));
+}
+
 // Same for a group size known only at run time (small shapes; not hot).
 __device__ __forceinline__ float group_sum_rt(float v, int lpr) {
     for (int off = 1; off < lpr; off <<= 1) v += __shfl_xor(v, off, 64);

@@ -8,33 +8,43 @@
 // use; batch-union MoE (each unique expert of the batch read once).
 //
 // A decode step moves ~170 MB of codes (GLM-5.2 shape, one token) in a few
-// tens of microseconds, so separate kernels pay their launch gaps, start-up
-// (worklist loads, activation staging) and drain tails several times over.
-// Here one persistent workgroup per compute unit runs four phases, with two
-// grid-wide barriers:
-//   1. (needs no routing) router rows e = b, b + nwg, ...: s = sigmoid(W_r x);
-//      stage x as MFMA B operands in LDS; gate/up of the shared experts, whose
-//      tokens are known up front, over this workgroup's share of their rows;
-//   -- barrier: every score is written --
+// tens of microseconds.  Every separately started streaming phase pays a
+// ramp of a few microseconds (first loads in flight, last loads draining,
+// stragglers), so this kernel streams all expert bytes of a workgroup as ONE
+// continuous sequence.  One persistent workgroup per compute unit:
+//   1. router rows e = b, b + nwg, ...: s = sigmoid(W_r x), stored for all;
+//      arrive at the grid barrier; stage x as MFMA B operands in LDS; wait;
 //   2. every workgroup routes the batch itself from the scores (route.h), so
 //      the worklist needs no second exchange; workgroup 0 also writes the
 //      routing and worklist outputs;
-//   3. gate/up of the routed experts over this workgroup's share of rows;
-//   -- barrier: every h row is written; each workgroup arrives, issues its
-//      first down-weight loads, and only then waits --
-//   4. down + combine for this workgroup's output rows over every expert.
+//   3. the stream, through one ring of in-flight 16-byte loads per wave:
+//      gate/up of every active expert (this workgroup's rows
+//      [b*I/nwg, (b+1)*I/nwg) of each, expert by expert, its h kept in LDS and
+//      written out at once after the last block, then counted as done), then
+//      down + combine for this workgroup's output rows [b*H/nwg, (b+1)*H/nwg)
+//      over every expert, once every workgroup's h is out.
+// Inside the stream the workgroup synchronises only through LDS: loads in
+// flight are never waited for at a sync.  That matters on this GPU, where a
+// wave's loads and stores retire in issue order, so a store waited for in
+// the middle of the stream would hold up every load issued after it; hence
+// h goes out in one batch, between the gate/up and down segments.
 //
-// The barrier is a counter and a generation number in a caller-owned
-// workspace (device memory, zeroed once before first use): a workgroup reads
-// the generation, adds one to the counter; the last to arrive resets the
-// counter and advances the generation; the rest wait for the generation to
-// change.  The counter returns to zero by the end of every launch, so the
-// workspace needs no clearing between launches.  All workgroups must be
-// resident at once: the grid is one workgroup per compute unit and each asks
-// for more than half of a compute unit's LDS.  The wait is bounded: after the
-// spin limit the workgroup sets the workspace's error word and goes on, so a
-// launch that cannot be co-resident (the GPU shared with other work) ends
-// with garbage outputs and a raised flag instead of hanging.
+// Both exchanges between workgroups (scores before routing, h before down)
+// count arrivals on a 64-bit counter in a caller-owned workspace (device
+// memory, zeroed once before first use) that only ever grows: each launch
+// adds 2*nwg, so this launch's first exchange completes at the next multiple
+// of nwg above the count found at the start, and the second nwg later.  The
+// data exchanged is written with device-scope stores, which go through to
+// the device-coherent level at once, and the h exchange is read with
+// device-coherent loads; a workgroup only waits for its own stores to
+// complete before it counts itself, so no exchange writes back a cache (with
+// eight L2s, one per XCD, a release fence per workgroup would).  All
+// workgroups must be resident at once: the grid is one workgroup per compute
+// unit and each asks for more than half of a compute unit's LDS.  Every wait
+// is bounded: past the spin limit the workgroup sets the workspace's error
+// word and goes on, so a launch that cannot be co-resident (the GPU shared
+// with other work) ends with garbage outputs and a raised flag instead of
+// hanging.
 #include "mfma.h"
 #include "route.h"
 
@@ -45,12 +55,16 @@ namespace {
 using namespace mfma;
 
 constexpr int kFusedExperts = 512;                      // routed experts at most
-using FusedRoute = RouteLdsT<kCols, kFusedExperts>;
+using FusedRoute = RouteLdsT<kCols, kFusedExperts, kMW>;
 constexpr int kRowF4 = MOEDEC_MAX_DIM / 4 / kMT;        // float4 of a router row per thread
 constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a couple of seconds
+constexpr int kStreamW = 4;                             // stream items in flight per wave
+constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
+constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
+constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
 
-// workspace words
-constexpr int kWsCount = 0, kWsGen = 1, kWsError = 2, kWsSpin = 3;
+// workspace words: [0, 1] the 64-bit arrival counter, [2] error, [3] spin cap
+constexpr int kWsError = 2, kWsSpin = 3;
 
 struct FusedArgs {
     ExpertArgs a;                  // experts; its worklist pointers are unused
@@ -69,41 +83,41 @@ struct FusedArgs {
     int32_t* ws;
     int E, n_group, topk_group, n_shared;
     float rsf;
-    int ns;                        // tokens staged at once for gate/up
     int qc;                        // assignments staged at once for down
-    int down_rows;                 // output rows of one down pass of a workgroup
+    int rb;                        // gate/up blocks whose partial sums LDS holds at once
+    int off_gured, off_gsc, off_dsc, off_pairs, off_chunk, off_hprod;   // dynamic LDS layout (bytes)
 };
 
-// Split-phase grid barrier (see the file comment).  arrive(): every wave makes
-// its global writes visible device-wide, then one thread arrives.  wait():
-// that thread waits for the last arrival, with acquire ordering, then the
-// workgroup resynchronises; the acquire (by the one thread) invalidates the
-// compute unit's caches that the whole workgroup reads through.
+// Workgroup barrier for LDS only: loads in flight to registers stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Split-phase grid barrier (see the file comment).  arrive(): the workgroup's
+// stores complete, then one thread adds its arrival (no wait for the add).
+// wait(): that thread polls the counter until every workgroup has arrived,
+// invalidates the caches it reads through, and the workgroup resynchronises.
 struct GridGate {
-    int32_t* ws;
+    unsigned long long* count;
+    int32_t* error;
     int spin_max;
-    int* gen_s;                    // LDS: the generation read before arriving
+    unsigned long long base;        // the count when this launch started (a multiple of nwg)
 
     __device__ void arrive() {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's stores (device scope) have completed
         __syncthreads();
-        if (threadIdx.x == 0) {
-            const int g0 = __hip_atomic_load(ws + kWsGen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *gen_s = g0;
-            const int old = __hip_atomic_fetch_add(ws + kWsCount, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            if (old == (int)gridDim.x - 1) {
-                __hip_atomic_store(ws + kWsCount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(ws + kWsGen, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __device__ void wait() {
+    // exchange x (1 or 2) of this launch is complete
+    __device__ void wait(int x) {
         if (threadIdx.x == 0) {
-            const int g0 = *gen_s;
+            const unsigned long long target = base + (unsigned long long)x * gridDim.x;
             int n = 0;
-            while (__hip_atomic_load(ws + kWsGen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+            while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
                 if (++n >= spin_max) {
-                    __hip_atomic_store(ws + kWsError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
@@ -117,7 +131,7 @@ struct GridGate {
 // Router rows e = part, part + nparts, ... for all T tokens: every thread holds
 // its float4s of the row, dots them with each token, the wave sums by DPP and
 // the 8 waves' sums are added in wave order.
-__device__ void router_rows(const FusedArgs& f, int part, int nparts, float (*red)[kMW]) {
+__device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int nparts, float (*red)[kMW]) {
     const int H = f.a.H, T = f.a.T, E = f.E;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n4 = H >> 2;
@@ -150,9 +164,511 @@ __device__ void router_rows(const FusedArgs& f, int part, int nparts, float (*re
         if ((int)threadIdx.x < T) {
             float z = 0.f;
             for (int w = 0; w < kMW; ++w) z += red[threadIdx.x][w];
-            f.scores[(size_t)threadIdx.x * E + e] = 1.0f / (1.0f + expf(-z));
+            store_device(f.scores + (size_t)threadIdx.x * E + e, 1.0f / (1.0f + expf(-z)));
         }
         __syncthreads();
+    }
+}
+
+// Stage the down B operands of one chunk: n rows of h (row k = h[qrow[k]],
+// times qmul[k]) into hi/lo[((ch*4 + q)*ldn + k)*NCALL + c] (half8), with one
+// power-of-two scale 2^kexp; groups past the row end are zero.  h is read once,
+// with device-coherent 16-byte loads, consecutive lanes reading consecutive
+// 16 bytes (all kStageV4 loads of a thread issued before any is used); each
+// value then goes to its place in the B layout (column p of a code group is
+// element e of call c with col(c, e) = p).  n * I <= kStageV4 * 4 * kMT.
+// Returns kexp.
+template <int BITS>
+__device__ __forceinline__ int stage_h(const float* h, int h_bytes, int I, const int* qrow, const float* qmul,
+                                       int n, int ldn, half8* hi, half8* lo, float* scratch) {
+    using M = MfmaCodec<BITS>;
+    constexpr int CW = 16 * (8 / BITS);
+    const int P = I / CW;
+    const int NCH = (P + 3) / 4;
+    const int I4 = I >> 2, total4 = n * I4;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(h), (short)0, h_bytes, kBufWord3);
+    u32x4 v[kStageV4];
+#pragma unroll
+    for (int u = 0; u < kStageV4; ++u) {
+        const int i4 = threadIdx.x + u * kMT;
+        const int k = min(i4 / I4, n - 1), c4 = i4 - (i4 / I4) * I4;
+        const int off = i4 < total4 ? (qrow[k] * I4 + c4) * 16 : 0;
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < kStageV4; ++u) {
+        const int i4 = threadIdx.x + u * kMT;
+        if (i4 < total4) {
+            const float mm = fmaxf(fmaxf(fabsf(__uint_as_float(v[u].x)), fabsf(__uint_as_float(v[u].y))),
+                                   fmaxf(fabsf(__uint_as_float(v[u].z)), fabsf(__uint_as_float(v[u].w))));
+            m = fmaxf(m, fabsf(qmul[i4 / I4]) * mm);
+        }
+    }
+    const int kexp = f16_exponent(block_max(m, scratch));
+    const float sc = ldexpf(1.0f, kexp);
+    _Float16* hh = reinterpret_cast<_Float16*>(hi);
+    _Float16* hl = reinterpret_cast<_Float16*>(lo);
+#pragma unroll
+    for (int u = 0; u < kStageV4; ++u) {
+        const int i4 = threadIdx.x + u * kMT;
+        if (i4 < total4) {
+            const int k = i4 / I4, col0 = (i4 - k * I4) * 4;
+            const float sk = qmul[k] * sc;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int col = col0 + e4;
+                const int g = col / CW, p = col - g * CW;
+                int c = 0, e = 0;
+                M::place(p, c, e);
+                const float x = __uint_as_float(v[u][e4]) * sk;
+                const _Float16 hx = (_Float16)x;
+                const int dst = ((g * ldn + k) * M::NCALL + c) * 8 + e;
+                hh[dst] = hx;
+                hl[dst] = (_Float16)(x - (float)hx);
+            }
+        }
+    }
+    const int pad = (NCH * 4 - P) * n * M::NCALL;
+    for (int uu = threadIdx.x; uu < pad; uu += kMT) {
+        const int c = uu % M::NCALL;
+        const int k = (uu / M::NCALL) % n;
+        const int g = P + uu / (M::NCALL * n);
+        half8 z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
+        hi[(g * ldn + k) * M::NCALL + c] = z;
+        lo[(g * ldn + k) * M::NCALL + c] = z;
+    }
+    return kexp;
+}
+
+// Exclusive prefix over j < n of cnt(j) into out[0..n] (out[n] = total).
+template <typename Cnt>
+__device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
+    __shared__ int wtot[kMW];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int per = (n + 1 + kMT - 1) / kMT;
+    const int j0 = threadIdx.x * per, j1 = min(j0 + per, n);
+    int local = 0;
+    for (int j = j0; j < j1; ++j) local += cnt(j);
+    int inc = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += u;
+    }
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    int run = inc - local;
+    for (int w = 0; w < wave; ++w) run += wtot[w];
+    for (int j = j0; j < min(j0 + per, n + 1); ++j) {
+        out[j] = run;
+        if (j < n) run += cnt(j);
+    }
+    __syncthreads();
+}
+
+// Phase 3 (see the file comment).  Items of a wave, all waves alike:
+//   gate/up: for each active expert j, each 16-row block of this workgroup's
+//            rows, each of the wave's K-chunks -> loads of gate and up;
+//   down:    for each (expert, staging chunk) pair, each of the wave's
+//            K-chunks -> loads of the two 16-row blocks of output rows.
+// A wave's K-chunks are c = wave*nk + k, k < nk; chunks past the row end are
+// computed against zero activations.  Every load is issued at a clamped
+// (valid) address, so every item issues exactly two loads and the wait
+// counts before each use are static.
+template <int BITS>
+__device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, float x_unscale,
+                                       float* scratch, GridGate& gate) {
+    using M = MfmaCodec<BITS>;
+    constexpr int NCALL = M::NCALL;
+    constexpr int W = kStreamW;
+    const ExpertArgs& a = f.a;
+    const int H = a.H, I = a.I, T = a.T, K = a.top_k, slots = a.slots;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int nwg = gridDim.x, b = blockIdx.x;
+    const int n_act = r.n_active;
+    const int A = r.seg[n_act];
+    const int* eid = r.eid;
+    const int* seg = r.seg;
+    const int* asn = r.assign;
+    // gate/up geometry: this workgroup's rows [gr0, gr0 + rg) of every expert
+    const int rbg = H * BITS / 8, Pg = rbg >> 4, NCHg = (Pg + 3) >> 2, nkg = (NCHg + kMW - 1) / kMW;
+    const int gr0 = (int)((long long)b * I / nwg);
+    const int rg = (int)((long long)(b + 1) * I / nwg) - gr0;
+    const int nbg = (rg + 15) >> 4;
+    // down geometry: output rows [dr0, dr0 + rd), rd <= 32
+    const int rbd = I * BITS / 8, Pd = rbd >> 4, NCHd = (Pd + 3) >> 2, nkd = (NCHd + kMW - 1) / kMW;
+    const int dr0 = (int)((long long)b * H / nwg);
+    const int rd = (int)((long long)(b + 1) * H / nwg) - dr0;
+    const int qc = f.qc;
+    // LDS
+    const half8* xhi = reinterpret_cast<const half8*>(dyn);
+    const half8* xlo = xhi + (size_t)NCHg * 4 * T * NCALL;
+    half8* hhi = reinterpret_cast<half8*>(dyn);                   // replaces x once gate/up is done
+    half8* hlo = hhi + (size_t)NCHd * 4 * qc * NCALL;
+    float* dred = reinterpret_cast<float*>(dyn);                  // replaces h at the very end
+    float* gred = reinterpret_cast<float*>(dyn + f.off_gured);    // [rb][kMW][2][16][T] + counters
+    // per partial-sum slot: waves arrived at its block, and blocks finalised through it
+    const int rb = f.rb;
+    int* slot_cnt = reinterpret_cast<int*>(gred + (size_t)rb * kMW * 2 * 16 * T);
+    int* slot_done = slot_cnt + rb;
+    float* gsc = reinterpret_cast<float*>(dyn + f.off_gsc);       // [n_act][2][rg]
+    float* hprod = reinterpret_cast<float*>(dyn + f.off_hprod);   // [n_act][rg][T]: this workgroup's h
+    float* dsc = reinterpret_cast<float*>(dyn + f.off_dsc);       // [n_act][rd]
+    int* pstart = reinterpret_cast<int*>(dyn + f.off_pairs);      // [n_act + 1]
+    int* qrow = reinterpret_cast<int*>(dyn + f.off_chunk);        // [qc]
+    float* qmul = reinterpret_cast<float*>(qrow + qc);            // [qc]
+    int* amap = reinterpret_cast<int*>(qmul + qc);                // [qc][16]
+    int* ctab = amap + qc * kCols;                                 // [chunks + 1][3]
+
+    // row scales of every active expert for this workgroup's rows: LDS from here on
+    for (int i = threadIdx.x; i < n_act * rg; i += kMT) {
+        const int j = i / rg, rr = i - j * rg;
+        const size_t src = (size_t)eid[j] * I + gr0 + rr;
+        gsc[(j * 2 + 0) * rg + rr] = a.s_gate[src];
+        gsc[(j * 2 + 1) * rg + rr] = a.s_up[src];
+    }
+    for (int i = threadIdx.x; i < n_act * rd; i += kMT) {
+        const int j = i / rd, rr = i - j * rd;
+        dsc[j * rd + rr] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
+    }
+    // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc
+    block_prefix(n_act, [&](int j) { return (seg[j + 1] - 1) / qc - seg[j] / qc + 1; }, pstart);
+    // Positions: the gate/up items, then each down chunk's items, every segment
+    // padded to a multiple of W, so a segment starts at ring slot 0 and its
+    // start (h out, chunk staging) runs between rounds, outside the unrolled
+    // ring body.  Padding positions issue loads of a real item and compute
+    // nothing.
+    const int Ngu = n_act * nbg * nkg;
+    const int Gpad = (Ngu + W - 1) / W * W;
+    const int nchunk = rd > 0 ? (A + qc - 1) / qc : 0;
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int q = 0; q < nchunk; ++q) {
+            const int jf = mw_upper_index(seg, n_act, q * qc);
+            const int jl = mw_upper_index(seg, n_act, min(A, (q + 1) * qc) - 1);
+            const int p0 = pstart[jf] + (q - seg[jf] / qc), p1 = pstart[jl] + (q - seg[jl] / qc);
+            ctab[3 * q] = run;                        // first position (after Gpad)
+            ctab[3 * q + 1] = (p1 - p0 + 1) * nkd;    // items
+            ctab[3 * q + 2] = p0;                     // first pair
+            run += (ctab[3 * q + 1] + W - 1) / W * W;
+        }
+        ctab[3 * nchunk] = run;
+    }
+    __syncthreads();
+    const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
+    if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
+    if (Np == 0) return;
+
+    // Two cursors walk the positions in order, one W positions ahead issuing
+    // loads, one computing; a cursor advances by counting (no division or
+    // search per item) and reads LDS only when its expert changes.  All
+    // fields are uniform over the workgroup.
+    struct Cursor {
+        int kind;                   // 0 gate/up, 1 down
+        int pos;                    // position within the segment
+        int q;                      // down chunk
+        bool valid;                 // a real item (not padding)
+        int j, blk, k;              // expert, gate/up block, K-chunk of the wave
+        int pair, pend;             // down pair; first pair of the next expert
+    };
+    auto enter_chunk = [&](Cursor& c, int q) {
+        c.kind = 1;
+        c.pos = 0;
+        c.q = q;
+        c.pair = ctab[3 * q + 2];
+        c.j = mw_upper_index(pstart, n_act, c.pair);
+        c.pend = pstart[c.j + 1];
+        c.k = 0;
+        c.valid = ctab[3 * q + 1] > 0;
+    };
+    auto start = [&](Cursor& c) {
+        c.blk = c.k = c.j = 0;
+        c.pair = c.pend = c.q = 0;
+        if (Gpad > 0) {
+            c.kind = 0;
+            c.pos = 0;
+            c.valid = true;
+        } else {
+            enter_chunk(c, 0);
+        }
+    };
+    auto advance = [&](Cursor& c) {
+        ++c.pos;
+        if (c.kind == 0) {
+            c.valid = c.pos < Ngu;
+            if (c.valid && ++c.k == nkg) {
+                c.k = 0;
+                if (++c.blk == nbg) {
+                    c.blk = 0;
+                    ++c.j;
+                }
+            }
+            if (c.pos == Gpad && nchunk > 0) enter_chunk(c, 0);
+        } else {
+            c.valid = c.pos < ctab[3 * c.q + 1];
+            if (c.valid && ++c.k == nkd) {
+                c.k = 0;
+                if (++c.pair == c.pend) {
+                    ++c.j;
+                    c.pend = pstart[c.j + 1];
+                }
+            }
+            const int padded = (ctab[3 * c.q + 1] + W - 1) / W * W;
+            if (c.pos == padded && c.q + 1 < nchunk) enter_chunk(c, c.q + 1);
+        }
+    };
+    // (past the last position a cursor stays on the last real item: loads stay valid)
+
+    auto issue = [&](const Cursor& c, uint4* dst) {
+        if (c.kind == 0) {
+            const int cc = min(wave * nkg + c.k, NCHg - 1);
+            const int grp = min(cc * 4 + lq, Pg - 1);
+            const int rows_blk = min(16, rg - c.blk * 16);
+            const size_t row = (size_t)eid[c.j] * I + gr0 + c.blk * 16 + min(ln, rows_blk - 1);
+            const size_t off = row * rbg + grp * 16;
+            dst[0] = ld16(a.w_gate + off);
+            dst[1] = ld16(a.w_up + off);
+        } else {
+            const int cc = min(wave * nkd + c.k, NCHd - 1);
+            const int grp = min(cc * 4 + lq, Pd - 1);
+            const uint8_t* base = a.w_down + ((size_t)eid[c.j] * H + dr0) * rbd + grp * 16;
+            dst[0] = ld16(base + (size_t)min(ln, rd - 1) * rbd);
+            dst[1] = ld16(base + (size_t)min(16 + ln, rd - 1) * rbd);
+        }
+    };
+
+    floatx4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
+    floatx4 acc[kNBD], tot[kNBD];
+#pragma unroll
+    for (int bb = 0; bb < kNBD; ++bb) acc[bb] = tot[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float d_unscale = 1.f;
+    int chunk_first = 0;            // first expert of the staged chunk
+    // per-expert state of the computing cursor
+    int cj = -1, cs0 = 0, cnc = 0, ctok = 0, cbq = -1;
+
+    // Columns of the MFMA output that no token uses hold garbage and are never
+    // read, so B operands need no zeroing; chunks past the row end are skipped.
+    auto gu_item = [&](const Cursor& c, const uint4* cur) {
+        if (c.j != cj) {
+            cj = c.j;
+            cs0 = seg[cj];
+            cnc = seg[cj + 1] - cs0;
+            ctok = asn[cs0 + min(ln, cnc - 1)] / slots;          // B slot of this lane's column
+        }
+        const int ch = wave * nkg + c.k;
+        if (ch < NCHg) {
+            half8 bh[NCALL], bl[NCALL];
+#pragma unroll
+            for (int cc = 0; cc < NCALL; ++cc) {
+                const int src = ((ch * 4 + lq) * T + ctok) * NCALL + cc;
+                bh[cc] = xhi[src];
+                bl[cc] = xlo[src];
+            }
+#pragma unroll
+            for (int cc = 0; cc < NCALL; ++cc) {
+                const half8 ag = a_operand<BITS>(cur[0], cc);
+                accg = mfma::mfma(ag, bh[cc], accg);
+                accg = mfma::mfma(ag, bl[cc], accg);
+                const half8 au = a_operand<BITS>(cur[1], cc);
+                accu = mfma::mfma(au, bh[cc], accu);
+                accu = mfma::mfma(au, bl[cc], accu);
+            }
+        }
+        if (c.k == nkg - 1) {
+            // This wave's part of the block is done.  No workgroup barrier here
+            // (every one would wait for the slowest wave's loads): the wave leaves
+            // its partial sums in the block's LDS slot and counts itself; the
+            // last of the 8 waves to arrive adds them up, in wave order, and
+            // writes h = silu(g) * v for the block.  A slot is reused rb blocks
+            // later, once its block is finalised.
+            const int bidx = c.j * nbg + c.blk;
+            const int slot = bidx % rb;
+            float* part = gred + (size_t)slot * kMW * 2 * 16 * T;
+            if (bidx >= rb) {
+                int n = 0;
+                while (__hip_atomic_load(slot_done + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                       bidx - rb + 1) {
+                    if (++n > (1 << 24)) {
+                        __hip_atomic_store(f.ws + kWsError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (ln < cnc) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = accg[ii];
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = accu[ii];
+                }
+            }
+            accg = accu = floatx4{0.f, 0.f, 0.f, 0.f};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            int arrived = 0;
+            if (lane == 0)
+                arrived = __hip_atomic_fetch_add(slot_cnt + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            arrived = __shfl(arrived, 0, kWave);
+            if (arrived == kMW - 1) {   // the last wave: finalise the block
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                const int rows_blk = min(16, rg - c.blk * 16);
+                for (int idx = lane; idx < rows_blk * cnc; idx += kWave) {
+                    const int rr = idx / cnc, n = idx - rr * cnc;
+                    float gs = 0.f, vs = 0.f;
+                    for (int w = 0; w < kMW; ++w) {
+                        gs += part[((w * 2 + 0) * 16 + rr) * T + n];
+                        vs += part[((w * 2 + 1) * 16 + rr) * T + n];
+                    }
+                    const int row = c.blk * 16 + rr;
+                    const float gv = gs * x_unscale * gsc[(cj * 2 + 0) * rg + row];
+                    const float uv = vs * x_unscale * gsc[(cj * 2 + 1) * rg + row];
+                    hprod[(cj * rg + row) * T + n] = gv / (1.0f + __expf(-gv)) * uv;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                if (lane == 0) {
+                    __hip_atomic_store(slot_cnt + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(slot_done + slot, bidx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+        }
+    };
+
+    auto dn_item = [&](const Cursor& c, const uint4* cur) {
+        if (c.j != cj) {
+            cj = c.j;
+            cbq = amap[(cj - chunk_first) * kCols + ln];      // staged slot of this lane's token, or -1
+        }
+        const int ch = wave * nkd + c.k;
+        if (ch < NCHd) {
+            const int slot = max(cbq, 0);
+            half8 bh[NCALL], bl[NCALL];
+#pragma unroll
+            for (int cc = 0; cc < NCALL; ++cc) {
+                const int src = ((ch * 4 + lq) * qc + slot) * NCALL + cc;
+                bh[cc] = hhi[src];
+                bl[cc] = hlo[src];
+            }
+#pragma unroll
+            for (int bb = 0; bb < kNBD; ++bb) {
+#pragma unroll
+                for (int cc = 0; cc < NCALL; ++cc) {
+                    const half8 av = a_operand<BITS>(cur[bb], cc);
+                    acc[bb] = mfma::mfma(av, bh[cc], acc[bb]);
+                    acc[bb] = mfma::mfma(av, bl[cc], acc[bb]);
+                }
+            }
+        }
+        if (c.k == nkd - 1) {         // this pair is complete: scale rows, add (tokens routed here only)
+            if (cbq >= 0) {
+#pragma unroll
+                for (int bb = 0; bb < kNBD; ++bb) {
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        const int rr = min(bb * 16 + 4 * lq + i2, rd - 1);
+                        tot[bb][i2] += (dsc[cj * rd + rr] * d_unscale) * acc[bb][i2];
+                    }
+                }
+            }
+#pragma unroll
+            for (int bb = 0; bb < kNBD; ++bb) acc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // segment starts, between rounds
+    auto flush_h = [&]() {            // all of this workgroup's h: out at once (device scope), then counted
+        for (int idx = threadIdx.x; idx < n_act * rg * T; idx += kMT) {
+            const int jj = idx / (rg * T), rem = idx - jj * rg * T;
+            const int row = rem / T, n = rem - row * T;
+            if (n < seg[jj + 1] - seg[jj])
+                store_device(f.h + (size_t)asn[seg[jj] + n] * I + gr0 + row, hprod[idx]);
+        }
+        gate.arrive();
+    };
+    auto dn_stage = [&](int q) {
+        lds_barrier();                // everyone is done with the previous B operands
+        const int q0 = q * qc, q1 = min(A, q0 + qc), nq = q1 - q0;
+        const int jf = mw_upper_index(seg, n_act, q0);
+        const int jl = mw_upper_index(seg, n_act, q1 - 1);
+        for (int ql = threadIdx.x; ql < nq; ql += kMT) {
+            const int as = asn[q0 + ql];
+            const int t = as / slots, sl = as - t * slots;
+            qrow[ql] = as;
+            qmul[ql] = sl < K ? r.selw[t * K + sl] : 1.0f;
+        }
+        for (int i = threadIdx.x; i < (jl - jf + 1) * kCols; i += kMT) amap[i] = -1;
+        __syncthreads();
+        for (int ql = threadIdx.x; ql < nq; ql += kMT) {
+            const int jj = mw_upper_index(seg, n_act, q0 + ql);
+            amap[(jj - jf) * kCols + qrow[ql] / slots] = ql;
+        }
+        if (q == 0) gate.wait(2);     // every workgroup's h is out
+        const int kexp = stage_h<BITS>(f.h, A * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, scratch);
+        __syncthreads();
+        d_unscale = ldexpf(1.0f, -kexp);
+        chunk_first = jf;
+        cj = -1;                      // the computing cursor reloads its expert's column map
+    };
+
+    for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
+    __syncthreads();
+
+    Cursor ci, cc_;
+    start(ci);
+    start(cc_);
+    uint4 ring[W][2];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        issue(ci, ring[w]);
+        advance(ci);
+    }
+    // gate/up segment, then the down chunks: two loops, so each hot loop holds
+    // one kind of item (the ring and both cursors carry over, Gpad % W == 0)
+    for (int base = 0; base < Gpad; base += W) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const uint4 cur[2] = {ring[w][0], ring[w][1]};
+            issue(ci, ring[w]);
+            advance(ci);
+            if (cc_.valid) gu_item(cc_, cur);
+            advance(cc_);
+        }
+    }
+    __syncthreads();                  // every block finalised (hprod complete)
+    if (Ngu > 0) flush_h();
+    cj = -1;
+    int next_chunk = 0;
+    for (int base = Gpad; base < Np; base += W) {
+        if (next_chunk < nchunk && base == Gpad + ctab[3 * next_chunk]) dn_stage(next_chunk++);
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const uint4 cur[2] = {ring[w][0], ring[w][1]};
+            issue(ci, ring[w]);
+            advance(ci);
+            if (cc_.valid) dn_item(cc_, cur);
+            advance(cc_);
+        }
+    }
+
+    // the waves' partial sums -> LDS -> y, summed in wave order
+    if (nchunk == 0) return;
+    lds_barrier();
+    if (ln < T) {
+#pragma unroll
+        for (int bb = 0; bb < kNBD; ++bb)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) dred[((wave * kNBD + bb) * 16 + 4 * lq + i2) * 16 + ln] = tot[bb][i2];
+    }
+    lds_barrier();
+    for (int idx = threadIdx.x; idx < rd * T; idx += kMT) {
+        const int t = idx / rd, rr = idx - t * rd;
+        const int bb = rr >> 4, r16 = rr & 15;
+        float s = 0.f;
+        for (int w = 0; w < kMW; ++w) s += dred[((w * kNBD + bb) * 16 + r16) * 16 + t];
+        f.y[(size_t)t * H + dr0 + rr] = s;
     }
 }
 
@@ -161,40 +677,31 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     constexpr int NCALL = MfmaCodec<BITS>::NCALL;
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ FusedRoute r;
-    __shared__ GateUpLds s;
     __shared__ float gemv_red[kCols][kMW];
-    __shared__ int sh_eid[8], sh_seg[9], sh_assign[8 * kCols];
-    __shared__ int gen_s;
+    __shared__ int tok_s[kCols];
+    __shared__ float scratch[kMW];
 
     const ExpertArgs& a = f.a;
     const int T = a.T, H = a.H, K = a.top_k, S = f.n_shared, E = f.E;
-    const int NCH = ((H * BITS / 8) / 16 + 3) / 4;
+    const int NCHg = ((H * BITS / 8) / 16 + 3) / 4;
     half8* xhi = reinterpret_cast<half8*>(dyn);
-    half8* xlo = xhi + (size_t)NCH * 4 * f.ns * NCALL;
-    float* red = reinterpret_cast<float*>(xlo + (size_t)NCH * 4 * f.ns * NCALL);
-    const bool stage_all = T <= f.ns;
+    half8* xlo = xhi + (size_t)NCHg * 4 * T * NCALL;
     const int spin = f.ws[kWsSpin] > 0 ? f.ws[kWsSpin] : kSpinDefault;
-    GridGate gate{f.ws, spin, &gen_s};
+    unsigned long long* count = reinterpret_cast<unsigned long long*>(f.ws);
+    // the count is a multiple of nwg between launches: this launch's barrier completes at the next one
+    const unsigned long long found = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    GridGate gate{count, f.ws + kWsError, spin, found / gridDim.x * gridDim.x};
 
-    // ---- phase 1: router rows, staging, shared experts' gate/up
+    // ---- phase 1
     router_rows(f, blockIdx.x, gridDim.x, gemv_red);
-    if (stage_all) stage_tokens<BITS>(f.x, T, H, f.ns, xhi, xlo, s);
-    for (int i = threadIdx.x; i < S * T; i += kMT) {   // the shared experts' worklist: every token
-        const int j = i / T, t = i - j * T;
-        sh_assign[i] = t * a.slots + K + j;
-    }
-    if ((int)threadIdx.x <= S) {
-        if ((int)threadIdx.x < S) sh_eid[threadIdx.x] = E + threadIdx.x;
-        sh_seg[threadIdx.x] = threadIdx.x * T;
-    }
-    __syncthreads();
-    gate_up_units<BITS>(a, f.x, f.h, sh_eid, sh_seg, sh_assign, S, f.ns, stage_all, blockIdx.x, gridDim.x, xhi,
-                        xlo, red, s);
-
-    // ---- barrier 1, phase 2: routing (every workgroup, identically)
     gate.arrive();
-    gate.wait();
-    route_select_block<kCols, kFusedExperts>(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
+    if (threadIdx.x < kCols) tok_s[threadIdx.x] = threadIdx.x;
+    __syncthreads();
+    const int kexp_x = stage_b<BITS>(f.x, H, H, tok_s, nullptr, T, T, xhi, xlo, scratch);
+    gate.wait(1);
+
+    // ---- phase 2: routing (every workgroup, identically)
+    route_select_block(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < T * K; i += kMT) {
             f.topk_idx[i] = r.sel[i];
@@ -209,86 +716,71 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
         for (int i = threadIdx.x; i < T * a.slots; i += kMT) f.wl_assign[i] = r.assign[i];
     }
 
-    // ---- phase 3: routed experts' gate/up (the shared ones are the last S worklist entries)
-    gate_up_units<BITS>(a, f.x, f.h, r.eid, r.seg, r.assign, r.n_active - S, f.ns, stage_all, blockIdx.x,
-                        gridDim.x, xhi, xlo, red, s);
-
-    // ---- barrier 2 (inside the first down pass), phase 4: down + combine
-    struct Once {
-        GridGate& g;
-        bool done;
-        __device__ void arrive() {
-            if (!done) g.arrive();
-        }
-        __device__ void wait() {
-            if (!done) g.wait();
-            done = true;
-        }
-    } once{gate, false};
-    for (int r0 = blockIdx.x * f.down_rows; r0 < H; r0 += gridDim.x * f.down_rows) {
-        const int r1 = min(r0 + f.down_rows, H);
-        down_rows<BITS>(f.h, r.selw, a, f.y, r0, r1, f.qc, dyn, r.eid, r.seg, r.assign, r.n_active, s.scratch,
-                        once);
-    }
-    if (!once.done) {          // no rows here: still arrive, so the others can go on
-        once.arrive();
-        once.wait();
-    }
+    // ---- phase 3: the stream
+    stream<BITS>(f, r, dyn, ldexpf(1.0f, -kexp_x), scratch, gate);
 }
 
-struct FusedPlan {
-    int ns, qc, rows;
-    size_t lds;
-};
+size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
+// Dynamic LDS of a launch: [staging: x, then each down chunk's h, then the
+// final reduction][gate/up reduction][gate/up scales][down scales][pair
+// starts][chunk tables]; the chunk size qc is the largest that fits.
 template <int BITS>
-hipError_t fused_plan(const FusedArgs& f, int nwg, FusedPlan& p) {
-    static size_t static_lds = 0;        // the kernel's static LDS, read once
+hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st) {
     auto k = layer_fused_kernel<BITS>;
+    static size_t static_lds = 0;        // the kernel's static LDS, read once
     if (static_lds == 0) {
         hipFuncAttributes attr;
         hipError_t err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k));
         if (err != hipSuccess) return err;
         static_lds = (attr.sharedSizeBytes + 1023) & ~(size_t)1023;
     }
+    const int nwg = cu_count();
+    const int H = l.ex.H, I = l.ex.I, T = l.T;
+    const int rg = (I + nwg - 1) / nwg, rd = (H + nwg - 1) / nwg;
+    if (rd > kNBD * 16) return hipErrorInvalidValue;             // more output rows than a pass holds
+    const int A = T * l.ex.slots;
+    const int max_active = l.ex.max_active;
     if (static_lds + kLdsOnePerCu > kLdsMax) return hipErrorInvalidValue;
     const size_t avail = kLdsMax - static_lds;
-    const size_t per_tok = gate_up_lds_per_token<BITS>(f.a.H);
-    int fit = (int)(avail / per_tok);
-    if (fit > kCols) fit = kCols;
-    if (fit < 1) return hipErrorInvalidValue;
-    p.ns = f.a.T < fit ? f.a.T : fit;
-    const size_t fixed = down_lds_fixed_bytes();
-    const size_t per_q = down_lds_bytes_per_assignment<BITS>(f.a.I);
-    if (avail < fixed + per_q) return hipErrorInvalidValue;
-    const int A = f.a.T * f.a.slots;
-    p.qc = (int)((avail - fixed) / per_q);
-    if (p.qc > A) p.qc = A;
-    int rows = (f.a.H + nwg - 1) / nwg;
-    if (rows < 16) rows = 16;
-    if (rows > kNBD * 16) rows = kNBD * 16;
-    p.rows = rows;
-    size_t lds = (size_t)p.ns * per_tok;
-    const size_t lds_down = fixed + (size_t)p.qc * per_q;
-    if (lds < lds_down) lds = lds_down;
+    const size_t x_bytes = align16(staged_row_bytes<BITS>(H) * T);
+    const size_t dred_bytes = (size_t)kMW * kNBD * 256 * sizeof(float);
+    const int n_blocks = max_active * ((rg + 15) / 16);
+    const int rb = n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8;   // partial-sum slots
+    const size_t gured = align16((size_t)rb * kMW * 2 * 16 * T * sizeof(float) + 2 * rb * sizeof(int));
+    const size_t gsc = align16((size_t)max_active * rg * 2 * sizeof(float));
+    const size_t dsc = align16((size_t)max_active * rd * sizeof(float));
+    const size_t pairs = align16((size_t)(max_active + 1) * sizeof(int));
+    const size_t hprod = align16((size_t)max_active * rg * T * sizeof(float));
+    const size_t fixed = gured + gsc + dsc + pairs + hprod;
+    auto staging = [&](int q) {
+        size_t s = align16(staged_row_bytes<BITS>(I) * q);
+        if (s < x_bytes) s = x_bytes;
+        if (s < dred_bytes) s = dred_bytes;
+        return s;
+    };
+    auto total = [&](int q) {
+        const size_t chunks = (size_t)(A + q - 1) / q;
+        return staging(q) + fixed + align16(((size_t)q * (2 + kCols) + 3 * (chunks + 1)) * sizeof(int));
+    };
+    int qc = A;
+    if ((size_t)qc * I > (size_t)kStageV4 * 4 * kMT) qc = kStageV4 * 4 * kMT / I;   // a chunk's h fits registers
+    while (qc > 0 && total(qc) > avail) --qc;
+    if (qc < 1) return hipErrorInvalidValue;
+    const size_t stg = staging(qc);
+    f.qc = qc;
+    f.rb = rb;
+    f.off_gured = (int)stg;
+    f.off_gsc = (int)(stg + gured);
+    f.off_dsc = (int)(stg + gured + gsc);
+    f.off_pairs = (int)(stg + gured + gsc + dsc);
+    f.off_hprod = (int)(stg + gured + gsc + dsc + pairs);
+    f.off_chunk = (int)(stg + fixed);
+    size_t lds = total(qc);
     if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
-    p.lds = lds;
-    return hipSuccess;
-}
-
-template <int BITS>
-hipError_t layer_fused_bits(FusedArgs f, hipStream_t st) {
-    const int nwg = cu_count();
-    FusedPlan p;
-    hipError_t err = fused_plan<BITS>(f, nwg, p);
+    hipError_t err = allow_lds(k, lds);
     if (err != hipSuccess) return err;
-    f.ns = p.ns;
-    f.qc = p.qc;
-    f.down_rows = p.rows;
-    auto k = layer_fused_kernel<BITS>;
-    err = allow_lds(k, p.lds);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k, dim3(nwg), dim3(kMT), p.lds, st, f);
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(kMT), lds, st, f);
     return hipGetLastError();
 }
 
@@ -317,9 +809,9 @@ hipError_t launch_layer_fused(int bits, const FusedLayerArgs& l, hipStream_t st)
     f.n_shared = l.n_shared;
     f.rsf = l.rsf;
     switch (bits) {
-        case 4: return layer_fused_bits<4>(f, st);
-        case 8: return layer_fused_bits<8>(f, st);
-        case 2: return layer_fused_bits<2>(f, st);
+        case 4: return layer_fused_bits<4>(f, l, st);
+        case 8: return layer_fused_bits<8>(f, l, st);
+        case 2: return layer_fused_bits<2>(f, l, st);
         default: return hipErrorInvalidValue;
     }
 }

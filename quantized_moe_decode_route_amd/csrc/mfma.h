@@ -54,6 +54,10 @@ struct MfmaCodec<4> {
     static constexpr int NB = 5;          // 16-row blocks per gate/up group
     static constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64086408u, kBias = 0x64086408u;   // 1032
     __device__ static int col(int c, int e) { return 8 * c + (e >> 1) + 4 * (e & 1); }
+    __device__ static void place(int p, int& c, int& e) {      // col(c, e) == p
+        c = p >> 3;
+        e = 2 * (p & 3) + ((p >> 2) & 1);
+    }
 };
 template <>
 struct MfmaCodec<8> {
@@ -61,6 +65,10 @@ struct MfmaCodec<8> {
     static constexpr int NB = 5;
     static constexpr uint32_t kMask = 0x00FF00FFu, kMagic = 0x64806480u, kBias = 0x64806480u;   // 1152
     __device__ static int col(int c, int e) { return 8 * c + 4 * (e >> 2) + ((e >> 1) & 1) + 2 * (e & 1); }
+    __device__ static void place(int p, int& c, int& e) {      // col(c, e) == p
+        c = p >> 3;
+        e = 4 * ((p >> 2) & 1) + 2 * (p & 1) + ((p >> 1) & 1);
+    }
 };
 template <>
 struct MfmaCodec<2> {
@@ -69,6 +77,10 @@ struct MfmaCodec<2> {
     static constexpr uint32_t kMask = 0x00030003u, kMagic = 0x64026402u, kBias = 0x64026402u;   // 1026
     // call c = 2*dword + half; element e = 2*s + t is field 4*half + s + 8*t of the dword
     __device__ static int col(int c, int e) { return 16 * (c >> 1) + 4 * (c & 1) + (e >> 1) + 8 * (e & 1); }
+    __device__ static void place(int p, int& c, int& e) {      // col(c, e) == p
+        c = 2 * (p >> 4) + ((p >> 2) & 1);
+        e = 2 * (p & 3) + ((p >> 3) & 1);
+    }
 };
 
 __device__ __forceinline__ uint32_t q_pair(uint32_t w, int sh, uint32_t mask, uint32_t magic, uint32_t bias) {
@@ -156,7 +168,7 @@ __device__ __forceinline__ int f16_exponent(float m) {
 }
 
 // cpre[j] = segments (chunks of up to `cmax` tokens) of experts 0..j-1, j in [0, n].
-__device__ void mw_segment_prefix(const int* seg, int n, int cmax, int* cpre) {
+__device__ __forceinline__ void mw_segment_prefix(const int* seg, int n, int cmax, int* cpre) {
     __shared__ int wtot[kMW];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int per = (n + 1 + kMT - 1) / kMT;
@@ -183,22 +195,94 @@ __device__ void mw_segment_prefix(const int* seg, int n, int cmax, int* cpre) {
 // Stage n activation rows (row k of src = src + row_off[k] * ld, times mul[k])
 // into the B-operand layout: hi/lo[((ch*4 + q)*ldn + k)*NCALL + c] (half8),
 // with one power-of-two scale 2^kexp for all of them; groups past the row end
-// are zero.  Returns kexp.
+// are zero.  Returns kexp.  A thread takes whole 16-byte-code groups (the CW
+// activations one A-operand group multiplies): when every group fits in
+// registers (IPT per thread) all loads are issued at once and each value is
+// read once; otherwise a max pass and a convert pass read the rows twice.
 template <int BITS>
-__device__ int stage_b(const float* __restrict__ src, int ld, int ncols, const int* row_off, const float* mul,
-                       int n, int ldn, half8* hi, half8* lo, float* scratch) {
+__device__ __forceinline__ int stage_b(const float* __restrict__ src, int ld, int ncols, const int* row_off,
+                                       const float* mul, int n, int ldn, half8* hi, half8* lo, float* scratch) {
     using M = MfmaCodec<BITS>;
-    constexpr int CW = 16 * (8 / BITS);
+    constexpr int CW = 16 * (8 / BITS);          // activations per code group
+    constexpr int F4 = CW / 4;
+    constexpr int IPT = BITS == 2 ? 1 : 2;       // groups per thread held in registers
     const int P = ncols / CW;                    // 16-byte groups of a row
     const int NCH = (P + 3) / 4;
+    const int items = n * P;
+    int kexp;
+    if (items <= IPT * kMT) {
+        float v[IPT][CW];
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {      // every load first, at clamped (valid) items
+            const int idx = min((int)threadIdx.x + it * kMT, items - 1);
+            const int k = idx / P, g = idx - k * P;
+            const float4* p4 = reinterpret_cast<const float4*>(src + (size_t)row_off[k] * ld + g * CW);
+#pragma unroll
+            for (int q = 0; q < F4; ++q) {
+                const float4 t = p4[q];
+                v[it][4 * q] = t.x;
+                v[it][4 * q + 1] = t.y;
+                v[it][4 * q + 2] = t.z;
+                v[it][4 * q + 3] = t.w;
+            }
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int idx = threadIdx.x + it * kMT;
+            if (idx < items) {
+                const float sm = mul ? fabsf(mul[idx / P]) : 1.f;
+                float mm = 0.f;
+#pragma unroll
+                for (int i = 0; i < CW; ++i) mm = fmaxf(mm, fabsf(v[it][i]));
+                m = fmaxf(m, sm * mm);
+            }
+        }
+        kexp = f16_exponent(block_max(m, scratch));
+        const float sc = ldexpf(1.0f, kexp);
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int idx = threadIdx.x + it * kMT;
+            if (idx < items) {
+                const int k = idx / P, g = idx - k * P;
+                const float sk = (mul ? mul[k] : 1.f) * sc;
+#pragma unroll
+                for (int c = 0; c < M::NCALL; ++c) {
+                    half8 vh, vl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = v[it][M::col(c, e)] * sk;
+                        const _Float16 hx = (_Float16)x;
+                        vh[e] = hx;
+                        vl[e] = (_Float16)(x - (float)hx);
+                    }
+                    const int dst = (g * ldn + k) * M::NCALL + c;
+                    hi[dst] = vh;
+                    lo[dst] = vl;
+                }
+            }
+        }
+        const int pad = (NCH * 4 - P) * n * M::NCALL;   // zero groups past the row end
+        for (int u = threadIdx.x; u < pad; u += kMT) {
+            const int c = u % M::NCALL;
+            const int k = (u / M::NCALL) % n;
+            const int g = P + u / (M::NCALL * n);
+            half8 z;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
+            hi[(g * ldn + k) * M::NCALL + c] = z;
+            lo[(g * ldn + k) * M::NCALL + c] = z;
+        }
+        return kexp;
+    }
     float m = 0.f;
     for (int idx = threadIdx.x; idx < n * (ncols / 4); idx += kMT) {
         const int k = idx / (ncols / 4), c4 = idx - k * (ncols / 4);
-        const float4 v = reinterpret_cast<const float4*>(src + (size_t)row_off[k] * ld)[c4];
-        const float s = mul ? fabsf(mul[k]) : 1.f;
-        m = fmaxf(m, s * fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        const float4 t = reinterpret_cast<const float4*>(src + (size_t)row_off[k] * ld)[c4];
+        const float sm = mul ? fabsf(mul[k]) : 1.f;
+        m = fmaxf(m, sm * fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
     }
-    const int kexp = f16_exponent(block_max(m, scratch));
+    kexp = f16_exponent(block_max(m, scratch));
     const float sc = ldexpf(1.0f, kexp);
     const int units = NCH * 4 * n * M::NCALL;
     for (int u = threadIdx.x; u < units; u += kMT) {
@@ -208,13 +292,13 @@ __device__ int stage_b(const float* __restrict__ src, int ld, int ncols, const i
         half8 vh, vl;
         if (g < P) {
             const float* row = src + (size_t)row_off[k] * ld + g * CW;
-            const float s = (mul ? mul[k] : 1.f) * sc;
+            const float sk = (mul ? mul[k] : 1.f) * sc;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = row[M::col(c, e)] * s;
-                const _Float16 h = (_Float16)v;
-                vh[e] = h;
-                vl[e] = (_Float16)(v - (float)h);
+                const float x = row[M::col(c, e)] * sk;
+                const _Float16 hx = (_Float16)x;
+                vh[e] = hx;
+                vl[e] = (_Float16)(x - (float)hx);
             }
         } else {
 #pragma unroll
@@ -227,6 +311,13 @@ __device__ int stage_b(const float* __restrict__ src, int ld, int ncols, const i
     return kexp;
 }
 
+
+// A store that other workgroups of the same launch read after a grid barrier:
+// device scope, so it goes through to the device-coherent level at once and
+// the barrier needs no cache write-back.
+__device__ __forceinline__ void store_device(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ------------------------------------------------------------------ gate / up
 //
@@ -241,8 +332,9 @@ __device__ int stage_b(const float* __restrict__ src, int ld, int ncols, const i
 // the group re-read its last row (their outputs are never written) and groups
 // past the row end meet zero activations.  red: LDS [kMW][NB][2][16][ns];
 // sg_s / su_s: LDS [NB*16].  Returns with the workgroup synchronised.
-template <int BITS>
-__device__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, int rlo, int rhi, int nc,
+// kDeviceStore: h is read by other workgroups of the launch (store_device).
+template <int BITS, bool kDeviceStore = false>
+__device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, int rlo, int rhi, int nc,
                              const int* colslot, const int* asg, const half8* xhi, const half8* xlo, int ns,
                              float unscale, float* red, float* sg_s, float* su_s) {
     using M = MfmaCodec<BITS>;
@@ -263,10 +355,11 @@ __device__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, 
     for (int g0 = rlo; g0 < rhi; g0 += kNB * 16) {
         const int gn = min(rhi - g0, kNB * 16);          // rows in this group
         const int nb = (gn + 15) >> 4;
-        if ((int)threadIdx.x < gn) {                      // row scales, read at the end
-            sg_s[threadIdx.x] = a.s_gate[(size_t)e * I + g0 + threadIdx.x];
-            su_s[threadIdx.x] = a.s_up[(size_t)e * I + g0 + threadIdx.x];
-        }
+        // row scales: loaded now, used after the K loop (to LDS only then, so
+        // nothing waits for them before the code loads are issued)
+        const int sr = min((int)threadIdx.x, gn - 1);
+        const float sgv = a.s_gate[(size_t)e * I + g0 + sr];
+        const float suv = a.s_up[(size_t)e * I + g0 + sr];
         floatx4 accg[kNB], accu[kNB];
 #pragma unroll
         for (int b = 0; b < kNB; ++b) accg[b] = accu[b] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -318,6 +411,10 @@ __device__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, 
                 if (t + 1 < nk) compute(cw0 + t + 1, g1b, u1b);
             }
         }
+        if ((int)threadIdx.x < gn) {
+            sg_s[threadIdx.x] = sgv;
+            su_s[threadIdx.x] = suv;
+        }
         // partial sums of this wave's K-chunks -> LDS; lane holds rows 4*lq + i, column ln
         if (ln < nc) {
 #pragma unroll
@@ -344,7 +441,9 @@ __device__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, int e, 
             const int row = g0 + r;
             const float gv = gs * unscale * sg_s[r];
             const float uv = vs * unscale * su_s[r];
-            h[(size_t)asg[n] * I + row] = gv / (1.0f + __expf(-gv)) * uv;
+            const float hv = gv / (1.0f + __expf(-gv)) * uv;
+            if constexpr (kDeviceStore) store_device(h + (size_t)asg[n] * I + row, hv);
+            else h[(size_t)asg[n] * I + row] = hv;
         }
         __syncthreads();
     }
@@ -362,7 +461,7 @@ struct GateUpLds {
 // Stage all T tokens of x once (B slot = token index); sets s.kexp and
 // s.staged.  Used when T <= ns.
 template <int BITS>
-__device__ void stage_tokens(const float* __restrict__ x, int T, int H, int ns, half8* xhi, half8* xlo,
+__device__ __forceinline__ void stage_tokens(const float* __restrict__ x, int T, int H, int ns, half8* xhi, half8* xlo,
                              GateUpLds& s) {
     if (threadIdx.x < kCols) s.tok[threadIdx.x] = threadIdx.x;
     __syncthreads();
@@ -378,8 +477,8 @@ __device__ void stage_tokens(const float* __restrict__ x, int T, int H, int ns, 
 // contiguous shares.  With stage_all the tokens were staged by stage_tokens
 // and a segment's columns point at their tokens' slots; otherwise each
 // segment stages its own tokens (skipped when they are already staged).
-template <int BITS>
-__device__ void gate_up_units(const ExpertArgs& a, const float* __restrict__ x, float* __restrict__ h,
+template <int BITS, bool kDeviceStore = false>
+__device__ __forceinline__ void gate_up_units(const ExpertArgs& a, const float* __restrict__ x, float* __restrict__ h,
                               const int* eid, const int* seg, const int* assign, int n_exp, int ns, bool stage_all,
                               int part, int nparts, half8* xhi, half8* xlo, float* red, GateUpLds& s) {
     const int H = a.H, I = a.I;
@@ -415,7 +514,7 @@ __device__ void gate_up_units(const ExpertArgs& a, const float* __restrict__ x, 
                 __syncthreads();
             }
         }
-        gate_up_rows<BITS>(a, h, e, rlo, rhi, nc, s.col, s.asg, xhi, xlo, ns, ldexpf(1.0f, -s.kexp), red, s.sg,
+        gate_up_rows<BITS, kDeviceStore>(a, h, e, rlo, rhi, nc, s.col, s.asg, xhi, xlo, ns, ldexpf(1.0f, -s.kexp), red, s.sg,
                            s.su);
     }
 }
@@ -467,7 +566,7 @@ __host__ __device__ constexpr size_t down_lds_bytes_per_assignment(int I) {
 __host__ __device__ constexpr size_t down_lds_fixed_bytes() { return (size_t)kMW * kNBD * 256 * sizeof(float); }
 
 template <int BITS, typename Gate>
-__device__ void down_rows(const float* h, const float* topk_w, const ExpertArgs& a, float* __restrict__ y, int r0,
+__device__ __forceinline__ void down_rows(const float* h, const float* topk_w, const ExpertArgs& a, float* __restrict__ y, int r0,
                           int r1, int qc, unsigned char* dyn, const int* eid, const int* seg, const int* assign,
                           int n_act, float* scratch, Gate& gate) {
     using M = MfmaCodec<BITS>;

@@ -9,24 +9,20 @@
 // (s_k / sum over the chosen s in slot order) * routed_scaling_factor.
 #pragma once
 
+#include <climits>
+
 #include "common.h"
 
 namespace moedec {
 
-// LDS of route_select_block for batches of up to TM tokens and EM routed
-// experts (top_k <= 32, n_group <= 64, n_shared <= 8).
-template <int TM, int EM>
+// LDS of route_select_block for batches of up to TM tokens, EM routed experts
+// and NW waves (top_k <= 32, n_group <= 64, n_shared <= 8).
+template <int TM, int EM, int NW>
 struct RouteLdsT {
     int sel[TM * 32];                      // chosen experts [T][K], slot order
     float selw[TM * 32];                   // their weights
-    float c[EM];                           // one token's corrected scores
-    float s[EM];                           //   and sigmoid scores
-    int cand[EM];                          //   candidates: at kept group rank * min(per, K) + rank in group,
-    float cand_c[EM];                      //   with their corrected and sigmoid scores
-    float cand_s[EM];
-    float gs[64];                          //   group scores
-    int gslot[64];                         //   rank of a kept group among the groups, else -1
-    float ws[32];                          //   chosen experts' sigmoid scores, slot order
+    float c[NW][EM];                       // each wave's token: corrected scores
+    float gs[NW][64];                      //   and group scores
     int key[TM * 40];                      // assignment sort keys, then "new expert starts here"
     int sexp[TM * 40];                     // expert of each sorted position
     int eid[EM + 8];                       // worklist: unique experts ascending
@@ -34,100 +30,118 @@ struct RouteLdsT {
     int assign[TM * 40];                   //           assignments by expert
     int n_active;
 };
-using RouteLds = RouteLdsT<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS>;
 
 // (v, i) beats (u, j) if v > u, or v == u and i < j: a strict total order.
 __device__ __forceinline__ bool beats(float v, int i, float u, int j) { return v > u || (v == u && i < j); }
 
+// Orders one wave's LDS writes before its later LDS reads (LDS serves a wave
+// in issue order; this keeps the compiler from reordering across it).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Route T tokens whose sigmoid scores are in global memory (s[t][e]) and build
-// the batch union, all in LDS `r`; the whole workgroup calls this (any
-// multiple of 64 threads) and every
-// selection is a rank count, so no step waits on a serial chain of rounds:
-//   1. thread per expert: c = s + bias into LDS;
-//   2. thread per group: score = largest + second largest c of the group;
-//   3. thread per group: rank among the group scores; kept if rank < topk_group;
-//   4. thread per expert of a kept group: rank within its group; only the
-//      group's top min(per, top_k) can be among the token's top_k, so they are
-//      the candidates, placed without atomics at (group rank, rank in group);
-//   5. thread per candidate: rank among all candidates = its slot if < top_k;
-//   6. thread per slot: weight = s / (sum of the chosen s in slot order) * rsf.
+// the batch union, all in LDS `r`; the whole workgroup (NW waves) calls this.
+// Each wave routes its own tokens with wave-wide operations only (no
+// workgroup barrier per token):
+//   1. lane l holds experts l, l+64, ...: s, and c = s + bias (also to LDS);
+//   2. lane g < n_group: group score = largest + second largest c of group g;
+//   3. lane g: rank among the group scores; kept if rank < topk_group;
+//   4. top_k rounds of a wave arg-max over the kept groups' experts, by
+//      (c descending, index ascending) -- DPP and lane reads, no LDS round
+//      trips; round k's winner is slot k, and the total of the chosen s is
+//      summed in slot order as the rounds go;
+//   5. lane k < top_k: weight k = s_k / total * rsf.
 // The worklist is then a rank sort of the assignments by (expert, assignment).
 // A NaN corrected score or group score ranks below every number (as -inf,
-// ties by index), so the ranks are always permutations and every slot gets a
-// valid expert whatever the inputs hold.
-template <int TM, int EM>
-__device__ void route_select_block(const float* scores, const float* __restrict__ bias, int T, int E,
-                                   int n_group, int topk_group, int top_k, int n_shared, float rsf,
-                                   RouteLdsT<TM, EM>& r) {
-    const int nthr = blockDim.x;
+// ties by index), so every slot gets a distinct valid expert whatever the
+// inputs hold.
+template <int TM, int EM, int NW>
+__device__ __forceinline__ void route_select_block(const float* scores, const float* __restrict__ bias, int T,
+                                                   int E, int n_group, int topk_group, int top_k, int n_shared,
+                                                   float rsf, RouteLdsT<TM, EM, NW>& r) {
+    constexpr int NV = EM / kWave;                    // experts per lane
+    static_assert(NV <= 32, "the candidate mask is 32 bits");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
     const int per = E / n_group;
-    const int kg = per < top_k ? per : top_k;        // candidates per kept group
-    const int n_cand = topk_group * kg;
-    for (int t = 0; t < T; ++t) {
-        const float* st = scores + (size_t)t * E;
-        for (int e = threadIdx.x; e < E; e += nthr) {
-            const float sv = st[e];
-            const float cv = sv + bias[e];
-            r.s[e] = sv;
-            r.c[e] = cv == cv ? cv : -INFINITY;
+    for (int t = wave; t < T; t += nwaves) {
+        float* cw = r.c[wave];
+        float cl[NV], sl[NV], bl[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {                 // every load first (clamped index), then use
+            const int e = min(lane + kWave * j, E - 1);
+            sl[j] = scores[(size_t)t * E + e];
+            bl[j] = bias[e];
         }
-        __syncthreads();
-        for (int g = threadIdx.x; g < n_group; g += nthr) {
+        unsigned live = 0;                             // bit j: expert lane + 64 j exists
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = lane + kWave * j;
+            const float v = sl[j] + bl[j];
+            cl[j] = v == v ? v : -INFINITY;
+            if (e < E) {
+                cw[e] = cl[j];
+                live |= 1u << j;
+            }
+        }
+        wave_lds_sync();
+        float gsv = -INFINITY;
+        if (lane < n_group) {
             float m1 = -INFINITY, m2 = -INFINITY;
-            const float* cg = r.c + g * per;
+            const float* cg = cw + lane * per;
 #pragma unroll 8
-            for (int k = 0; k < per; ++k) {          // branch-free, so the reads issue back to back
+            for (int k = 0; k < per; ++k) {            // branch-free, so the reads issue back to back
                 const float v = cg[k];
                 m2 = fmaxf(m2, fminf(m1, v));
                 m1 = fmaxf(m1, v);
             }
             const float gsum = m1 + m2;                 // NaN only from +inf + -inf
-            r.gs[g] = gsum == gsum ? gsum : -INFINITY;
+            gsv = gsum == gsum ? gsum : -INFINITY;
+            r.gs[wave][lane] = gsv;
         }
-        __syncthreads();
-        for (int g = threadIdx.x; g < n_group; g += nthr) {
-            const float v = r.gs[g];
-            int rank = 0;
+        wave_lds_sync();
+        int grank = 0;
+        if (lane < n_group) {
 #pragma unroll 8
-            for (int h = 0; h < n_group; ++h) rank += beats(r.gs[h], h, v, g);
-            r.gslot[g] = rank < topk_group ? rank : -1;   // kept groups get distinct slots
+            for (int h = 0; h < n_group; ++h) grank += beats(r.gs[wave][h], h, gsv, lane);
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += nthr) {
-            const int g = e / per;
-            const int gsl = r.gslot[g];
-            if (gsl >= 0) {
-                const float v = r.c[e];
-                const float* cg = r.c + g * per;
-                int rank = 0;
-#pragma unroll 8
-                for (int k = 0; k < per; ++k) rank += beats(cg[k], g * per + k, v, e);
-                if (rank < kg) {
-                    r.cand[gsl * kg + rank] = e;
-                    r.cand_c[gsl * kg + rank] = v;
-                    r.cand_s[gsl * kg + rank] = r.s[e];
+        const unsigned long long kept = __ballot(lane < n_group && grank < topk_group);
+        unsigned cand = 0;                             // bit j: expert lane + 64 j is a candidate
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int g = min((lane + kWave * j) / per, 63);
+            if (((live >> j) & 1u) && ((kept >> g) & 1ull)) cand |= 1u << j;
+        }
+        // round k: each lane's best candidate (ascending j keeps the lower index
+        // on ties), the wave's largest c, then the lowest index holding it
+        float total = 0.f, my_s = 0.f;
+        for (int k = 0; k < top_k; ++k) {
+            bool bvalid = false;
+            float bv = -INFINITY, bs = 0.f;
+            int bj = 0;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (((cand >> j) & 1u) && (!bvalid || cl[j] > bv)) {
+                    bv = cl[j];
+                    bs = sl[j];
+                    bj = j;
+                    bvalid = true;
                 }
             }
+            const float m = wave_max(bvalid ? bv : -INFINITY);
+            const int bi = wave_min(bvalid && bv == m ? lane + kWave * bj : INT_MAX);
+            const int win = bi == INT_MAX ? 0 : bi;   // INT_MAX cannot happen: top_k <= kept experts
+            const int owner = win & (kWave - 1), jw = win / kWave;
+            const float sw = bits_f(__builtin_amdgcn_readlane(f_bits(bs), owner));
+            if (lane == owner) cand &= ~(1u << jw);
+            if (lane == 0) r.sel[t * top_k + k] = win;
+            if (lane == k) my_s = sw;
+            total += sw;                               // slot order
         }
-        __syncthreads();
-        for (int q = threadIdx.x; q < n_cand; q += nthr) {
-            const int e = r.cand[q];
-            const float v = r.cand_c[q];
-            int rank = 0;
-#pragma unroll 8
-            for (int p = 0; p < n_cand; ++p) rank += beats(r.cand_c[p], r.cand[p], v, e);
-            if (rank < top_k) {
-                r.sel[t * top_k + rank] = e;
-                r.ws[rank] = r.cand_s[q];
-            }
-        }
-        __syncthreads();
-        if ((int)threadIdx.x < top_k) {
-            float total = 0.f;
-            for (int k = 0; k < top_k; ++k) total += r.ws[k];   // slot order
-            r.selw[t * top_k + threadIdx.x] = (r.ws[threadIdx.x] / total) * rsf;
-        }
-        __syncthreads();
+        if (lane < top_k) r.selw[t * top_k + lane] = (my_s / total) * rsf;
     }
     __syncthreads();
 

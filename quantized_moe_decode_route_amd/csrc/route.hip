@@ -11,8 +11,8 @@
 // of its 16-byte loads of the row before using them, then the row is dotted
 // with each token and s = sigmoid(W_r[e] . x_t) is written.
 // Kernel 2 (route_select): one workgroup running route_select_block (see
-// route.h): per token one wave with the scores in registers, then the
-// expert-ascending worklist by a rank sort in LDS.
+// route.h): each wave routes its tokens with wave-wide arg-max rounds, then
+// the expert-ascending worklist comes from a rank sort in LDS.
 #include "route.h"
 
 namespace moedec {
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     int top_k, int n_shared, float rsf, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ wl_n_active, int32_t* __restrict__ wl_expert_id, int32_t* __restrict__ wl_seg,
     int32_t* __restrict__ wl_assign) {
-    __shared__ RouteLds r;
+    __shared__ RouteLdsT<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS, kSelThreads / kWave> r;
     route_select_block(scores, bias, T, E, n_group, topk_group, top_k, n_shared, rsf, r);
     // outputs
     for (int i = threadIdx.x; i < T * top_k; i += blockDim.x) {

@@ -60,6 +60,8 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_unpack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
 
+MOEDEC_ERR_UNSUPPORTED = 2
+
 # limits of the fused layer call (include/moedec.h)
 FUSED_MAX_TOKENS = 16
 FUSED_MAX_EXPERTS = 512
@@ -336,8 +338,14 @@ def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: E
     if buf is None:
         buf = LayerBuffers.allocate(T, ex.hidden, ex.inter, ex.n_experts, top_k, ex.n_shared, x.device)
     if fused is None:
-        fused = fused_supported(T, ex)
-    if fused:
+        if fused_supported(T, ex):
+            try:
+                return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k,
+                                   rsf=rsf, buf=buf)
+            except MoedecError as err:
+                if err.status != MOEDEC_ERR_UNSUPPORTED:   # the shape does not fit the fused plan
+                    raise
+    elif fused:
         return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
                            buf=buf)
     route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
