@@ -295,11 +295,15 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int* eid = r.eid;
     const int* seg = r.seg;
     const int* asn = r.assign;
-    // gate/up geometry: this workgroup's rows [gr0, gr0 + rg) of every expert
+    // gate/up geometry: this workgroup's rows [gr0, gr0 + rg) of every expert,
+    // taken as one list rho = j*rg + r (expert j, row gr0 + r) cut into 16-row
+    // blocks, so a block may hold rows of two experts: B carries every token,
+    // and each row keeps only the columns of tokens routed to its expert
     const int rbg = H * BITS / 8, Pg = rbg >> 4, NCHg = (Pg + 3) >> 2, nkg = (NCHg + kMW - 1) / kMW;
     const int gr0 = (int)((long long)b * I / nwg);
     const int rg = (int)((long long)(b + 1) * I / nwg) - gr0;
-    const int nbg = (rg + 15) >> 4;
+    const int NR = n_act * rg;
+    const int nbg = (NR + 15) >> 4;
     // down geometry: output rows [dr0, dr0 + rd), rd <= 32
     const int rbd = I * BITS / 8, Pd = rbd >> 4, NCHd = (Pd + 3) >> 2, nkd = (NCHd + kMW - 1) / kMW;
     const int dr0 = (int)((long long)b * H / nwg);
@@ -343,7 +347,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     // start (h out, chunk staging) runs between rounds, outside the unrolled
     // ring body.  Padding positions issue loads of a real item and compute
     // nothing.
-    const int Ngu = n_act * nbg * nkg;
+    const int Ngu = nbg * nkg;
     const int Gpad = (Ngu + W - 1) / W * W;
     const int nchunk = rd > 0 ? (A + qc - 1) / qc : 0;
     if (threadIdx.x == 0) {
@@ -403,10 +407,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             c.valid = c.pos < Ngu;
             if (c.valid && ++c.k == nkg) {
                 c.k = 0;
-                if (++c.blk == nbg) {
-                    c.blk = 0;
-                    ++c.j;
-                }
+                ++c.blk;
             }
             if (c.pos == Gpad && nchunk > 0) enter_chunk(c, 0);
         } else {
@@ -424,13 +425,20 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     };
     // (past the last position a cursor stays on the last real item: loads stay valid)
 
+    // this lane's row of the issuing cursor's gate/up block (recomputed when the block changes)
+    int iblk = -1;
+    size_t irow_off = 0;
     auto issue = [&](const Cursor& c, uint4* dst) {
         if (c.kind == 0) {
+            if (c.blk != iblk) {
+                iblk = c.blk;
+                const int rho = min(iblk * 16 + ln, NR - 1);
+                const int j = rho / rg;
+                irow_off = ((size_t)eid[j] * I + gr0 + (rho - j * rg)) * rbg;
+            }
             const int cc = min(wave * nkg + c.k, NCHg - 1);
             const int grp = min(cc * 4 + lq, Pg - 1);
-            const int rows_blk = min(16, rg - c.blk * 16);
-            const size_t row = (size_t)eid[c.j] * I + gr0 + c.blk * 16 + min(ln, rows_blk - 1);
-            const size_t off = row * rbg + grp * 16;
+            const size_t off = irow_off + grp * 16;
             dst[0] = ld16(a.w_gate + off);
             dst[1] = ld16(a.w_up + off);
         } else {
@@ -449,23 +457,18 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     float d_unscale = 1.f;
     int chunk_first = 0;            // first expert of the staged chunk
     // per-expert state of the computing cursor
-    int cj = -1, cs0 = 0, cnc = 0, ctok = 0, cbq = -1;
+    int cj = -1, cbq = -1;
 
     // Columns of the MFMA output that no token uses hold garbage and are never
     // read, so B operands need no zeroing; chunks past the row end are skipped.
+    const int tcol = min(ln, T - 1);              // this lane's token column in B
     auto gu_item = [&](const Cursor& c, const uint4* cur) {
-        if (c.j != cj) {
-            cj = c.j;
-            cs0 = seg[cj];
-            cnc = seg[cj + 1] - cs0;
-            ctok = asn[cs0 + min(ln, cnc - 1)] / slots;          // B slot of this lane's column
-        }
         const int ch = wave * nkg + c.k;
         if (ch < NCHg) {
             half8 bh[NCALL], bl[NCALL];
 #pragma unroll
             for (int cc = 0; cc < NCALL; ++cc) {
-                const int src = ((ch * 4 + lq) * T + ctok) * NCALL + cc;
+                const int src = ((ch * 4 + lq) * T + tcol) * NCALL + cc;
                 bh[cc] = xhi[src];
                 bl[cc] = xlo[src];
             }
@@ -486,7 +489,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             // last of the 8 waves to arrive adds them up, in wave order, and
             // writes h = silu(g) * v for the block.  A slot is reused rb blocks
             // later, once its block is finalised.
-            const int bidx = c.j * nbg + c.blk;
+            const int bidx = c.blk;
             const int slot = bidx % rb;
             float* part = gred + (size_t)slot * kMW * 2 * 16 * T;
             if (bidx >= rb) {
@@ -500,7 +503,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
-            if (ln < cnc) {
+            if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = accg[ii];
@@ -515,18 +518,24 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             arrived = __shfl(arrived, 0, kWave);
             if (arrived == kMW - 1) {   // the last wave: finalise the block
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                const int rows_blk = min(16, rg - c.blk * 16);
-                for (int idx = lane; idx < rows_blk * cnc; idx += kWave) {
-                    const int rr = idx / cnc, n = idx - rr * cnc;
-                    float gs = 0.f, vs = 0.f;
-                    for (int w = 0; w < kMW; ++w) {
-                        gs += part[((w * 2 + 0) * 16 + rr) * T + n];
-                        vs += part[((w * 2 + 1) * 16 + rr) * T + n];
+                const int rows_blk = min(16, NR - bidx * 16);
+                for (int idx = lane; idx < rows_blk * T; idx += kWave) {
+                    const int rr = idx / T, t = idx - rr * T;
+                    const int rho = bidx * 16 + rr;
+                    const int j = rho / rg, r = rho - j * rg;
+                    const int s0 = seg[j], nc = seg[j + 1] - s0;
+                    int n = 0;
+                    while (n < nc && asn[s0 + n] / slots != t) ++n;     // token t's column of expert j
+                    if (n < nc) {
+                        float gs = 0.f, vs = 0.f;
+                        for (int w = 0; w < kMW; ++w) {
+                            gs += part[((w * 2 + 0) * 16 + rr) * T + t];
+                            vs += part[((w * 2 + 1) * 16 + rr) * T + t];
+                        }
+                        const float gv = gs * x_unscale * gsc[(j * 2 + 0) * rg + r];
+                        const float uv = vs * x_unscale * gsc[(j * 2 + 1) * rg + r];
+                        hprod[(j * rg + r) * T + n] = gv / (1.0f + __expf(-gv)) * uv;
                     }
-                    const int row = c.blk * 16 + rr;
-                    const float gv = gs * x_unscale * gsc[(cj * 2 + 0) * rg + row];
-                    const float uv = vs * x_unscale * gsc[(cj * 2 + 1) * rg + row];
-                    hprod[(cj * rg + row) * T + n] = gv / (1.0f + __expf(-gv)) * uv;
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                 if (lane == 0) {
@@ -745,7 +754,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t avail = kLdsMax - static_lds;
     const size_t x_bytes = align16(staged_row_bytes<BITS>(H) * T);
     const size_t dred_bytes = (size_t)kMW * kNBD * 256 * sizeof(float);
-    const int n_blocks = max_active * ((rg + 15) / 16);
+    const int n_blocks = (max_active * rg + 15) / 16;
     const int rb = n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8;   // partial-sum slots
     const size_t gured = align16((size_t)rb * kMW * 2 * 16 * T * sizeof(float) + 2 * rb * sizeof(int));
     const size_t gsc = align16((size_t)max_active * rg * 2 * sizeof(float));
