@@ -133,9 +133,12 @@ def main() -> None:
     ap.add_argument("--workload", default="glm_t1")
     ap.add_argument("--layers", type=int, default=4, help="resident layers the steps rotate over")
     ap.add_argument("--graph-steps", type=int, default=8)
-    ap.add_argument("--kernel-steps", type=int, default=100, help="eager steps timing the dominant kernel")
+    ap.add_argument("--kernel-steps", type=int, default=100, help="eager gate/up launches timed (split path)")
     ap.add_argument("--split", action="store_true", help="time the three separate calls instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB 20 times (a known-size "
+                         "reference for the HBM traffic counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,6 +149,16 @@ def main() -> None:
     import torch
 
     from quantized_moe_decode_route_amd import ops, synth
+
+    if args.copy_mib > 0:
+        n = args.copy_mib << 18                      # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 20}), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.workload]
     if cfg.layers != 1:
@@ -222,10 +235,14 @@ def main() -> None:
     run(0, args.warmup)
     torch.cuda.synchronize()
     first = args.warmup
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev_a.record()
     run(first, args.steps)
+    ev_b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    region_s = ev_a.elapsed_time(ev_b) * 1e-3
     idx = (np.arange(first, first + args.steps) % period)
     total_bytes = int(sbytes[idx].sum())
     gbs = total_bytes / wall / 1e9
@@ -234,26 +251,29 @@ def main() -> None:
     print(f"[bench] {args.steps} steps in {wall * 1e3:.1f} ms: {ms_per_step * 1e3:.2f} us/step, "
           f"{gbs:.0f} GB/s, {tok_s:.0f} tok/s", file=sys.stderr, flush=True)
 
-    # the dominant kernel timed live with HIP events on the stream it is launched
-    # on (torch's current stream), the caches emptied of its data before every
-    # launch by reading (not writing) a 1 GiB buffer
+    # The dominant kernel, timed live with HIP events on the stream it runs on.
+    # Fused: it is the whole step, so its average launch is the event-timed
+    # region of graph replays above divided by the steps (the launches run
+    # back to back, each on a layer the previous steps did not touch).
+    # Split: gate/up launched eagerly, each after a read (not a write) of a
+    # 1 GiB buffer that empties the caches of its data.
     kind = "fused" if fused else "gate_up"
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
-    kb = []
-    sink = torch.zeros((), dtype=torch.float32, device=dev)
-    for k in range(args.kernel_steps):
-        i = first + args.steps + k
-        l = i % L
-        sink += flush.sum()
-        x = tokens(i)
-        if fused:
-            ev0[k].record()
-            ops.layer_fused(x, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], **kw)
-            ev1[k].record()
-            kb.append(fused_bytes(cfg, int(n_active[i % period])))
-        else:
+    if fused:
+        if any(b.fused_error() for b in bufs):
+            raise SystemExit("a wait of the fused launch timed out: results invalid")
+        kb = [fused_bytes(cfg, int(n)) for n in n_active[idx]]
+        dur = np.array([region_s / args.steps])
+    else:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_steps)]
+        kb = []
+        sink = torch.zeros((), dtype=torch.float32, device=dev)
+        for k in range(args.kernel_steps):
+            i = first + args.steps + k
+            l = i % L
+            sink += flush.sum()
+            x = tokens(i)
             ops.route_topk(x, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route,
                            **kw)
             ev0[k].record()
@@ -262,10 +282,8 @@ def main() -> None:
             ops.down_combine(bufs[l].h, experts[l], bufs[l].route.worklist, bufs[l].route.topk_w, cfg.top_k,
                              out=bufs[l].y)
             kb.append(gate_up_bytes(cfg, int(n_active[i % period])))
-    torch.cuda.synchronize()
-    if fused and any(b.fused_error() for b in bufs):
-        raise SystemExit("a grid barrier of the fused launch timed out: results invalid")
-    dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
+        torch.cuda.synchronize()
+        dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
     traffic = traffic_from_profile(kind, cfg.name)
     kname = f"layer_fused_kernel<{cfg.bits}>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
