@@ -45,6 +45,7 @@
 // word and goes on, so a launch that cannot be co-resident (the GPU shared
 // with other work) ends with garbage outputs and a raised flag instead of
 // hanging.
+#include "imma.h"
 #include "mfma.h"
 #include "route.h"
 
@@ -53,6 +54,7 @@ namespace moedec {
 namespace {
 
 using namespace mfma;
+using namespace imma;
 
 constexpr int kFusedExperts = 512;                      // routed experts at most
 using FusedRoute = RouteLdsT<kCols, kFusedExperts, kMW>;
@@ -60,6 +62,7 @@ constexpr int kRowF4 = MOEDEC_MAX_DIM / 4 / kMT;        // float4 of a router ro
 constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a couple of seconds
 constexpr int kStreamW = 4;                             // stream items in flight per wave
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
+constexpr int kStageX4 = 12;                            // float4 of x a thread holds at once
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
 
@@ -170,21 +173,120 @@ __device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int np
     }
 }
 
-// Stage the down B operands of one chunk: n rows of h (row k = h[qrow[k]],
-// times qmul[k]) into hi/lo[((ch*4 + q)*ldn + k)*NCALL + c] (half8), with one
-// power-of-two scale 2^kexp; groups past the row end are zero.  h is read once,
-// with device-coherent 16-byte loads, consecutive lanes reading consecutive
-// 16 bytes (all kStageV4 loads of a thread issued before any is used); each
-// value then goes to its place in the B layout (column p of a code group is
-// element e of call c with col(c, e) = p).  n * I <= kStageV4 * 4 * kMT.
-// Returns kexp.
+// Running maximum of non-negative floats in LDS (their bits order as unsigned).
+__device__ __forceinline__ void lds_max(unsigned* slot, float v) {
+    __hip_atomic_fetch_max(slot, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Maximum of |v| over the values of column t (wave-wide when the whole wave
+// holds one column, else per lane) into cmax[t]; invalid lanes pass t < 0.
+__device__ __forceinline__ void column_max(unsigned* cmax, int t, float m) {
+    const int t0 = __builtin_amdgcn_readfirstlane(t);
+    if (t0 < 0) return;                                    // lane 0 holds the smallest index
+    if (__ballot(t != t0) == 0) {
+        m = wave_max(m);
+        if ((threadIdx.x & (kWave - 1)) == 0) lds_max(cmax + t0, m);
+    } else if (t >= 0) {
+        lds_max(cmax + t, m);
+    }
+}
+
+// Scatter 4 consecutive columns col0.. of row k (already scaled by 2^e) into
+// the int8 B layout: unit ((g*ldn + k)*NM + m) of hi / lo, slot s, for column
+// g*CW + col(m, s).
 template <int BITS>
-__device__ __forceinline__ int stage_h(const float* h, int h_bytes, int I, const int* qrow, const float* qmul,
-                                       int n, int ldn, half8* hi, half8* lo, float* scratch) {
-    using M = MfmaCodec<BITS>;
-    constexpr int CW = 16 * (8 / BITS);
-    const int P = I / CW;
-    const int NCH = (P + 3) / 4;
+__device__ __forceinline__ void scatter4(float4 v, float sc, int col0, int k, int ldn, uint8_t* hi, uint8_t* lo) {
+    using C = I8Codec<BITS>;
+    const float xs[4] = {v.x * sc, v.y * sc, v.z * sc, v.w * sc};
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        const int col = col0 + e4;
+        const int g = col / C::CW, p = col - g * C::CW;
+        int m = 0, sl = 0;
+        C::place(p, m, sl);
+        int h8 = 0, l8 = 0;
+        split16(xs[e4], h8, l8);
+        const int dst = ((g * ldn + k) * C::NM + m) * 16 + sl;
+        hi[dst] = (uint8_t)h8;
+        lo[dst] = (uint8_t)l8;
+    }
+}
+
+// Zero the B units of groups [P, 4*NCH) of n rows (the columns past the row
+// end of the last K-chunk).
+template <int BITS>
+__device__ __forceinline__ void zero_pad(int P, int NCH, int n, int ldn, i32x4* hi, i32x4* lo) {
+    constexpr int NM = I8Codec<BITS>::NM;
+    const int pad = (NCH * 4 - P) * n * NM;
+    for (int uu = threadIdx.x; uu < pad; uu += kMT) {
+        const int m = uu % NM;
+        const int k = (uu / NM) % n;
+        const int g = P + uu / (NM * n);
+        hi[(g * ldn + k) * NM + m] = i32x4{0, 0, 0, 0};
+        lo[(g * ldn + k) * NM + m] = i32x4{0, 0, 0, 0};
+    }
+}
+
+// Stage the T token rows of x (row-major [T][H]) as int8 hi/lo B operands,
+// unit ((g*T + t)*NM + m); column t = token t has its own exponent, and
+// xu[t] = 2^-(e_t + kShift) undoes it and the code factor.  cmax[0..T) must
+// be zero on entry.  When all of x fits the registers (kStageX4 float4 per
+// thread) it is read once, else twice (a max pass and a convert pass).
+template <int BITS>
+__device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int T, i32x4* hi, i32x4* lo,
+                                        unsigned* cmax, float* xu) {
+    using C = I8Codec<BITS>;
+    const int H4 = H >> 2, total4 = T * H4;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const bool single = total4 <= kStageX4 * kMT;
+    float4 v[kStageX4];
+    for (int b0 = 0; b0 < total4; b0 += kStageX4 * kMT) {
+#pragma unroll
+        for (int u = 0; u < kStageX4; ++u) {           // every load first, then use
+            const int i4 = b0 + (int)threadIdx.x + u * kMT;
+            v[u] = x4[min(i4, total4 - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kStageX4; ++u) {
+            const int i4 = b0 + (int)threadIdx.x + u * kMT;
+            const bool ok = i4 < total4;
+            const float m = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+            column_max(cmax, ok ? i4 / H4 : -1, ok ? m : 0.f);
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < T) xu[threadIdx.x] = ldexpf(1.0f, -q16_exponent(__uint_as_float(cmax[threadIdx.x])) - C::kShift);
+    uint8_t* h8 = reinterpret_cast<uint8_t*>(hi);
+    uint8_t* l8 = reinterpret_cast<uint8_t*>(lo);
+    for (int b0 = 0; b0 < total4; b0 += kStageX4 * kMT) {
+        if (!single) {
+#pragma unroll
+            for (int u = 0; u < kStageX4; ++u) v[u] = x4[min(b0 + (int)threadIdx.x + u * kMT, total4 - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kStageX4; ++u) {
+            const int i4 = b0 + (int)threadIdx.x + u * kMT;
+            if (i4 < total4) {
+                const int t = i4 / H4;
+                const float sc = ldexpf(1.0f, q16_exponent(__uint_as_float(cmax[t])));
+                scatter4<BITS>(v[u], sc, (i4 - t * H4) * 4, t, T, h8, l8);
+            }
+        }
+    }
+    const int P = H / C::CW;
+    zero_pad<BITS>(P, (P + 3) / 4, T, T, hi, lo);
+}
+
+// Stage the down B operands of one chunk: n rows of h (row k = h[qrow[k]],
+// times qmul[k]) into hi/lo unit ((g*ldn + k)*NM + m), every row with its own
+// exponent; dsl[k] = 2^-(e_k + kShift) undoes it.  h is read once, with
+// device-coherent 16-byte loads, consecutive lanes reading consecutive 16
+// bytes (all kStageV4 loads of a thread issued before any is used).
+// n * I <= kStageV4 * 4 * kMT; cmax[0..n) must be zero on entry.
+template <int BITS>
+__device__ __forceinline__ void stage_h(const float* h, int h_bytes, int I, const int* qrow, const float* qmul,
+                                        int n, int ldn, i32x4* hi, i32x4* lo, unsigned* cmax, float* dsl) {
+    using C = I8Codec<BITS>;
     const int I4 = I >> 2, total4 = n * I4;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(h), (short)0, h_bytes, kBufWord3);
@@ -196,52 +298,32 @@ __device__ __forceinline__ int stage_h(const float* h, int h_bytes, int I, const
         const int off = i4 < total4 ? (qrow[k] * I4 + c4) * 16 : 0;
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent);
     }
-    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < kStageV4; ++u) {
+        const int i4 = threadIdx.x + u * kMT;
+        const bool ok = i4 < total4;
+        const int k = ok ? i4 / I4 : 0;
+        const float mm = fmaxf(fmaxf(fabsf(__uint_as_float(v[u].x)), fabsf(__uint_as_float(v[u].y))),
+                               fmaxf(fabsf(__uint_as_float(v[u].z)), fabsf(__uint_as_float(v[u].w))));
+        column_max(cmax, ok ? k : -1, ok ? fabsf(qmul[k]) * mm : 0.f);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < n) dsl[threadIdx.x] = ldexpf(1.0f, -q16_exponent(__uint_as_float(cmax[threadIdx.x])) - C::kShift);
+    uint8_t* h8 = reinterpret_cast<uint8_t*>(hi);
+    uint8_t* l8 = reinterpret_cast<uint8_t*>(lo);
 #pragma unroll
     for (int u = 0; u < kStageV4; ++u) {
         const int i4 = threadIdx.x + u * kMT;
         if (i4 < total4) {
-            const float mm = fmaxf(fmaxf(fabsf(__uint_as_float(v[u].x)), fabsf(__uint_as_float(v[u].y))),
-                                   fmaxf(fabsf(__uint_as_float(v[u].z)), fabsf(__uint_as_float(v[u].w))));
-            m = fmaxf(m, fabsf(qmul[i4 / I4]) * mm);
+            const int k = i4 / I4;
+            const float sk = qmul[k] * ldexpf(1.0f, q16_exponent(__uint_as_float(cmax[k])));
+            const float4 f4 = make_float4(__uint_as_float(v[u].x), __uint_as_float(v[u].y), __uint_as_float(v[u].z),
+                                          __uint_as_float(v[u].w));
+            scatter4<BITS>(f4, sk, (i4 - k * I4) * 4, k, ldn, h8, l8);
         }
     }
-    const int kexp = f16_exponent(block_max(m, scratch));
-    const float sc = ldexpf(1.0f, kexp);
-    _Float16* hh = reinterpret_cast<_Float16*>(hi);
-    _Float16* hl = reinterpret_cast<_Float16*>(lo);
-#pragma unroll
-    for (int u = 0; u < kStageV4; ++u) {
-        const int i4 = threadIdx.x + u * kMT;
-        if (i4 < total4) {
-            const int k = i4 / I4, col0 = (i4 - k * I4) * 4;
-            const float sk = qmul[k] * sc;
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int col = col0 + e4;
-                const int g = col / CW, p = col - g * CW;
-                int c = 0, e = 0;
-                M::place(p, c, e);
-                const float x = __uint_as_float(v[u][e4]) * sk;
-                const _Float16 hx = (_Float16)x;
-                const int dst = ((g * ldn + k) * M::NCALL + c) * 8 + e;
-                hh[dst] = hx;
-                hl[dst] = (_Float16)(x - (float)hx);
-            }
-        }
-    }
-    const int pad = (NCH * 4 - P) * n * M::NCALL;
-    for (int uu = threadIdx.x; uu < pad; uu += kMT) {
-        const int c = uu % M::NCALL;
-        const int k = (uu / M::NCALL) % n;
-        const int g = P + uu / (M::NCALL * n);
-        half8 z;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
-        hi[(g * ldn + k) * M::NCALL + c] = z;
-        lo[(g * ldn + k) * M::NCALL + c] = z;
-    }
-    return kexp;
+    const int P = I / C::CW;
+    zero_pad<BITS>(P, (P + 3) / 4, n, ldn, hi, lo);
 }
 
 // Exclusive prefix over j < n of cnt(j) into out[0..n] (out[n] = total).
@@ -280,10 +362,10 @@ __device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
 // (valid) address, so every item issues exactly two loads and the wait
 // counts before each use are static.
 template <int BITS>
-__device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, float x_unscale,
-                                       float* scratch, GridGate& gate) {
-    using M = MfmaCodec<BITS>;
-    constexpr int NCALL = M::NCALL;
+__device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, const float* xu,
+                                       GridGate& gate) {
+    using C = I8Codec<BITS>;
+    constexpr int NM = C::NM;
     constexpr int W = kStreamW;
     const ExpertArgs& a = f.a;
     const int H = a.H, I = a.I, T = a.T, K = a.top_k, slots = a.slots;
@@ -310,10 +392,10 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int rd = (int)((long long)(b + 1) * H / nwg) - dr0;
     const int qc = f.qc;
     // LDS
-    const half8* xhi = reinterpret_cast<const half8*>(dyn);
-    const half8* xlo = xhi + (size_t)NCHg * 4 * T * NCALL;
-    half8* hhi = reinterpret_cast<half8*>(dyn);                   // replaces x once gate/up is done
-    half8* hlo = hhi + (size_t)NCHd * 4 * qc * NCALL;
+    const i32x4* xhi = reinterpret_cast<const i32x4*>(dyn);
+    const i32x4* xlo = xhi + (size_t)NCHg * 4 * T * NM;
+    i32x4* hhi = reinterpret_cast<i32x4*>(dyn);                   // replaces x once gate/up is done
+    i32x4* hlo = hhi + (size_t)NCHd * 4 * qc * NM;
     float* dred = reinterpret_cast<float*>(dyn);                  // replaces h at the very end
     float* gred = reinterpret_cast<float*>(dyn + f.off_gured);    // [rb][kMW][2][16][T] + counters
     // per partial-sum slot: waves arrived at its block, and blocks finalised through it
@@ -326,7 +408,9 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     int* pstart = reinterpret_cast<int*>(dyn + f.off_pairs);      // [n_act + 1]
     int* qrow = reinterpret_cast<int*>(dyn + f.off_chunk);        // [qc]
     float* qmul = reinterpret_cast<float*>(qrow + qc);            // [qc]
-    int* amap = reinterpret_cast<int*>(qmul + qc);                // [qc][16]
+    unsigned* qmax = reinterpret_cast<unsigned*>(qmul + qc);      // [qc]
+    float* dsl = reinterpret_cast<float*>(qmax + qc);             // [qc]
+    int* amap = reinterpret_cast<int*>(dsl + qc);                 // [qc][16]
     int* ctab = amap + qc * kCols;                                 // [chunks + 1][3]
 
     // row scales of every active expert for this workgroup's rows: LDS from here on
@@ -450,14 +534,19 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         }
     };
 
-    floatx4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
-    floatx4 acc[kNBD], tot[kNBD];
+    const i32x4 zero4 = {0, 0, 0, 0};
+    i32x4 gh = zero4, gl = zero4, uh = zero4, ul = zero4;     // gate / up, hi / lo parts
+    i32x4 ah[kNBD], al[kNBD];
+    floatx4 tot[kNBD];
 #pragma unroll
-    for (int bb = 0; bb < kNBD; ++bb) acc[bb] = tot[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float d_unscale = 1.f;
+    for (int bb = 0; bb < kNBD; ++bb) {
+        ah[bb] = al[bb] = zero4;
+        tot[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     int chunk_first = 0;            // first expert of the staged chunk
-    // per-expert state of the computing cursor
+    // per-expert state of the computing cursor: this lane's staged column and its unscale
     int cj = -1, cbq = -1;
+    float du = 0.f;
 
     // Columns of the MFMA output that no token uses hold garbage and are never
     // read, so B operands need no zeroing; chunks past the row end are skipped.
@@ -465,21 +554,21 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     auto gu_item = [&](const Cursor& c, const uint4* cur) {
         const int ch = wave * nkg + c.k;
         if (ch < NCHg) {
-            half8 bh[NCALL], bl[NCALL];
+            i32x4 bh[NM], bl[NM];
 #pragma unroll
-            for (int cc = 0; cc < NCALL; ++cc) {
-                const int src = ((ch * 4 + lq) * T + tcol) * NCALL + cc;
-                bh[cc] = xhi[src];
-                bl[cc] = xlo[src];
+            for (int m = 0; m < NM; ++m) {
+                const int src = ((ch * 4 + lq) * T + tcol) * NM + m;
+                bh[m] = xhi[src];
+                bl[m] = xlo[src];
             }
 #pragma unroll
-            for (int cc = 0; cc < NCALL; ++cc) {
-                const half8 ag = a_operand<BITS>(cur[0], cc);
-                accg = mfma::mfma(ag, bh[cc], accg);
-                accg = mfma::mfma(ag, bl[cc], accg);
-                const half8 au = a_operand<BITS>(cur[1], cc);
-                accu = mfma::mfma(au, bh[cc], accu);
-                accu = mfma::mfma(au, bl[cc], accu);
+            for (int m = 0; m < NM; ++m) {
+                const i32x4 ag = operand<BITS>(cur[0], m);
+                gh = mma(ag, bh[m], gh);
+                gl = mma(ag, bl[m], gl);
+                const i32x4 au = operand<BITS>(cur[1], m);
+                uh = mma(au, bh[m], uh);
+                ul = mma(au, bl[m], ul);
             }
         }
         if (c.k == nkg - 1) {
@@ -506,11 +595,11 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = accg[ii];
-                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = accu[ii];
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
                 }
             }
-            accg = accu = floatx4{0.f, 0.f, 0.f, 0.f};
+            gh = gl = uh = ul = zero4;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             int arrived = 0;
             if (lane == 0)
@@ -532,8 +621,8 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                             gs += part[((w * 2 + 0) * 16 + rr) * T + t];
                             vs += part[((w * 2 + 1) * 16 + rr) * T + t];
                         }
-                        const float gv = gs * x_unscale * gsc[(j * 2 + 0) * rg + r];
-                        const float uv = vs * x_unscale * gsc[(j * 2 + 1) * rg + r];
+                        const float gv = gs * xu[t] * gsc[(j * 2 + 0) * rg + r];
+                        const float uv = vs * xu[t] * gsc[(j * 2 + 1) * rg + r];
                         hprod[(j * rg + r) * T + n] = gv / (1.0f + __expf(-gv)) * uv;
                     }
                 }
@@ -550,24 +639,25 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         if (c.j != cj) {
             cj = c.j;
             cbq = amap[(cj - chunk_first) * kCols + ln];      // staged slot of this lane's token, or -1
+            du = cbq >= 0 ? dsl[cbq] : 0.f;
         }
         const int ch = wave * nkd + c.k;
         if (ch < NCHd) {
             const int slot = max(cbq, 0);
-            half8 bh[NCALL], bl[NCALL];
+            i32x4 bh[NM], bl[NM];
 #pragma unroll
-            for (int cc = 0; cc < NCALL; ++cc) {
-                const int src = ((ch * 4 + lq) * qc + slot) * NCALL + cc;
-                bh[cc] = hhi[src];
-                bl[cc] = hlo[src];
+            for (int m = 0; m < NM; ++m) {
+                const int src = ((ch * 4 + lq) * qc + slot) * NM + m;
+                bh[m] = hhi[src];
+                bl[m] = hlo[src];
             }
 #pragma unroll
             for (int bb = 0; bb < kNBD; ++bb) {
 #pragma unroll
-                for (int cc = 0; cc < NCALL; ++cc) {
-                    const half8 av = a_operand<BITS>(cur[bb], cc);
-                    acc[bb] = mfma::mfma(av, bh[cc], acc[bb]);
-                    acc[bb] = mfma::mfma(av, bl[cc], acc[bb]);
+                for (int m = 0; m < NM; ++m) {
+                    const i32x4 av = operand<BITS>(cur[bb], m);
+                    ah[bb] = mma(av, bh[m], ah[bb]);
+                    al[bb] = mma(av, bl[m], al[bb]);
                 }
             }
         }
@@ -578,12 +668,12 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) {
                         const int rr = min(bb * 16 + 4 * lq + i2, rd - 1);
-                        tot[bb][i2] += (dsc[cj * rd + rr] * d_unscale) * acc[bb][i2];
+                        tot[bb][i2] += (dsc[cj * rd + rr] * du) * combine(ah[bb][i2], al[bb][i2]);
                     }
                 }
             }
 #pragma unroll
-            for (int bb = 0; bb < kNBD; ++bb) acc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int bb = 0; bb < kNBD; ++bb) ah[bb] = al[bb] = zero4;
         }
     };
 
@@ -609,15 +699,15 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             qmul[ql] = sl < K ? r.selw[t * K + sl] : 1.0f;
         }
         for (int i = threadIdx.x; i < (jl - jf + 1) * kCols; i += kMT) amap[i] = -1;
+        for (int i = threadIdx.x; i < nq; i += kMT) qmax[i] = 0u;
         __syncthreads();
         for (int ql = threadIdx.x; ql < nq; ql += kMT) {
             const int jj = mw_upper_index(seg, n_act, q0 + ql);
             amap[(jj - jf) * kCols + qrow[ql] / slots] = ql;
         }
         if (q == 0) gate.wait(2);     // every workgroup's h is out
-        const int kexp = stage_h<BITS>(f.h, A * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, scratch);
+        stage_h<BITS>(f.h, A * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl);
         __syncthreads();
-        d_unscale = ldexpf(1.0f, -kexp);
         chunk_first = jf;
         cj = -1;                      // the computing cursor reloads its expert's column map
     };
@@ -683,18 +773,19 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
 
 template <int BITS>
 __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
-    constexpr int NCALL = MfmaCodec<BITS>::NCALL;
+    constexpr int NM = I8Codec<BITS>::NM;
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ FusedRoute r;
     __shared__ float gemv_red[kCols][kMW];
-    __shared__ int tok_s[kCols];
-    __shared__ float scratch[kMW];
+    __shared__ unsigned xmax[kCols];
+    __shared__ float xu[kCols];
 
     const ExpertArgs& a = f.a;
     const int T = a.T, H = a.H, K = a.top_k, S = f.n_shared, E = f.E;
     const int NCHg = ((H * BITS / 8) / 16 + 3) / 4;
-    half8* xhi = reinterpret_cast<half8*>(dyn);
-    half8* xlo = xhi + (size_t)NCHg * 4 * T * NCALL;
+    i32x4* xhi = reinterpret_cast<i32x4*>(dyn);
+    i32x4* xlo = xhi + (size_t)NCHg * 4 * T * NM;
+    if (threadIdx.x < kCols) xmax[threadIdx.x] = 0u;
     const int spin = f.ws[kWsSpin] > 0 ? f.ws[kWsSpin] : kSpinDefault;
     unsigned long long* count = reinterpret_cast<unsigned long long*>(f.ws);
     // the count is a multiple of nwg between launches: this launch's barrier completes at the next one
@@ -704,9 +795,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     // ---- phase 1
     router_rows(f, blockIdx.x, gridDim.x, gemv_red);
     gate.arrive();
-    if (threadIdx.x < kCols) tok_s[threadIdx.x] = threadIdx.x;
-    __syncthreads();
-    const int kexp_x = stage_b<BITS>(f.x, H, H, tok_s, nullptr, T, T, xhi, xlo, scratch);
+    stage_x<BITS>(f.x, H, T, xhi, xlo, xmax, xu);
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
@@ -726,7 +815,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     }
 
     // ---- phase 3: the stream
-    stream<BITS>(f, r, dyn, ldexpf(1.0f, -kexp_x), scratch, gate);
+    stream<BITS>(f, r, dyn, xu, gate);
 }
 
 size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -752,7 +841,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const int max_active = l.ex.max_active;
     if (static_lds + kLdsOnePerCu > kLdsMax) return hipErrorInvalidValue;
     const size_t avail = kLdsMax - static_lds;
-    const size_t x_bytes = align16(staged_row_bytes<BITS>(H) * T);
+    const size_t x_bytes = align16(staged_row_bytes_i8<BITS>(H) * T);
     const size_t dred_bytes = (size_t)kMW * kNBD * 256 * sizeof(float);
     const int n_blocks = (max_active * rg + 15) / 16;
     const int rb = n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8;   // partial-sum slots
@@ -763,14 +852,14 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t hprod = align16((size_t)max_active * rg * T * sizeof(float));
     const size_t fixed = gured + gsc + dsc + pairs + hprod;
     auto staging = [&](int q) {
-        size_t s = align16(staged_row_bytes<BITS>(I) * q);
+        size_t s = align16(staged_row_bytes_i8<BITS>(I) * q);
         if (s < x_bytes) s = x_bytes;
         if (s < dred_bytes) s = dred_bytes;
         return s;
     };
     auto total = [&](int q) {
         const size_t chunks = (size_t)(A + q - 1) / q;
-        return staging(q) + fixed + align16(((size_t)q * (2 + kCols) + 3 * (chunks + 1)) * sizeof(int));
+        return staging(q) + fixed + align16(((size_t)q * (4 + kCols) + 3 * (chunks + 1)) * sizeof(int));
     };
     int qc = A;
     if ((size_t)qc * I > (size_t)kStageV4 * 4 * kMT) qc = kStageV4 * 4 * kMT / I;   // a chunk's h fits registers
