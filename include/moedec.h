@@ -171,20 +171,23 @@ int moe_expert_down_combine_q2(const float* h, const moedec_experts* ex, const m
  *   y                          : fp32 [T, H] (the layer output)
  *   workspace : int32 [MOEDEC_FUSED_WORKSPACE_INTS], device memory the caller
  *       zeroes once before the first call and then leaves to the library; it
- *       holds the state of the launch's grid-wide barriers, so launches that
- *       may run at the same time need separate workspaces.  After the call
- *       (once the stream has reached it) workspace[2] != 0 means a barrier
- *       wait timed out: not every workgroup could be resident at once (the
- *       GPU was shared with other work); that call's outputs are invalid and
- *       the workspace must be zeroed again.  workspace[3] > 0 caps the
- *       barrier wait at that many polling rounds (0: about two seconds).
+ *       holds the arrival counters of the launch's two grid-wide exchanges, so
+ *       launches that may run at the same time need separate workspaces, and
+ *       one workspace serves one GPU.  After the call (once the stream has
+ *       reached it) workspace[MOEDEC_FUSED_WS_ERROR] != 0 means a wait timed
+ *       out: not every workgroup could be resident at once (the GPU was
+ *       shared with other work); that call's outputs are invalid and the
+ *       workspace must be zeroed again.  workspace[MOEDEC_FUSED_WS_SPIN] > 0
+ *       caps each wait at that many polling rounds (0: about two seconds).
  * The scores may differ from moe_route_topk's in the last bits (another
  * summation order); routing and results are otherwise those of the separate
  * calls given the same scores.  Limits: T <= MOEDEC_FUSED_MAX_TOKENS,
  * n_experts <= MOEDEC_FUSED_MAX_EXPERTS, else MOEDEC_ERR_UNSUPPORTED (use the
  * separate calls).
  */
-#define MOEDEC_FUSED_WORKSPACE_INTS 16
+#define MOEDEC_FUSED_WORKSPACE_INTS 1024
+#define MOEDEC_FUSED_WS_ERROR 512
+#define MOEDEC_FUSED_WS_SPIN 513
 #define MOEDEC_FUSED_MAX_TOKENS 16
 #define MOEDEC_FUSED_MAX_EXPERTS 512
 int moe_layer_fused_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,

@@ -63,6 +63,16 @@ __device__ __forceinline__ int wave_min(int v) {
     return min(min(r0, r1), min(r2, r3));
 }
 
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+    v = max(v, (unsigned)dpp_i<0xB1>((int)v));
+    v = max(v, (unsigned)dpp_i<0x4E>((int)v));
+    v = max(v, (unsigned)dpp_i<0x141>((int)v));
+    v = max(v, (unsigned)dpp_i<0x140>((int)v));
+    const unsigned r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const unsigned r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // Same for a group size known only at run time (small shapes; not hot).
 __device__ __forceinline__ float group_sum_rt(float v, int lpr) {
     for (int off = 1; off < lpr; off <<= 1) v += __shfl_xor(v, off, 64);

@@ -15,8 +15,8 @@
 //   1. router rows e = b, b + nwg, ...: s = sigmoid(W_r x), stored for all;
 //      arrive at the grid barrier; stage x as MFMA B operands in LDS; wait;
 //   2. every workgroup routes the batch itself from the scores (route.h), so
-//      the worklist needs no second exchange; workgroup 0 also writes the
-//      routing and worklist outputs;
+//      the worklist needs no second exchange (workgroup 0 writes the routing
+//      and worklist outputs from LDS at the very end);
 //   3. the stream, through one ring of in-flight 16-byte loads per wave:
 //      gate/up of every active expert (this workgroup's rows
 //      [b*I/nwg, (b+1)*I/nwg) of each, expert by expert, its h kept in LDS and
@@ -60,14 +60,18 @@ constexpr int kFusedExperts = 512;                      // routed experts at mos
 using FusedRoute = RouteLdsT<kCols, kFusedExperts, kMW>;
 constexpr int kRowF4 = MOEDEC_MAX_DIM / 4 / kMT;        // float4 of a router row per thread
 constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a couple of seconds
-constexpr int kStreamW = 4;                             // stream items in flight per wave
+constexpr int kStreamW = 3;                             // stream items in flight per wave (3 measured best)
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
 constexpr int kStageX4 = 12;                            // float4 of x a thread holds at once
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
 
-// workspace words: [0, 1] the 64-bit arrival counter, [2] error, [3] spin cap
-constexpr int kWsError = 2, kWsSpin = 3;
+// Workspace: kGates 64-bit arrival counters 256 bytes apart (workgroup b
+// counts on counter b % kGates, so arrivals on different counters do not
+// queue behind each other), then the error word and the spin cap.
+constexpr int kGates = 8, kGateStride = 64;
+constexpr int kWsError = MOEDEC_FUSED_WS_ERROR, kWsSpin = MOEDEC_FUSED_WS_SPIN;
+static_assert(kGates * kGateStride <= kWsError && kWsSpin < MOEDEC_FUSED_WORKSPACE_INTS, "workspace layout");
 
 struct FusedArgs {
     ExpertArgs a;                  // experts; its worklist pointers are unused
@@ -98,29 +102,52 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Split-phase grid barrier (see the file comment).  arrive(): the workgroup's
-// stores complete, then one thread adds its arrival (no wait for the add).
-// wait(): that thread polls the counter until every workgroup has arrived,
-// invalidates the caches it reads through, and the workgroup resynchronises.
+// Split-phase grid barrier (see the file comment).  settle(): the
+// workgroup's stores have completed; count(): one thread adds the workgroup's
+// arrival (no wait for the add).  Loads issued between the two do not queue
+// behind the add.  wait(): lanes of wave 0 poll the counters until every
+// workgroup has arrived, the caches read through are invalidated, and the
+// workgroup resynchronises.  Each launch adds 2 to every counter per member
+// workgroup, so a counter's launch index is its count / (2 * members), read
+// by each workgroup from its own counter before its first arrival.
 struct GridGate {
-    unsigned long long* count;
-    int32_t* error;
+    int32_t* ws;
     int spin_max;
-    unsigned long long base;        // the count when this launch started (a multiple of nwg)
+    unsigned long long launch;      // launches completed on this workspace before this one
 
-    __device__ void arrive() {
+    __device__ __forceinline__ static int members(int i) { return ((int)gridDim.x - i + kGates - 1) / kGates; }
+    __device__ __forceinline__ unsigned long long* counter(int i) const {
+        return reinterpret_cast<unsigned long long*>(ws + i * kGateStride);
+    }
+    __device__ __forceinline__ void init() {
+        const int own = blockIdx.x % kGates;
+        const unsigned long long found = __hip_atomic_load(counter(own), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        launch = found / (2ull * members(own));
+    }
+    __device__ __forceinline__ void settle() {
         __builtin_amdgcn_s_waitcnt(0);     // this wave's stores (device scope) have completed
         __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_fetch_add(count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ void count() {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(counter(blockIdx.x % kGates), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ void arrive() {
+        settle();
+        count();
     }
     // exchange x (1 or 2) of this launch is complete
-    __device__ void wait(int x) {
-        if (threadIdx.x == 0) {
-            const unsigned long long target = base + (unsigned long long)x * gridDim.x;
+    __device__ __forceinline__ void wait(int x) {
+        if (threadIdx.x < kWave) {
+            const int i = threadIdx.x;
+            const int m = i < kGates ? members(i) : 0;
+            const unsigned long long target = (2ull * launch + (unsigned long long)x) * (unsigned long long)m;
             int n = 0;
-            while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            while (true) {
+                const bool done = m == 0 || __hip_atomic_load(counter(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+                if (__ballot(!done) == 0) break;
                 if (++n >= spin_max) {
-                    __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (i == 0) __hip_atomic_store(ws + kWsError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
@@ -232,9 +259,9 @@ __device__ __forceinline__ void zero_pad(int P, int NCH, int n, int ldn, i32x4* 
 // xu[t] = 2^-(e_t + kShift) undoes it and the code factor.  cmax[0..T) must
 // be zero on entry.  When all of x fits the registers (kStageX4 float4 per
 // thread) it is read once, else twice (a max pass and a convert pass).
-template <int BITS>
+template <int BITS, typename Hook>
 __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int T, i32x4* hi, i32x4* lo,
-                                        unsigned* cmax, float* xu) {
+                                        unsigned* cmax, float* xu, Hook&& after_loads) {
     using C = I8Codec<BITS>;
     const int H4 = H >> 2, total4 = T * H4;
     const float4* x4 = reinterpret_cast<const float4*>(x);
@@ -245,6 +272,10 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int 
         for (int u = 0; u < kStageX4; ++u) {           // every load first, then use
             const int i4 = b0 + (int)threadIdx.x + u * kMT;
             v[u] = x4[min(i4, total4 - 1)];
+        }
+        if (b0 == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            after_loads();
         }
 #pragma unroll
         for (int u = 0; u < kStageX4; ++u) {
@@ -377,19 +408,21 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int* eid = r.eid;
     const int* seg = r.seg;
     const int* asn = r.assign;
-    // gate/up geometry: this workgroup's rows [gr0, gr0 + rg) of every expert,
-    // taken as one list rho = j*rg + r (expert j, row gr0 + r) cut into 16-row
-    // blocks, so a block may hold rows of two experts: B carries every token,
+    // gate/up geometry: every active expert's rows as one list (entry j*I + r
+    // is row r of expert j); this workgroup takes the contiguous stretch
+    // [g0, g0 + NR) of it -- one or two runs of consecutive code rows, which
+    // stream faster than a few rows of every expert -- cut into 16-row
+    // blocks; a block may hold rows of two experts: B carries every token,
     // and each row keeps only the columns of tokens routed to its expert
     const int rbg = H * BITS / 8, Pg = rbg >> 4, NCHg = (Pg + 3) >> 2, nkg = (NCHg + kMW - 1) / kMW;
-    const int gr0 = (int)((long long)b * I / nwg);
-    const int rg = (int)((long long)(b + 1) * I / nwg) - gr0;
-    const int NR = n_act * rg;
+    const long long NRT = (long long)n_act * I;
+    const int g0 = (int)(NRT * b / nwg);
+    const int NR = (int)(NRT * (b + 1) / nwg) - g0;
     const int nbg = (NR + 15) >> 4;
     // down geometry: output rows [dr0, dr0 + rd), rd <= 32
     const int rbd = I * BITS / 8, Pd = rbd >> 4, NCHd = (Pd + 3) >> 2, nkd = (NCHd + kMW - 1) / kMW;
-    const int dr0 = (int)((long long)b * H / nwg);
-    const int rd = (int)((long long)(b + 1) * H / nwg) - dr0;
+    const int dr0 = b * H / nwg;
+    const int rd = (b + 1) * H / nwg - dr0;
     const int qc = f.qc;
     // LDS
     const i32x4* xhi = reinterpret_cast<const i32x4*>(dyn);
@@ -402,8 +435,8 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int rb = f.rb;
     int* slot_cnt = reinterpret_cast<int*>(gred + (size_t)rb * kMW * 2 * 16 * T);
     int* slot_done = slot_cnt + rb;
-    float* gsc = reinterpret_cast<float*>(dyn + f.off_gsc);       // [n_act][2][rg]
-    float* hprod = reinterpret_cast<float*>(dyn + f.off_hprod);   // [n_act][rg][T]: this workgroup's h
+    float* gsc = reinterpret_cast<float*>(dyn + f.off_gsc);       // [NR][2]: gate, up row scales
+    float* hprod = reinterpret_cast<float*>(dyn + f.off_hprod);   // [NR][T]: this workgroup's h
     float* dsc = reinterpret_cast<float*>(dyn + f.off_dsc);       // [n_act][rd]
     int* pstart = reinterpret_cast<int*>(dyn + f.off_pairs);      // [n_act + 1]
     int* qrow = reinterpret_cast<int*>(dyn + f.off_chunk);        // [qc]
@@ -413,19 +446,6 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     int* amap = reinterpret_cast<int*>(dsl + qc);                 // [qc][16]
     int* ctab = amap + qc * kCols;                                 // [chunks + 1][3]
 
-    // row scales of every active expert for this workgroup's rows: LDS from here on
-    for (int i = threadIdx.x; i < n_act * rg; i += kMT) {
-        const int j = i / rg, rr = i - j * rg;
-        const size_t src = (size_t)eid[j] * I + gr0 + rr;
-        gsc[(j * 2 + 0) * rg + rr] = a.s_gate[src];
-        gsc[(j * 2 + 1) * rg + rr] = a.s_up[src];
-    }
-    for (int i = threadIdx.x; i < n_act * rd; i += kMT) {
-        const int j = i / rd, rr = i - j * rd;
-        dsc[j * rd + rr] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
-    }
-    // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc
-    block_prefix(n_act, [&](int j) { return (seg[j + 1] - 1) / qc - seg[j] / qc + 1; }, pstart);
     // Positions: the gate/up items, then each down chunk's items, every segment
     // padded to a multiple of W, so a segment starts at ring slot 0 and its
     // start (h out, chunk staging) runs between rounds, outside the unrolled
@@ -434,23 +454,6 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int Ngu = nbg * nkg;
     const int Gpad = (Ngu + W - 1) / W * W;
     const int nchunk = rd > 0 ? (A + qc - 1) / qc : 0;
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int q = 0; q < nchunk; ++q) {
-            const int jf = mw_upper_index(seg, n_act, q * qc);
-            const int jl = mw_upper_index(seg, n_act, min(A, (q + 1) * qc) - 1);
-            const int p0 = pstart[jf] + (q - seg[jf] / qc), p1 = pstart[jl] + (q - seg[jl] / qc);
-            ctab[3 * q] = run;                        // first position (after Gpad)
-            ctab[3 * q + 1] = (p1 - p0 + 1) * nkd;    // items
-            ctab[3 * q + 2] = p0;                     // first pair
-            run += (ctab[3 * q + 1] + W - 1) / W * W;
-        }
-        ctab[3 * nchunk] = run;
-    }
-    __syncthreads();
-    const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
-    if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
-    if (Np == 0) return;
 
     // Two cursors walk the positions in order, one W positions ahead issuing
     // loads, one computing; a cursor advances by counting (no division or
@@ -517,8 +520,8 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             if (c.blk != iblk) {
                 iblk = c.blk;
                 const int rho = min(iblk * 16 + ln, NR - 1);
-                const int j = rho / rg;
-                irow_off = ((size_t)eid[j] * I + gr0 + (rho - j * rg)) * rbg;
+                const int g = g0 + rho, j = g / I;
+                irow_off = ((size_t)eid[j] * I + (g - j * I)) * rbg;
             }
             const int cc = min(wave * nkg + c.k, NCHg - 1);
             const int grp = min(cc * 4 + lq, Pg - 1);
@@ -611,7 +614,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                 for (int idx = lane; idx < rows_blk * T; idx += kWave) {
                     const int rr = idx / T, t = idx - rr * T;
                     const int rho = bidx * 16 + rr;
-                    const int j = rho / rg, r = rho - j * rg;
+                    const int j = (g0 + rho) / I;
                     const int s0 = seg[j], nc = seg[j + 1] - s0;
                     int n = 0;
                     while (n < nc && asn[s0 + n] / slots != t) ++n;     // token t's column of expert j
@@ -621,9 +624,9 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                             gs += part[((w * 2 + 0) * 16 + rr) * T + t];
                             vs += part[((w * 2 + 1) * 16 + rr) * T + t];
                         }
-                        const float gv = gs * xu[t] * gsc[(j * 2 + 0) * rg + r];
-                        const float uv = vs * xu[t] * gsc[(j * 2 + 1) * rg + r];
-                        hprod[(j * rg + r) * T + n] = gv / (1.0f + __expf(-gv)) * uv;
+                        const float gv = gs * xu[t] * gsc[rho * 2 + 0];
+                        const float uv = vs * xu[t] * gsc[rho * 2 + 1];
+                        hprod[rho * T + n] = gv / (1.0f + __expf(-gv)) * uv;
                     }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -679,11 +682,10 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
 
     // segment starts, between rounds
     auto flush_h = [&]() {            // all of this workgroup's h: out at once (device scope), then counted
-        for (int idx = threadIdx.x; idx < n_act * rg * T; idx += kMT) {
-            const int jj = idx / (rg * T), rem = idx - jj * rg * T;
-            const int row = rem / T, n = rem - row * T;
-            if (n < seg[jj + 1] - seg[jj])
-                store_device(f.h + (size_t)asn[seg[jj] + n] * I + gr0 + row, hprod[idx]);
+        for (int idx = threadIdx.x; idx < NR * T; idx += kMT) {
+            const int rho = idx / T, n = idx - rho * T;
+            const int g = g0 + rho, jj = g / I;
+            if (n < seg[jj + 1] - seg[jj]) store_device(f.h + (size_t)asn[seg[jj] + n] * I + (g - jj * I), hprod[idx]);
         }
         gate.arrive();
     };
@@ -712,18 +714,63 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         cj = -1;                      // the computing cursor reloads its expert's column map
     };
 
-    for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
-    __syncthreads();
-
+    // The stream's first loads go out before the down chunk tables are built
+    // (only down items read them) when the gate/up segment holds more than a
+    // ring's worth of items, so the filling cursor stays inside it.
     Cursor ci, cc_;
-    start(ci);
-    start(cc_);
     uint4 ring[W][2];
+    auto fill = [&]() {
+        start(ci);
+        start(cc_);
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-        issue(ci, ring[w]);
-        advance(ci);
+        for (int w = 0; w < W; ++w) {
+            issue(ci, ring[w]);
+            advance(ci);
+        }
+    };
+    const bool early = Gpad > W;
+    // Nothing issued earlier is still in flight (routing consumed its
+    // loads); saying so here keeps later register reuse from waiting for
+    // the ring's loads.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (early) fill();
+
+    // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc
+    block_prefix(n_act, [&](int j) { return (seg[j + 1] - 1) / qc - seg[j] / qc + 1; }, pstart);
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int q = 0; q < nchunk; ++q) {
+            const int jf = mw_upper_index(seg, n_act, q * qc);
+            const int jl = mw_upper_index(seg, n_act, min(A, (q + 1) * qc) - 1);
+            const int p0 = pstart[jf] + (q - seg[jf] / qc), p1 = pstart[jl] + (q - seg[jl] / qc);
+            ctab[3 * q] = run;                        // first position (after Gpad)
+            ctab[3 * q + 1] = (p1 - p0 + 1) * nkd;    // items
+            ctab[3 * q + 2] = p0;                     // first pair
+            run += (ctab[3 * q + 1] + W - 1) / W * W;
+        }
+        ctab[3 * nchunk] = run;
     }
+    __syncthreads();
+    const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
+    if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
+    if (Np == 0) return;
+    if (!early) fill();
+    for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
+    // Row scales of every active expert for this workgroup's rows, to LDS:
+    // loaded after the ring is filled, so their latency overlaps the ring's
+    // (the first items wait for the ring anyway).
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = threadIdx.x; i < NR; i += kMT) {
+        const int g = g0 + i, j = g / I;
+        const size_t src = (size_t)eid[j] * I + (g - j * I);
+        gsc[i * 2 + 0] = a.s_gate[src];
+        gsc[i * 2 + 1] = a.s_up[src];
+    }
+    for (int i = threadIdx.x; i < n_act * rd; i += kMT) {
+        const int j = i / rd, rr = i - j * rd;
+        dsc[i] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
+    }
+    __syncthreads();
     // gate/up segment, then the down chunks: two loops, so each hot loop holds
     // one kind of item (the ring and both cursors carry over, Gpad % W == 0)
     for (int base = 0; base < Gpad; base += W) {
@@ -786,20 +833,24 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     i32x4* xhi = reinterpret_cast<i32x4*>(dyn);
     i32x4* xlo = xhi + (size_t)NCHg * 4 * T * NM;
     if (threadIdx.x < kCols) xmax[threadIdx.x] = 0u;
-    const int spin = f.ws[kWsSpin] > 0 ? f.ws[kWsSpin] : kSpinDefault;
-    unsigned long long* count = reinterpret_cast<unsigned long long*>(f.ws);
-    // the count is a multiple of nwg between launches: this launch's barrier completes at the next one
-    const unsigned long long found = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    GridGate gate{count, f.ws + kWsError, spin, found / gridDim.x * gridDim.x};
+    GridGate gate{f.ws, f.ws[kWsSpin] > 0 ? f.ws[kWsSpin] : kSpinDefault, 0ull};
+    gate.init();
 
     // ---- phase 1
     router_rows(f, blockIdx.x, gridDim.x, gemv_red);
-    gate.arrive();
-    stage_x<BITS>(f.x, H, T, xhi, xlo, xmax, xu);
+    gate.settle();
+    stage_x<BITS>(f.x, H, T, xhi, xlo, xmax, xu, [&] { gate.count(); });   // x loads go out before the count
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
     route_select_block(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
+
+    // ---- phase 3: the stream
+    stream<BITS>(f, r, dyn, xu, gate);
+
+    // Workgroup 0 writes the routing outputs last, from LDS: stores issued
+    // earlier would make the compiler wait for the stream's first loads
+    // wherever it reuses their registers.
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < T * K; i += kMT) {
             f.topk_idx[i] = r.sel[i];
@@ -813,9 +864,6 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
         }
         for (int i = threadIdx.x; i < T * a.slots; i += kMT) f.wl_assign[i] = r.assign[i];
     }
-
-    // ---- phase 3: the stream
-    stream<BITS>(f, r, dyn, xu, gate);
 }
 
 size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -835,7 +883,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     }
     const int nwg = cu_count();
     const int H = l.ex.H, I = l.ex.I, T = l.T;
-    const int rg = (I + nwg - 1) / nwg, rd = (H + nwg - 1) / nwg;
+    const int rd = (H + nwg - 1) / nwg;
     if (rd > kNBD * 16) return hipErrorInvalidValue;             // more output rows than a pass holds
     const int A = T * l.ex.slots;
     const int max_active = l.ex.max_active;
@@ -843,13 +891,14 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t avail = kLdsMax - static_lds;
     const size_t x_bytes = align16(staged_row_bytes_i8<BITS>(H) * T);
     const size_t dred_bytes = (size_t)kMW * kNBD * 256 * sizeof(float);
-    const int n_blocks = (max_active * rg + 15) / 16;
+    const int nr_max = (int)(((long long)max_active * I + nwg - 1) / nwg);   // gate/up rows of a workgroup
+    const int n_blocks = (nr_max + 15) / 16;
     const int rb = n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8;   // partial-sum slots
     const size_t gured = align16((size_t)rb * kMW * 2 * 16 * T * sizeof(float) + 2 * rb * sizeof(int));
-    const size_t gsc = align16((size_t)max_active * rg * 2 * sizeof(float));
+    const size_t gsc = align16((size_t)nr_max * 2 * sizeof(float));
     const size_t dsc = align16((size_t)max_active * rd * sizeof(float));
     const size_t pairs = align16((size_t)(max_active + 1) * sizeof(int));
-    const size_t hprod = align16((size_t)max_active * rg * T * sizeof(float));
+    const size_t hprod = align16((size_t)nr_max * T * sizeof(float));
     const size_t fixed = gured + gsc + dsc + pairs + hprod;
     auto staging = [&](int q) {
         size_t s = align16(staged_row_bytes_i8<BITS>(I) * q);

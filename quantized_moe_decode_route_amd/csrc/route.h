@@ -50,11 +50,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 //   2. lane g < n_group: group score = largest + second largest c of group g;
 //   3. lane g: rank among the group scores; kept if rank < topk_group;
 //   4. top_k rounds of a wave arg-max over the kept groups' experts, by
-//      (c descending, index ascending) -- DPP and lane reads, no LDS round
-//      trips; round k's winner is slot k, and the total of the chosen s is
-//      summed in slot order as the rounds go;
+//      (c descending, index ascending), on order-preserving integer keys of
+//      c -- branch-free selects, DPP and lane reads, no LDS round trips;
+//      round k's winner is slot k, and the total of the chosen s is summed
+//      in slot order as the rounds go;
 //   5. lane k < top_k: weight k = s_k / total * rsf.
-// The worklist is then a rank sort of the assignments by (expert, assignment).
+// The worklist is then a rank sort of the assignments by (expert, assignment)
+// (one wave when they fit its lanes, else the whole workgroup).
 // A NaN corrected score or group score ranks below every number (as -inf,
 // ties by index), so every slot gets a distinct valid expert whatever the
 // inputs hold.
@@ -109,34 +111,41 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
             for (int h = 0; h < n_group; ++h) grank += beats(r.gs[wave][h], h, gsv, lane);
         }
         const unsigned long long kept = __ballot(lane < n_group && grank < topk_group);
-        unsigned cand = 0;                             // bit j: expert lane + 64 j is a candidate
+        // Candidates as order-preserving 32-bit keys of c (+0 for -0, so equal
+        // values tie and go by index); 0 (below -inf's key) marks an expert
+        // that is not, or no longer, a candidate.
+        const float inv_per = 1.0f / (float)per;
+        unsigned key[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const int g = min((lane + kWave * j) / per, 63);
-            if (((live >> j) & 1u) && ((kept >> g) & 1ull)) cand |= 1u << j;
+            const int e = lane + kWave * j;
+            int g = (int)((float)e * inv_per);          // e / per, then corrected
+            g += (g + 1) * per <= e;
+            g -= g * per > e;
+            const unsigned u = __float_as_uint(cl[j] + 0.0f);
+            const unsigned ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            key[j] = (((live >> j) & 1u) && ((kept >> min(g, 63)) & 1ull)) ? ord : 0u;
         }
-        // round k: each lane's best candidate (ascending j keeps the lower index
-        // on ties), the wave's largest c, then the lowest index holding it
+        // round k: each lane's best (largest key, lowest j on ties), the
+        // wave's largest key, then the lowest expert index holding it
         float total = 0.f, my_s = 0.f;
         for (int k = 0; k < top_k; ++k) {
-            bool bvalid = false;
-            float bv = -INFINITY, bs = 0.f;
-            int bj = 0;
+            unsigned bk = key[NV - 1];
+            int bj = NV - 1;
+            float bs = sl[NV - 1];
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                if (((cand >> j) & 1u) && (!bvalid || cl[j] > bv)) {
-                    bv = cl[j];
-                    bs = sl[j];
-                    bj = j;
-                    bvalid = true;
-                }
+            for (int j = NV - 2; j >= 0; --j) {
+                const bool better = key[j] >= bk;
+                bk = better ? key[j] : bk;
+                bj = better ? j : bj;
+                bs = better ? sl[j] : bs;
             }
-            const float m = wave_max(bvalid ? bv : -INFINITY);
-            const int bi = wave_min(bvalid && bv == m ? lane + kWave * bj : INT_MAX);
-            const int win = bi == INT_MAX ? 0 : bi;   // INT_MAX cannot happen: top_k <= kept experts
+            const unsigned m = wave_max_u(bk);
+            const int win = wave_min(bk == m ? lane + kWave * bj : INT_MAX);   // top_k <= candidates
             const int owner = win & (kWave - 1), jw = win / kWave;
             const float sw = bits_f(__builtin_amdgcn_readlane(f_bits(bs), owner));
-            if (lane == owner) cand &= ~(1u << jw);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) key[j] = (lane == owner && j == jw) ? 0u : key[j];
             if (lane == 0) r.sel[t * top_k + k] = win;
             if (lane == k) my_s = sw;
             total += sw;                               // slot order
@@ -148,6 +157,40 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
     // batch union: rank sort of the assignments by (expert, assignment index)
     const int slots = top_k + n_shared;
     const int A = T * slots;
+    if (A <= kWave) {                  // one wave, no workgroup barriers
+        if (wave == 0) {
+            int k = INT_MAX;
+            if (lane < A) {
+                const int tt = lane / slots, s = lane - tt * slots;
+                const int e = s < top_k ? r.sel[tt * top_k + s] : E + (s - top_k);
+                k = (e << 16) | lane;
+                r.key[lane] = k;
+            }
+            wave_lds_sync();
+            int rank = 0;
+            for (int b = 0; b < A; ++b) rank += r.key[b] < k;
+            if (lane < A) {
+                r.assign[rank] = lane;
+                r.sexp[rank] = k >> 16;
+            }
+            wave_lds_sync();
+            const int ex = lane < A ? r.sexp[lane] : -1;
+            const bool first = lane < A && (lane == 0 || r.sexp[max(lane - 1, 0)] != ex);
+            const unsigned long long fm = __ballot(first);
+            const int sidx = __popcll(fm & ((1ull << lane) - 1ull));
+            if (first) {
+                r.eid[sidx] = ex;
+                r.seg[sidx] = lane;
+            }
+            if (lane == 0) {
+                const int n = __popcll(fm);
+                r.n_active = n;
+                r.seg[n] = A;
+            }
+        }
+        __syncthreads();
+        return;
+    }
     for (int a = threadIdx.x; a < A; a += blockDim.x) {
         const int t = a / slots, s = a - t * slots;
         const int e = s < top_k ? r.sel[t * top_k + s] : E + (s - top_k);

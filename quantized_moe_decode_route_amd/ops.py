@@ -65,7 +65,9 @@ MOEDEC_ERR_UNSUPPORTED = 2
 # limits of the fused layer call (include/moedec.h)
 FUSED_MAX_TOKENS = 16
 FUSED_MAX_EXPERTS = 512
-FUSED_WORKSPACE_INTS = 16
+FUSED_WORKSPACE_INTS = 1024
+FUSED_WS_ERROR = 512            # workspace word: a wait timed out
+FUSED_WS_GATES, FUSED_WS_GATE_STRIDE = 8, 64   # arrival counters (int64) every 64 int32 words
 
 
 def lib() -> ctypes.CDLL:
@@ -298,8 +300,15 @@ class LayerBuffers:
                             torch.zeros(FUSED_WORKSPACE_INTS, dtype=torch.int32, device=device))
 
     def fused_error(self) -> bool:
-        """True if a fused launch's barrier timed out (synchronises)."""
-        return bool(self.workspace[2].item() != 0)
+        """True if a fused launch's wait timed out (synchronises)."""
+        return bool(self.workspace[FUSED_WS_ERROR].item() != 0)
+
+
+def fused_arrivals(workspace: torch.Tensor) -> int:
+    """Arrivals counted in a fused-call workspace so far: the sum of its
+    counters (synchronises).  Each launch adds two per workgroup."""
+    c = workspace[:FUSED_WS_GATES * FUSED_WS_GATE_STRIDE].view(torch.int64)[::FUSED_WS_GATE_STRIDE // 2]
+    return int(c.sum().item())
 
 
 def fused_supported(T: int, ex: Experts) -> bool:

@@ -155,3 +155,15 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 256)
     with pytest.raises(ValueError):
         ops._dev(x, torch.float32, "x")
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's limits and workspace layout."""
+    import re
+    src = open(os.path.join(os.path.dirname(ops.__file__), "..", "include", "moedec.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(MOEDEC_\w+)\s+(\d+)", src)}
+    assert defs["MOEDEC_FUSED_WORKSPACE_INTS"] == ops.FUSED_WORKSPACE_INTS
+    assert defs["MOEDEC_FUSED_WS_ERROR"] == ops.FUSED_WS_ERROR
+    assert defs["MOEDEC_FUSED_MAX_TOKENS"] == ops.FUSED_MAX_TOKENS
+    assert defs["MOEDEC_FUSED_MAX_EXPERTS"] == ops.FUSED_MAX_EXPERTS
+    assert ops.FUSED_WS_GATES * ops.FUSED_WS_GATE_STRIDE <= ops.FUSED_WS_ERROR

@@ -1,6 +1,6 @@
 """The single-launch layer call beyond plain parity: every launch adds exactly
 two arrivals per workgroup (the scores exchange and the h exchange) to the
-workspace counter, and launches back to back on one workspace and HIP-graph
+workspace counters, and launches back to back on one workspace and HIP-graph
 replays give the eager results bit for bit (every reduction in the kernel has
 a fixed order, so equal inputs give equal bits)."""
 import numpy as np
@@ -58,8 +58,8 @@ def test_back_to_back_launches_share_a_workspace():
                       fused=True, **KW)
     torch.cuda.synchronize()
     nwg = torch.cuda.get_device_properties(DEV).multi_processor_count
-    count = int(ws.view(torch.int64)[0].item())
-    err = int(ws[2].item())
+    count = ops.fused_arrivals(ws)
+    err = int(ws[ops.FUSED_WS_ERROR].item())
     say(f"  workspace after {n} launches: arrivals {count} (2 x {nwg} workgroups each), error {err}")
     assert count == 2 * n * nwg and err == 0
     for i in range(n):
@@ -95,5 +95,5 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {i} differs from the eager run"
     nwg = torch.cuda.get_device_properties(DEV).multi_processor_count
     # the warm-up launch and n replays (capture runs nothing)
-    assert int(buf.workspace.view(torch.int64)[0].item()) == 2 * (n + 1) * nwg
+    assert ops.fused_arrivals(buf.workspace) == 2 * (n + 1) * nwg
 
