@@ -63,6 +63,7 @@ constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a co
 constexpr int kStreamW = 3;                             // stream items in flight per wave (3 measured best)
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
 constexpr int kStageX4 = 12;                            // float4 of x a thread holds at once
+constexpr size_t kDeferLds = 48 * 1024;                 // partial sums of all gate/up blocks at most
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
 
@@ -92,6 +93,7 @@ struct FusedArgs {
     float rsf;
     int qc;                        // assignments staged at once for down
     int rb;                        // gate/up blocks whose partial sums LDS holds at once
+    int deferred;                  // 1: every block has its own slot and is finalised after the segment
     int off_gured, off_gsc, off_dsc, off_pairs, off_chunk, off_hprod;   // dynamic LDS layout (bytes)
 };
 
@@ -103,11 +105,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Split-phase grid barrier (see the file comment).  settle(): the
-// workgroup's stores have completed; count(): one thread adds the workgroup's
-// arrival (no wait for the add).  Loads issued between the two do not queue
-// behind the add.  wait(): lanes of wave 0 poll the counters until every
-// workgroup has arrived, the caches read through are invalidated, and the
-// workgroup resynchronises.  Each launch adds 2 to every counter per member
+// workgroup's stores have completed; count(): the last wave adds the
+// workgroup's arrival (no wait for the add); wait(): the same wave polls the
+// counters until every workgroup has arrived, invalidates the caches read
+// through, and the workgroup resynchronises.  A wave's loads complete in
+// issue order, so only the counting wave's loads queue behind the add --
+// the poll does anyway -- and loads issued before the count do not.  Each launch adds 2 to every counter per member
 // workgroup, so a counter's launch index is its count / (2 * members), read
 // by each workgroup from its own counter before its first arrival.
 struct GridGate {
@@ -129,7 +132,7 @@ struct GridGate {
         __syncthreads();
     }
     __device__ __forceinline__ void count() {
-        if (threadIdx.x == 0)
+        if ((int)threadIdx.x == kMT - kWave)
             __hip_atomic_fetch_add(counter(blockIdx.x % kGates), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __device__ __forceinline__ void arrive() {
@@ -138,8 +141,8 @@ struct GridGate {
     }
     // exchange x (1 or 2) of this launch is complete
     __device__ __forceinline__ void wait(int x) {
-        if (threadIdx.x < kWave) {
-            const int i = threadIdx.x;
+        if ((int)threadIdx.x >= kMT - kWave) {
+            const int i = (int)threadIdx.x - (kMT - kWave);
             const int m = i < kGates ? members(i) : 0;
             const unsigned long long target = (2ull * launch + (unsigned long long)x) * (unsigned long long)m;
             int n = 0;
@@ -218,24 +221,46 @@ __device__ __forceinline__ void column_max(unsigned* cmax, int t, float m) {
     }
 }
 
-// Scatter 4 consecutive columns col0.. of row k (already scaled by 2^e) into
-// the int8 B layout: unit ((g*ldn + k)*NM + m) of hi / lo, slot s, for column
-// g*CW + col(m, s).
+// Scatter 4 consecutive columns col0.. (col0 % 4 == 0) of row k, already
+// scaled by 2^e, into the int8 B layout: unit ((g*ldn + k)*NM + m) of hi /
+// lo, slot s, for column g*CW + col(m, s).  Within a float4 the slots follow
+// a fixed pattern per code width, so the bytes go out in whole 16- or 32-bit
+// writes where they are adjacent: int4 columns (p, p+2) and (p+1, p+3) are
+// slots (s, s+1) of operands 0 and 1; int8 columns are 4 consecutive slots;
+// int2 columns are one slot of each of the 4 operands.
+__device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)d << 24);
+}
+
 template <int BITS>
 __device__ __forceinline__ void scatter4(float4 v, float sc, int col0, int k, int ldn, uint8_t* hi, uint8_t* lo) {
     using C = I8Codec<BITS>;
-    const float xs[4] = {v.x * sc, v.y * sc, v.z * sc, v.w * sc};
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-        const int col = col0 + e4;
-        const int g = col / C::CW, p = col - g * C::CW;
-        int m = 0, sl = 0;
-        C::place(p, m, sl);
-        int h8 = 0, l8 = 0;
-        split16(xs[e4], h8, l8);
-        const int dst = ((g * ldn + k) * C::NM + m) * 16 + sl;
-        hi[dst] = (uint8_t)h8;
-        lo[dst] = (uint8_t)l8;
+    int h0, h1, h2, h3, l0, l1, l2, l3;
+    split16(v.x * sc, h0, l0);
+    split16(v.y * sc, h1, l1);
+    split16(v.z * sc, h2, l2);
+    split16(v.w * sc, h3, l3);
+    const int g = col0 / C::CW, p0 = col0 - g * C::CW;
+    const int unit = (g * ldn + k) * C::NM * 16;
+    if constexpr (BITS == 4) {
+        const int s0 = unit + 4 * (p0 >> 3) + ((p0 >> 1) & 3);      // even: 2-byte aligned
+        *reinterpret_cast<uint16_t*>(hi + s0) = (uint16_t)pack_bytes(h0, h2, 0, 0);
+        *reinterpret_cast<uint16_t*>(hi + s0 + 16) = (uint16_t)pack_bytes(h1, h3, 0, 0);
+        *reinterpret_cast<uint16_t*>(lo + s0) = (uint16_t)pack_bytes(l0, l2, 0, 0);
+        *reinterpret_cast<uint16_t*>(lo + s0 + 16) = (uint16_t)pack_bytes(l1, l3, 0, 0);
+    } else if constexpr (BITS == 8) {
+        *reinterpret_cast<uint32_t*>(hi + unit + p0) = pack_bytes(h0, h1, h2, h3);
+        *reinterpret_cast<uint32_t*>(lo + unit + p0) = pack_bytes(l0, l1, l2, l3);
+    } else {
+        const int s0 = unit + 4 * (p0 >> 4) + ((p0 >> 2) & 3);
+        hi[s0] = (uint8_t)h0;
+        hi[s0 + 16] = (uint8_t)h1;
+        hi[s0 + 32] = (uint8_t)h2;
+        hi[s0 + 48] = (uint8_t)h3;
+        lo[s0] = (uint8_t)l0;
+        lo[s0 + 16] = (uint8_t)l1;
+        lo[s0 + 32] = (uint8_t)l2;
+        lo[s0 + 48] = (uint8_t)l3;
     }
 }
 
@@ -574,7 +599,19 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                 ul = mma(au, bl[m], ul);
             }
         }
-        if (c.k == nkg - 1) {
+        if (c.k == nkg - 1 && f.deferred) {
+            // every block has a slot of its own: leave the partial sums there;
+            // all blocks are finalised together after the gate/up segment
+            float* part = gred + (size_t)c.blk * kMW * 2 * 16 * T;
+            if (ln < T) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
+                }
+            }
+            gh = gl = uh = ul = zero4;
+        } else if (c.k == nkg - 1) {
             // This wave's part of the block is done.  No workgroup barrier here
             // (every one would wait for the slowest wave's loads): the wave leaves
             // its partial sums in the block's LDS slot and counts itself; the
@@ -783,7 +820,29 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             advance(cc_);
         }
     }
-    __syncthreads();                  // every block finalised (hprod complete)
+    __syncthreads();                  // every block's partial sums are in (and, ring slots: finalised)
+    if (f.deferred) {                 // h = silu(g) * v of every row and routed token, in parallel
+        for (int idx = threadIdx.x; idx < NR * T; idx += kMT) {
+            const int rho = idx / T, t = idx - rho * T;
+            const int j = (g0 + rho) / I;
+            const int s0 = seg[j], nc = seg[j + 1] - s0;
+            int n = 0;
+            while (n < nc && asn[s0 + n] / slots != t) ++n;     // token t's column of expert j
+            if (n < nc) {
+                const float* part = gred + (size_t)(rho >> 4) * kMW * 2 * 16 * T;
+                const int rr = rho & 15;
+                float gs = 0.f, vs = 0.f;
+                for (int w = 0; w < kMW; ++w) {
+                    gs += part[((w * 2 + 0) * 16 + rr) * T + t];
+                    vs += part[((w * 2 + 1) * 16 + rr) * T + t];
+                }
+                const float gv = gs * xu[t] * gsc[rho * 2 + 0];
+                const float uv = vs * xu[t] * gsc[rho * 2 + 1];
+                hprod[rho * T + n] = gv / (1.0f + __expf(-gv)) * uv;
+            }
+        }
+        __syncthreads();
+    }
     if (Ngu > 0) flush_h();
     cj = -1;
     int next_chunk = 0;
@@ -893,7 +952,11 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t dred_bytes = (size_t)kMW * kNBD * 256 * sizeof(float);
     const int nr_max = (int)(((long long)max_active * I + nwg - 1) / nwg);   // gate/up rows of a workgroup
     const int n_blocks = (nr_max + 15) / 16;
-    const int rb = n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8;   // partial-sum slots
+    // partial-sum slots: one per block when they fit kDeferLds (finalised
+    // after the segment), else a ring of 8 reused in order
+    const size_t slot_bytes = (size_t)kMW * 2 * 16 * T * sizeof(float);
+    const bool deferred = n_blocks >= 1 && (size_t)n_blocks * slot_bytes <= kDeferLds;
+    const int rb = deferred ? n_blocks : (n_blocks < 8 ? (n_blocks < 1 ? 1 : n_blocks) : 8);
     const size_t gured = align16((size_t)rb * kMW * 2 * 16 * T * sizeof(float) + 2 * rb * sizeof(int));
     const size_t gsc = align16((size_t)nr_max * 2 * sizeof(float));
     const size_t dsc = align16((size_t)max_active * rd * sizeof(float));
@@ -917,6 +980,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t stg = staging(qc);
     f.qc = qc;
     f.rb = rb;
+    f.deferred = deferred ? 1 : 0;
     f.off_gured = (int)stg;
     f.off_gsc = (int)(stg + gured);
     f.off_dsc = (int)(stg + gured + gsc);
