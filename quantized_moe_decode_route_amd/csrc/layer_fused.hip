@@ -107,8 +107,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Split-phase grid barrier (see the file comment).  settle(): the
 // workgroup's stores have completed; count(): the last wave adds the
 // workgroup's arrival (no wait for the add); wait(): the same wave polls the
-// counters until every workgroup has arrived, invalidates the caches read
-// through, and the workgroup resynchronises.  A wave's loads complete in
+// counters until every workgroup has arrived, and the workgroup
+// resynchronises.  The data exchanged is read afterwards with device-coherent
+// loads only, so no cache is invalidated.  A wave's loads complete in
 // issue order, so only the counting wave's loads queue behind the add --
 // the poll does anyway -- and loads issued before the count do not.  Each launch adds 2 to every counter per member
 // workgroup, so a counter's launch index is its count / (2 * members), read
@@ -155,7 +156,6 @@ struct GridGate {
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
     }
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
-    route_select_block(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
+    route_select_block<kCols, kFusedExperts, kMW, true>(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
 
     // ---- phase 3: the stream
     stream<BITS>(f, r, dyn, xu, gate);

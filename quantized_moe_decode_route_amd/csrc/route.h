@@ -60,7 +60,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // A NaN corrected score or group score ranks below every number (as -inf,
 // ties by index), so every slot gets a distinct valid expert whatever the
 // inputs hold.
-template <int TM, int EM, int NW>
+// kCoherentScores: read the scores with device-coherent loads (scores that
+// other workgroups of the same launch have just written), else plain loads.
+template <int TM, int EM, int NW, bool kCoherentScores = false>
 __device__ __forceinline__ void route_select_block(const float* scores, const float* __restrict__ bias, int T,
                                                    int E, int n_group, int topk_group, int top_k, int n_shared,
                                                    float rsf, RouteLdsT<TM, EM, NW>& r) {
@@ -75,7 +77,11 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
 #pragma unroll
         for (int j = 0; j < NV; ++j) {                 // every load first (clamped index), then use
             const int e = min(lane + kWave * j, E - 1);
-            sl[j] = scores[(size_t)t * E + e];
+            if constexpr (kCoherentScores)
+                sl[j] = __int_as_float(__hip_atomic_load(reinterpret_cast<const int*>(scores + (size_t)t * E + e),
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            else
+                sl[j] = scores[(size_t)t * E + e];
             bl[j] = bias[e];
         }
         unsigned live = 0;                             // bit j: expert lane + 64 j exists
