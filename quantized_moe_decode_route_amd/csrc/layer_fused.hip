@@ -62,7 +62,7 @@ constexpr int kRowF4 = MOEDEC_MAX_DIM / 4 / kMT;        // float4 of a router ro
 constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a couple of seconds
 constexpr int kStreamW = 3;                             // stream items in flight per wave (3 measured best)
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
-constexpr int kStageX4 = 12;                            // float4 of x a thread holds at once
+constexpr int kStageX4 = 4;                             // float4 of x a thread holds at once
 constexpr size_t kDeferLds = 48 * 1024;                 // partial sums of all gate/up blocks at most
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
@@ -726,8 +726,10 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         }
         gate.arrive();
     };
-    auto dn_stage = [&](int q) {
-        lds_barrier();                // everyone is done with the previous B operands
+    // Down chunk q's tables (they depend on the routing only): rows of h to
+    // stage and their weights, and each expert's column map; the caller
+    // synchronises before the map is read.
+    auto dn_prep = [&](int q) {
         const int q0 = q * qc, q1 = min(A, q0 + qc), nq = q1 - q0;
         const int jf = mw_upper_index(seg, n_act, q0);
         const int jl = mw_upper_index(seg, n_act, q1 - 1);
@@ -744,10 +746,15 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             const int jj = mw_upper_index(seg, n_act, q0 + ql);
             amap[(jj - jf) * kCols + qrow[ql] / slots] = ql;
         }
+    };
+    auto dn_stage = [&](int q) {
+        lds_barrier();                // everyone is done with the previous chunk
+        if (q > 0) dn_prep(q);        // chunk 0's tables were built during the setup
+        const int q0 = q * qc, nq = min(A, q0 + qc) - q0;
         if (q == 0) gate.wait(2);     // every workgroup's h is out
         stage_h<BITS>(f.h, A * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl);
         __syncthreads();
-        chunk_first = jf;
+        chunk_first = mw_upper_index(seg, n_act, q0);
         cj = -1;                      // the computing cursor reloads its expert's column map
     };
 
@@ -791,6 +798,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
     if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
     if (Np == 0) return;
+    if (nchunk > 0) dn_prep(0);       // while the ring's first loads are in flight
     if (!early) fill();
     for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
     // Row scales of every active expert for this workgroup's rows, to LDS:
