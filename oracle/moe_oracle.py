@@ -47,6 +47,11 @@ Readings (the pages are silent on these):
  R14 shared experts have weight 1 (not scaled by routed_scaling_factor).
  R15 the multi-layer stack is x <- x + MoE(rmsnorm(x)) with a weightless
      RMSNorm (eps 1e-6).
+ R20 requantising fp32 rows: s = absmax(row) / qmax, qmax = 2^(bits-1) - 1
+     (7 / 127 / 1), q = rint(w / s) half to even, clamped to the field; a
+     zero row gets s = 0 and codes 0.  Decided in fp32.
+ R21 a row holding a NaN or an infinity gets s = NaN and codes 0, so that the
+     problem shows in every output computed from it.
 
 Precision.  Routing decisions are taken in fp32, as the kernel takes them
 (scores rounded to fp32, c = s + b and the group sums in fp32, weights in
@@ -59,9 +64,12 @@ round trips and hand-derived byte fixtures; brute-force subset enumeration of
 group and expert selection; the one-group case against a library sort; the
 all-tied case; the weights-sum invariant; the one-hot-input and all-equal
 closed forms of the FFN; the RMSNorm closed form; the ~19 MB expert size of
-[HN-S].  Parity unpinned by the pages: the group-score rule R1 and the code
-layouts R8-R10 are readings; the tests pin the oracle to those readings, not
-the readings to the pages.
+[HN-S]; for the row quantiser, hand-worked rows, the exact round trip of code
+rows that reach +-qmax, the nearest-code brute force over the whole code
+alphabet, and the sign and power-of-two scaling symmetries.  Parity unpinned
+by the pages: the group-score rule R1, the code layouts R8-R10 and the
+quantiser rule R20-R21 are readings; the tests pin the oracle to those
+readings, not the readings to the pages.
 """
 from __future__ import annotations
 
@@ -119,6 +127,44 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
     w = unpack_rows(packed, bits).astype(np.float64)
     w *= np.asarray(scales, dtype=np.float64)[:, None]
     return w
+
+
+# ------------------------------------------------------------- row quantiser
+# [HN] implemented features: the offline converter item (dequantise from
+# 128x128 block scales, then requantise into the engine's container) and the
+# quantisation item (one scale per row).  The rule is reading R20; R21 covers
+# rows that hold a NaN or an infinity.
+
+def quantize_rows(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """fp32 rows [rows, n] -> (int8 codes [rows, n], fp32 scales [rows]).
+
+    Per row, in fp32 (the precision of the input, and the one the kernel
+    decides the codes in): s = absmax / qmax with qmax = 2^(bits-1) - 1, and
+    q = rint(w / s) (round half to even) clamped to the field's range (R20).
+    A zero row (absmax 0, or s rounding to 0) gets s = 0 and codes 0; a row
+    holding a NaN or an infinity gets s = NaN and codes 0 (R21)."""
+    assert bits in SUPPORTED_BITS
+    w32 = np.asarray(w, dtype=np.float32)
+    assert w32.ndim == 2
+    rows, n = w32.shape
+    lo, hi = code_range(bits)
+    qmax = np.float32(hi)
+    codes = np.zeros((rows, n), dtype=np.int8)
+    scales = np.zeros(rows, dtype=np.float32)
+    for r in range(rows):
+        row = w32[r]
+        if not np.all(np.isfinite(row)):
+            scales[r] = np.float32(np.nan)
+            continue
+        absmax = np.max(np.abs(row)) if n else np.float32(0.0)
+        s = np.float32(absmax / qmax)                      # one fp32 division
+        if s == 0:
+            continue
+        scales[r] = s
+        ratio = (row / s).astype(np.float32)               # fp32 division per element
+        q = np.rint(ratio)                                 # half to even
+        codes[r] = np.clip(q, lo, hi).astype(np.int8)
+    return codes, scales
 
 
 # --------------------------------------------------------------------- router
