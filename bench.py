@@ -39,7 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc")
 # sources each timed kernel is built from (the traffic counters are void once any changes)
 KERNEL_SRCS = {"fused": ["layer_fused.hip", "imma.h", "mfma.h", "route.h", "common.h"],
-               "gate_up": ["experts_mfma.hip", "mfma.h", "common.h"]}
+               "gate_up": ["experts_mfma.hip", "mfma.h", "common.h"],
+               "quantize": ["quant.hip", "common.h"]}
 
 
 def step_bytes(cfg, n_active: int) -> int:
@@ -125,6 +126,105 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
                       f"{elapsed:.1f} s of oracle time, 1 thread"}
 
 
+def quantize_bytes(rows: int, n: int, bits: int) -> int:
+    """Algorithmic bytes of one quantiser launch: the fp32 rows read once, the
+    packed codes and the row scales written once."""
+    return rows * n * 4 + rows * n * bits // 8 + rows * 4
+
+
+def bench_quantize(args) -> None:
+    """The row quantiser on GLM-5.2 expert matrices: int4, packed output, one
+    launch per matrix ([4096, 6144] gate+up rows, [6144, 2048] down rows),
+    rotating over 8 experts' fp32 matrices (1.2 GB) so no launch finds its input
+    in the caches; a step is one launch.  Prints one JSON line of its own."""
+    import torch
+
+    from quantized_moe_decode_route_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bits, n_exp = 4, 8
+    shapes = [(4096, 6144), (6144, 2048)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    mats, outs, scl = [], [], []
+    for e in range(n_exp):
+        for rows, n in shapes:
+            w = torch.randn((rows, n), generator=g, device=dev) * 0.02
+            mats.append(w)
+            outs.append(torch.empty((rows, n * bits // 8), dtype=torch.uint8, device=dev))
+            scl.append(torch.empty(rows, dtype=torch.float32, device=dev))
+    # per matrix shape: one HIP graph of the 8 experts' launches, replayed
+    # back to back; the launch average is the event-timed region / launches
+    stream = torch.cuda.Stream()
+    reps = max(args.steps // 160, 4)
+    per, tot_bytes, tot_s, launches = {}, 0, 0.0, 0
+    for si, (rows, n) in enumerate(shapes):
+        idx = [e * len(shapes) + si for e in range(n_exp)]
+        with torch.cuda.stream(stream):
+            for k in idx:
+                ops.quantize_rows(mats[k], bits, pack=True, out=outs[k], scales=scl[k])
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for k in idx:
+                ops.quantize_rows(mats[k], bits, pack=True, out=outs[k], scales=scl[k])
+        with torch.cuda.stream(stream):
+            graph.replay()
+            ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev_a.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            ev_b.record(stream)
+        stream.synchronize()
+        region = ev_a.elapsed_time(ev_b) * 1e-3
+        nl = reps * n_exp
+        b = quantize_bytes(rows, n, bits)
+        per[f"{rows}x{n}"] = {"avg_us": round(region / nl * 1e6, 2), "gbs": round(b * nl / region / 1e9, 1),
+                              "bytes_per_launch": b}
+        tot_bytes += b * nl
+        tot_s += region
+        launches += nl
+    value = tot_bytes / tot_s / 1e9
+    print(f"[bench] quantiser: {launches} launches, {value:.0f} GB/s ({per})", file=sys.stderr, flush=True)
+    # the dominant kernel: the gate/up-shaped launch (2/3 of the bytes)
+    dom = per["4096x6144"]
+    achieved = dom["bytes_per_launch"] / (dom["avg_us"] * 1e-6) / 1e9
+
+    base = None
+    if args.cpu_budget > 0:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import moe_oracle as orc
+        w = mats[0][:256].cpu().numpy()
+        t_used, nbytes, reps = 0.0, 0, 0
+        with threadpool_limits(limits=1):
+            while t_used < min(args.cpu_budget, 10.0) or reps == 0:
+                t0 = time.perf_counter()
+                orc.pack_rows(orc.quantize_rows(w, bits)[0], bits)
+                t_used += time.perf_counter() - t0
+                nbytes += quantize_bytes(w.shape[0], w.shape[1], bits)
+                reps += 1
+        base = {"value": round(nbytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{reps} x 256 rows of 6144 fp32 -> packed int4, {t_used:.1f} s, 1 thread"}
+
+    out = {
+        "metric": "row quantiser achieved HBM GB/s (fp32 expert matrices -> packed int4 codes + row scales)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": launches, "warmup": len(shapes) * n_exp,
+        "ms_per_step": round(tot_s / launches * 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "glm_expert_matrices_q4", "matrices": [list(s) for s in shapes], "experts": n_exp,
+                   "bits": bits, "output": "packed"},
+        "roofline": {"bound": "hbm", "kernel": "quantize_rows_cached<4, true, 4, 6> (4096 x 6144)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("quantize", "glm_expert_matrices_q4"),
+                     "avg_us": dom["avg_us"], "bytes_per_launch": dom["bytes_per_launch"], "per_shape": per},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,14 +236,15 @@ def main() -> None:
     ap.add_argument("--kernel-steps", type=int, default=100, help="eager gate/up launches timed (split path)")
     ap.add_argument("--split", action="store_true", help="time the three separate calls instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time the row quantiser instead (fp32 expert matrices -> packed codes + row scales)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 20 times (a known-size "
                          "reference for the HBM traffic counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -158,6 +259,10 @@ def main() -> None:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 20}), flush=True)
+        return
+
+    if args.quantize:
+        bench_quantize(args)
         return
 
     cfg = synth.CONFIGS[args.workload]

@@ -221,6 +221,37 @@ int moe_pack_q2(const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_
 int moe_unpack_q2(const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len, void* stream);
 
 /*
+ * Row quantiser: fp32 weight rows -> codes and one fp32 scale per row (Show
+ * HN page, "implemented features": the offline converter requantises the
+ * dequantised checkpoint into the engine's container; the quantisation item:
+ * int8, packed int4, packed int2 with a scale per row).  The pages state no
+ * rule; the one implemented: per row s = absmax / qmax (qmax = 127 / 7 / 1,
+ * one IEEE fp32 division), code = rint(w / s) with ties to even (IEEE fp32
+ * division) clamped to the field.  A row whose s is 0 (all zeros, or absmax
+ * so small that s underflows) gets s = 0 and codes 0; a row holding a NaN or
+ * an infinity gets s = NaN and codes 0.  Bit-exact and deterministic.
+ *   w      : fp32 [rows, row_len], 16-byte aligned; row_len % 4 == 0
+ *   codes  : int8 [rows, row_len] (one code per byte, as moe_pack_* reads),
+ *            4-byte aligned                       (moe_quantize_rows_q*)
+ *   packed : uint8 [rows, row_len*bits/8] in the moe_pack_* layout; 2-byte
+ *            aligned for q4, 4-byte for q8        (moe_quantize_pack_rows_q*)
+ *   scales : fp32 [rows], 4-byte aligned
+ * rows == 0 is a no-op; row_len == 0 writes scales of 0.  The caller owns
+ * every buffer; outputs must not overlap w.  Errors: MOEDEC_ERR_INVALID_ARG
+ * for negative sizes, row_len % 4 != 0, null or misaligned pointers;
+ * MOEDEC_ERR_UNSUPPORTED for more than 2^31 - 1 rows (one workgroup a row).
+ */
+int moe_quantize_rows_q8(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len, void* stream);
+int moe_quantize_rows_q4(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len, void* stream);
+int moe_quantize_rows_q2(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len, void* stream);
+int moe_quantize_pack_rows_q8(const float* w, uint8_t* packed, float* scales, int64_t rows, int64_t row_len,
+                              void* stream);
+int moe_quantize_pack_rows_q4(const float* w, uint8_t* packed, float* scales, int64_t rows, int64_t row_len,
+                              void* stream);
+int moe_quantize_pack_rows_q2(const float* w, uint8_t* packed, float* scales, int64_t rows, int64_t row_len,
+                              void* stream);
+
+/*
  * Between stacked MoE layers: x <- x + y (skipped when y is NULL), then
  * xn <- x / sqrt(mean(x^2) + eps) per token (weightless RMSNorm).  The pages
  * describe the MoE layer only; this pre-norm residual form is the reading

@@ -7,6 +7,12 @@
 
 #define MOEDEC_API extern "C" __attribute__((visibility("default")))
 
+namespace moedec {
+// quant.hip
+hipError_t launch_quantize_rows(int bits, bool pack, const float* w, void* out, float* scales, int64_t rows,
+                                int64_t row_len, hipStream_t stream);
+}  // namespace moedec
+
 using namespace moedec;
 
 namespace {
@@ -137,6 +143,20 @@ int unpack(int bits, const uint8_t* packed, int8_t* codes, int64_t rows, int64_t
     return device_status(launch_unpack(bits, packed, codes, rows, row_len, static_cast<hipStream_t>(stream)));
 }
 
+int quantize(int bits, bool pack, const float* w, void* out, float* scales, int64_t rows, int64_t row_len,
+             void* stream) {
+    if (rows < 0 || row_len < 0 || row_len % 4) return MOEDEC_ERR_INVALID_ARG;
+    if (rows == 0) return MOEDEC_OK;
+    if (!scales || (row_len > 0 && (!w || !out))) return MOEDEC_ERR_INVALID_ARG;
+    const uintptr_t out_align = (!pack || bits == 8) ? 4 : bits == 4 ? 2 : 1;
+    if (!aligned16(w) || (reinterpret_cast<uintptr_t>(scales) & 3u) ||
+        (reinterpret_cast<uintptr_t>(out) & (out_align - 1)))
+        return MOEDEC_ERR_INVALID_ARG;
+    if (rows > 0x7FFFFFFF) return MOEDEC_ERR_UNSUPPORTED;              // one workgroup per row
+    return device_status(launch_quantize_rows(bits, pack, w, out, scales, rows, row_len,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 MOEDEC_API const char* moedec_status_string(int status) {
@@ -208,6 +228,31 @@ MOEDEC_API int moe_pack_q2(const int8_t* codes, uint8_t* packed, int64_t rows, i
 }
 MOEDEC_API int moe_unpack_q2(const uint8_t* packed, int8_t* codes, int64_t rows, int64_t row_len, void* stream) {
     return unpack(2, packed, codes, rows, row_len, stream);
+}
+
+MOEDEC_API int moe_quantize_rows_q8(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len,
+                                    void* stream) {
+    return quantize(8, false, w, codes, scales, rows, row_len, stream);
+}
+MOEDEC_API int moe_quantize_rows_q4(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len,
+                                    void* stream) {
+    return quantize(4, false, w, codes, scales, rows, row_len, stream);
+}
+MOEDEC_API int moe_quantize_rows_q2(const float* w, int8_t* codes, float* scales, int64_t rows, int64_t row_len,
+                                    void* stream) {
+    return quantize(2, false, w, codes, scales, rows, row_len, stream);
+}
+MOEDEC_API int moe_quantize_pack_rows_q8(const float* w, uint8_t* packed, float* scales, int64_t rows,
+                                         int64_t row_len, void* stream) {
+    return quantize(8, true, w, packed, scales, rows, row_len, stream);
+}
+MOEDEC_API int moe_quantize_pack_rows_q4(const float* w, uint8_t* packed, float* scales, int64_t rows,
+                                         int64_t row_len, void* stream) {
+    return quantize(4, true, w, packed, scales, rows, row_len, stream);
+}
+MOEDEC_API int moe_quantize_pack_rows_q2(const float* w, uint8_t* packed, float* scales, int64_t rows,
+                                         int64_t row_len, void* stream) {
+    return quantize(2, true, w, packed, scales, rows, row_len, stream);
 }
 
 MOEDEC_API int moe_residual_rmsnorm(float* x, const float* y, float* xn, int T, int H, float eps, void* stream) {

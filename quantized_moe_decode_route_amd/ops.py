@@ -58,6 +58,8 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_expert_down_combine_{_b}"] = ([_P, _P, _P, _P, _I, _I, _P, _P], _I)
     _SIGS[f"moe_pack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_unpack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
+    _SIGS[f"moe_quantize_rows_{_b}"] = ([_P, _P, _P, _I64, _I64, _P], _I)
+    _SIGS[f"moe_quantize_pack_rows_{_b}"] = ([_P, _P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
@@ -269,6 +271,25 @@ def unpack(packed: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> 
     st = fn(_dev(packed, torch.uint8, "packed"), _dev(out, torch.int8, "codes"), rows, n, _stream(packed))
     _check(fn.__name__, st)
     return out
+
+
+def quantize_rows(w: torch.Tensor, bits: int, pack: bool = False, out: torch.Tensor | None = None,
+                  scales: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """moe_quantize_rows_q{bits} (pack=False: int8 codes [rows, n]) or
+    moe_quantize_pack_rows_q{bits} (pack=True: uint8 [rows, n*bits/8]) from
+    fp32 rows [rows, n]; returns (codes or packed, fp32 scales [rows])."""
+    rows, n = w.shape
+    if out is None:
+        out = (torch.empty((rows, n * bits // 8), dtype=torch.uint8, device=w.device) if pack
+               else torch.empty((rows, n), dtype=torch.int8, device=w.device))
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=w.device)
+    name = f"moe_quantize_pack_rows_{_suffix(bits)}" if pack else f"moe_quantize_rows_{_suffix(bits)}"
+    fn = getattr(lib(), name)
+    st = fn(_dev(w, torch.float32, "w"), _dev(out, torch.uint8 if pack else torch.int8, "out"),
+            _dev(scales, torch.float32, "scales"), rows, n, _stream(w))
+    _check(name, st)
+    return out, scales
 
 
 def residual_rmsnorm(x: torch.Tensor, y: torch.Tensor | None, xn: torch.Tensor, eps: float = 1e-6) -> None:

@@ -34,7 +34,7 @@ MIX1 = 0xBF58476D1CE4E5B9
 MIX2 = 0x94D049BB133111EB
 
 # stream kinds
-K_ROUTER, K_BIAS, K_TOKENS, K_GATE, K_UP, K_DOWN, K_SGATE, K_SUP, K_SDOWN, K_ZIPF = range(10)
+K_ROUTER, K_BIAS, K_TOKENS, K_GATE, K_UP, K_DOWN, K_SGATE, K_SUP, K_SDOWN, K_ZIPF, K_FLOATW = range(11)
 _CODE_KIND = {"gate": K_GATE, "up": K_UP, "down": K_DOWN}
 _SCALE_KIND = {"gate": K_SGATE, "up": K_SUP, "down": K_SDOWN}
 
@@ -260,3 +260,21 @@ def layer_device(cfg: MoEConfig, layer: int, device, chunk: int = 32) -> dict:
         s = np.stack([expert_scales(cfg, layer, e, m) for e in range(n)])
         out["s_" + m] = torch.from_numpy(s).to(device)
     return out
+
+
+# ------------------------------------------------- float rows to quantise
+
+def float_weight_rows(seed: int, rows: int, n: int, block: int = 128) -> np.ndarray:
+    """fp32 rows standing in for a dequantised block-scaled checkpoint (the
+    input of the row quantiser): N(0, 1) values times one magnitude per
+    block x block tile, log-uniform over 1e-4 .. 1e-1, with every ninth row
+    heavy-tailed (Student t, 3 degrees of freedom)."""
+    rng = _pcg(stream_key(seed, 0, K_FLOATW, rows, n))
+    w = rng.standard_normal((rows, n))
+    heavy = np.arange(rows) % 9 == 4
+    if heavy.any():
+        w[heavy] = rng.standard_t(3, size=(int(heavy.sum()), n))
+    tiles = 10.0 ** rng.uniform(-4.0, -1.0, size=((rows + block - 1) // block, (n + block - 1) // block))
+    w *= np.repeat(np.repeat(tiles, block, axis=0), block, axis=1)[:rows, :n]
+    return w.astype(np.float32)
+

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 19
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
 
@@ -142,6 +142,23 @@ def test_pack_validation(lib, bits):
     assert up(None, None, 4, 0, None) == 0
     if bits != 8:
         assert pk(FAKE, FAKE, 2, 8 // bits + 1, None) == 1   # row of a partial byte
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("pack", [False, True])
+def test_quantize_validation(lib, bits, pack):
+    fn = getattr(lib, f"moe_quantize_pack_rows_q{bits}" if pack else f"moe_quantize_rows_q{bits}")
+    assert fn(FAKE, FAKE, FAKE, -1, 8, None) == 1                 # negative sizes
+    assert fn(FAKE, FAKE, FAKE, 2, -8, None) == 1
+    assert fn(FAKE, FAKE, FAKE, 2, 6, None) == 1                  # row_len % 4
+    assert fn(None, FAKE, FAKE, 2, 8, None) == 1                  # null pointers
+    assert fn(FAKE, None, FAKE, 2, 8, None) == 1
+    assert fn(FAKE, FAKE, None, 2, 8, None) == 1
+    assert fn(FAKE + 4, FAKE, FAKE, 2, 8, None) == 1              # w not 16-byte aligned
+    assert fn(FAKE, FAKE, FAKE + 2, 2, 8, None) == 1              # scales not 4-byte aligned
+    if not pack or bits != 2:
+        assert fn(FAKE, FAKE + 1, FAKE, 2, 8, None) == 1          # codes / packed words misaligned
+    assert fn(None, None, None, 0, 8, None) == 0                  # no rows: nothing to do
 
 
 def test_rmsnorm_validation(lib):
