@@ -52,6 +52,14 @@ Readings (the pages are silent on these):
      zero row gets s = 0 and codes 0.  Decided in fp32.
  R21 a row holding a NaN or an infinity gets s = NaN and codes 0, so that the
      problem shows in every output computed from it.
+ R22 adaptive expert top-p (the run options' --topp): after the top-k
+     selection, order the K chosen experts by unbiased score s descending
+     (a NaN s last, ties to the lower index), add their s in that order in
+     fp32 and keep the shortest prefix whose sum reaches fp32(p * total),
+     total being the slot-order fp32 sum of R5 (at least one expert; p >= 1
+     keeps all K).  The kept experts stay in slot order in the first slots
+     (the rest hold index -1 and weight 0) and are reweighted by R5 over the
+     kept set alone.  Dropped slots have no assignment in the batch union.
 
 Precision.  Routing decisions are taken in fp32, as the kernel takes them
 (scores rounded to fp32, c = s + b and the group sums in fp32, weights in
@@ -219,6 +227,48 @@ def select_experts(scores: np.ndarray, bias: np.ndarray, n_group: int, topk_grou
     return idx, w
 
 
+def select_experts_topp(scores: np.ndarray, bias: np.ndarray, n_group: int, topk_group: int,
+                        top_k: int, rsf: float, top_p: float):
+    """Group-limited top-k, then the adaptive top-p prefix (R22).
+
+    Returns (idx int32 [T, K], w float32 [T, K], kept int32 [T]); slots past
+    kept[t] hold idx -1 and w 0."""
+    idx, w = select_experts(scores, bias, n_group, topk_group, top_k, rsf)
+    T = idx.shape[0]
+    kept = np.full(T, top_k, dtype=np.int32)
+    if not top_p < 1.0:
+        return idx, w, kept
+    s = np.asarray(scores, dtype=np.float32)
+    rsf32, p32 = np.float32(rsf), np.float32(top_p)
+    out_idx = np.full_like(idx, -1)
+    out_w = np.zeros_like(w)
+    for t in range(T):
+        chosen = [int(e) for e in idx[t]]
+        sv = {e: s[t, e] for e in chosen}
+        total = np.float32(0.0)
+        for e in chosen:                                       # slot order, as R5
+            total = np.float32(total + sv[e])
+        thr = np.float32(p32 * total)
+        by_weight = sorted(chosen, key=lambda e: (np.isnan(sv[e]), -sv[e] if not np.isnan(sv[e]) else 0.0, e))
+        cum, m = np.float32(0.0), top_k
+        for i, e in enumerate(by_weight):
+            cum = np.float32(cum + sv[e])
+            if cum >= thr:
+                m = i + 1
+                break
+        keep = set(by_weight[:m])
+        kept_slots = [e for e in chosen if e in keep]          # slot order
+        total2 = np.float32(0.0)
+        for e in kept_slots:
+            total2 = np.float32(total2 + sv[e])
+        for k, e in enumerate(kept_slots):
+            out_idx[t, k] = e
+            with np.errstate(invalid="ignore", divide="ignore"):
+                out_w[t, k] = np.float32(np.float32(sv[e] / total2) * rsf32)
+        kept[t] = m
+    return out_idx, out_w, kept
+
+
 def selection_margin(scores64: np.ndarray, bias: np.ndarray, n_group: int, topk_group: int,
                      top_k: int) -> np.ndarray:
     """Per token, the smallest fp64 gap that decides the selected set: between
@@ -252,9 +302,29 @@ def order_margin(scores64: np.ndarray, bias: np.ndarray, idx: np.ndarray) -> np.
     c = np.asarray(scores64, np.float64) + np.asarray(bias, np.float64)
     out = np.full(idx.shape[0], np.inf)
     for t in range(idx.shape[0]):
-        v = c[t, idx[t]]
+        v = c[t, idx[t][idx[t] >= 0]]
         if len(v) > 1:
             out[t] = float(np.min(v[:-1] - v[1:]))
+    return out
+
+
+def topp_margin(scores64: np.ndarray, idx_topk: np.ndarray, top_p: float) -> np.ndarray:
+    """Per token, the smallest fp64 distance between a prefix sum of the
+    top-k experts' scores (in score order) and p times their total, relative to
+    the total, and between consecutive scores in that order: where both are
+    wide, any correct fp32 implementation keeps the same prefix (R22)."""
+    out = np.full(idx_topk.shape[0], np.inf)
+    if not top_p < 1.0:
+        return out
+    s = np.asarray(scores64, np.float64)
+    for t in range(idx_topk.shape[0]):
+        v = np.sort(s[t, idx_topk[t]])[::-1]
+        total = v.sum()
+        cum = np.cumsum(v)
+        m = np.min(np.abs(cum - top_p * total)) / max(total, 1e-300)
+        if len(v) > 1:
+            m = min(m, float(np.min(v[:-1] - v[1:])))
+        out[t] = m
     return out
 
 
@@ -275,7 +345,8 @@ def batch_union(idx: np.ndarray, n_experts: int, n_shared: int) -> Worklist:
     owner = {}
     for t in range(T):
         for k in range(K):
-            owner[t * slots + k] = int(idx[t, k])
+            if idx[t, k] >= 0:                             # R22: a dropped slot has no assignment
+                owner[t * slots + k] = int(idx[t, k])
         for j in range(n_shared):
             owner[t * slots + K + j] = n_experts + j
     experts = sorted(set(owner.values()))
@@ -317,22 +388,23 @@ class LayerResult:
     y: np.ndarray           # [T, H] fp64
     margin: np.ndarray      # [T] fp64 selection margin (decides the set)
     order: np.ndarray       # [T] fp64 gap between consecutive slots (decides the order)
+    topp: np.ndarray | None = None   # [T] fp64 top-p prefix margin (R22); inf without top-p
 
 
 def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
               expert: Callable[[int], dict], *, n_group: int, topk_group: int, top_k: int,
-              n_shared: int, rsf: float, bits: int) -> LayerResult:
+              n_shared: int, rsf: float, bits: int, top_p: float = 1.0) -> LayerResult:
     """One routed-MoE layer on T tokens.
 
     expert(e) returns the packed codes and row scales of expert e
     ({q_gate, q_up, q_down, s_gate, s_up, s_down}); routed experts are
     0..E-1, shared ones E..E+S-1.  The selection is taken on the fp64 scores
-    rounded to fp32."""
+    rounded to fp32.  top_p < 1 adds the adaptive top-p prefix (R22)."""
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     E = router_w.shape[0]
     s64 = router_scores(x, router_w)
-    idx, w = select_experts(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf)
+    idx, w, _ = select_experts_topp(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf, top_p)
     wl = batch_union(idx, E, n_shared)
     slots = top_k + n_shared
     y = np.zeros((T, router_w.shape[1]), np.float64)
@@ -351,7 +423,10 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
             coef = float(w[t, slot]) if slot < top_k else 1.0
             y[t] += coef * o
     margin = selection_margin(s64, bias, n_group, topk_group, top_k)
-    return LayerResult(s64, idx, w, wl, h_all, y, margin, order_margin(s64, bias, idx))
+    idx_k, _ = select_experts(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf) if top_p < 1.0 \
+        else (idx, None)
+    return LayerResult(s64, idx, w, wl, h_all, y, margin, order_margin(s64, bias, idx),
+                       topp_margin(s64, idx_k, top_p))
 
 
 def rmsnorm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
