@@ -86,7 +86,7 @@ def traffic_from_profile(kind: str, workload: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s: float) -> dict:
+def cpu_baseline(cfg, budget_s: float, top_p: float | None = None) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_limits
 
@@ -113,7 +113,8 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
                     cache[e] = synth.expert_arrays(cfg, l, e)
             t0 = time.perf_counter()
             r = orc.moe_layer(x, rw, b, cache.__getitem__, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                              top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits)
+                              top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits,
+                              top_p=1.0 if top_p is None else top_p)
             elapsed += time.perf_counter() - t0
             nbytes += step_bytes(cfg, len(r.worklist.expert_id))
             ntok += cfg.tokens
@@ -236,6 +237,8 @@ def main() -> None:
     ap.add_argument("--kernel-steps", type=int, default=100, help="eager gate/up launches timed (split path)")
     ap.add_argument("--split", action="store_true", help="time the three separate calls instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="route with adaptive expert top-p at this p (moe_layer_fused_topp / moe_route_topp)")
     ap.add_argument("--quantize", action="store_true",
                     help="time the row quantiser instead (fp32 expert matrices -> packed codes + row scales)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -287,7 +290,8 @@ def main() -> None:
     fused = (not args.split) and ops.fused_supported(T, experts[0])
     if fused:
         try:
-            ops.layer_fused(tokens(0), layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0], **kw)
+            ops.layer_fused(tokens(0), layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0],
+                            top_p=args.top_p, **kw)
         except ops.MoedecError as err:
             if err.status != ops.MOEDEC_ERR_UNSUPPORTED:
                 raise
@@ -296,7 +300,7 @@ def main() -> None:
     def step(i):
         l = i % L
         ops.moe_layer(tokens(i), layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], fused=fused,
-                      **kw)
+                      top_p=args.top_p, **kw)
 
     # unique experts of every step of the period (routing is a function of (layer, token))
     n_active = np.zeros(period, np.int64)
@@ -380,7 +384,7 @@ def main() -> None:
             sink += flush.sum()
             x = tokens(i)
             ops.route_topk(x, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route,
-                           **kw)
+                           top_p=args.top_p, **kw)
             ev0[k].record()
             ops.gate_up_silu(x, experts[l], bufs[l].route.worklist, cfg.top_k, out=bufs[l].h)
             ev1[k].record()
@@ -390,15 +394,16 @@ def main() -> None:
         torch.cuda.synchronize()
         dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
-    traffic = traffic_from_profile(kind, cfg.name)
-    kname = f"layer_fused_kernel<{cfg.bits}>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
+    traffic = traffic_from_profile(kind, cfg.name) if args.top_p is None else None
+    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}>"
+             if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_us": round(float(dur.mean() * 1e6), 2),
                 "bytes_per_launch": int(np.mean(kb))}
     print(f"[bench] {kname} avg {dur.mean() * 1e6:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
-    base = cpu_baseline(cfg, args.cpu_budget) if args.cpu_budget > 0 else None
+    base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
 
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -409,7 +414,8 @@ def main() -> None:
         "config": {"workload": cfg.name, "path": "fused" if fused else "split", "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
                    "routed_experts": cfg.n_experts, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
                    "top_k": cfg.top_k, "shared_experts": cfg.n_shared, "bits": cfg.bits,
-                   "resident_layers": L, "unique_experts_per_step": float(n_active[idx].mean())},
+                   "resident_layers": L, "unique_experts_per_step": float(n_active[idx].mean()),
+                   "top_p": args.top_p},
         "roofline": roofline, "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

@@ -91,7 +91,9 @@ typedef struct moedec_experts {
  *   assign    : int32 [T*(K+S)]         assignment index t*(K+S)+slot, ascending
  *                                       within each expert; slots 0..K-1 are the
  *                                       routed slots of token t, K..K+S-1 its shared slots
- * Only the first n_active (+1 for seg) entries are defined after the call.
+ * Only the first n_active (+1 for seg) entries are defined after the call,
+ * and the first seg[n_active] of assign (T*(K+S) unless top-p dropped slots,
+ * which get no assignment).
  */
 typedef struct moedec_worklist {
     int32_t* n_active;
@@ -122,6 +124,28 @@ typedef struct moedec_worklist {
 int moe_route_topk(const float* x, const float* router_w, const float* bias,
                    int T, int H, int E, int n_group, int topk_group, int top_k,
                    int n_shared, float routed_scaling_factor,
+                   float* scores, int32_t* topk_idx, float* topk_w,
+                   const moedec_worklist* wl, void* stream);
+
+/*
+ * moe_route_topk followed by adaptive expert top-p (Show HN page, section
+ * "model download और run": the --topp run option, which reads fewer experts;
+ * section "community benchmarks": its measured effect).  The pages give no
+ * rule; the one implemented: after the top-k selection, order the top_k
+ * chosen experts by unbiased score s (descending; a NaN s last; ties to the
+ * lower index), add their s in that order in fp32 and keep the shortest
+ * prefix whose sum reaches fp32(top_p * total), total being the slot-order
+ * fp32 sum of the top_k scores (at least one expert is kept; top_p >= 1
+ * keeps all, exactly as moe_route_topk).  Per token, the kept experts move to
+ * the first slots in their slot order (corrected score descending) with
+ * weights s_k / (slot-order fp32 sum of the kept s) * routed_scaling_factor;
+ * the remaining slots hold index -1 and weight 0 and have no assignment in
+ * the worklist, so no expert is read for them.  Arguments and outputs as for
+ * moe_route_topk; top_p must not be NaN (MOEDEC_ERR_INVALID_ARG).
+ */
+int moe_route_topp(const float* x, const float* router_w, const float* bias,
+                   int T, int H, int E, int n_group, int topk_group, int top_k,
+                   int n_shared, float routed_scaling_factor, float top_p,
                    float* scores, int32_t* topk_idx, float* topk_w,
                    const moedec_worklist* wl, void* stream);
 
@@ -202,6 +226,24 @@ int moe_layer_fused_q2(const float* x, const float* router_w, const float* bias,
                        int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                        float* h, float* y, int32_t* workspace, void* stream);
+
+/*
+ * The fused layer step with the routing of moe_route_topp (adaptive expert
+ * top-p): only the kept experts are streamed.  Arguments as for
+ * moe_layer_fused_q*, plus top_p (not NaN; >= 1 is the plain top-k call).
+ */
+int moe_layer_fused_topp_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                            int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                            float top_p, float* scores, int32_t* topk_idx, float* topk_w,
+                            const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_topp_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                            int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                            float top_p, float* scores, int32_t* topk_idx, float* topk_w,
+                            const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_topp_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                            int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                            float top_p, float* scores, int32_t* topk_idx, float* topk_w,
+                            const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
 
 /*
  * Packing of codes (ideipro.ru: packing checked bit for bit; Show HN page,

@@ -93,10 +93,12 @@ int route_args_ok(int T, int H, int E, int n_group, int topk_group, int top_k, i
 }
 
 int layer_fused(int bits, const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
-                int T, int n_group, int topk_group, int top_k, float rsf, float* scores, int32_t* topk_idx,
-                float* topk_w, const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream) {
+                int T, int n_group, int topk_group, int top_k, float rsf, float top_p, float* scores,
+                int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, float* h, float* y, int32_t* workspace,
+                void* stream) {
     if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w || !h || !y || !workspace)
         return MOEDEC_ERR_INVALID_ARG;
+    if (isnan(top_p)) return MOEDEC_ERR_INVALID_ARG;
     FusedLayerArgs f{};
     int st = check_experts(ex, wl, bits, T, top_k, f.ex);
     if (st != MOEDEC_OK) return st;
@@ -124,6 +126,7 @@ int layer_fused(int bits, const float* x, const float* router_w, const float* bi
     f.topk_group = topk_group;
     f.n_shared = ex->n_shared;
     f.rsf = rsf;
+    f.top_p = top_p;
     const hipError_t err = launch_layer_fused(bits, f, static_cast<hipStream_t>(stream));
     if (err == hipErrorInvalidValue) return MOEDEC_ERR_UNSUPPORTED;   // shapes the LDS plan cannot hold
     return device_status(err);
@@ -171,18 +174,35 @@ MOEDEC_API const char* moedec_status_string(int status) {
 
 MOEDEC_API int moedec_abi_version(void) { return kAbiVersion; }
 
+namespace {
+int route(const float* x, const float* router_w, const float* bias, int T, int H, int E, int n_group,
+          int topk_group, int top_k, int n_shared, float rsf, float top_p, float* scores, int32_t* topk_idx,
+          float* topk_w, const moedec_worklist* wl, void* stream) {
+    if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w) return MOEDEC_ERR_INVALID_ARG;
+    if (wl && (!wl->n_active || !wl->expert_id || !wl->seg || !wl->assign)) return MOEDEC_ERR_INVALID_ARG;
+    if (isnan(top_p)) return MOEDEC_ERR_INVALID_ARG;
+    const int st = route_args_ok(T, H, E, n_group, topk_group, top_k, n_shared, rsf);
+    if (st != MOEDEC_OK) return st;
+    if (!aligned16(x) || !aligned16(router_w)) return MOEDEC_ERR_INVALID_ARG;
+    return device_status(launch_route(x, router_w, bias, T, H, E, n_group, topk_group, top_k, n_shared, rsf, top_p,
+                                      scores, topk_idx, topk_w, wl, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
 MOEDEC_API int moe_route_topk(const float* x, const float* router_w, const float* bias, int T, int H, int E,
                               int n_group, int topk_group, int top_k, int n_shared, float routed_scaling_factor,
                               float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                               void* stream) {
-    if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w) return MOEDEC_ERR_INVALID_ARG;
-    if (wl && (!wl->n_active || !wl->expert_id || !wl->seg || !wl->assign)) return MOEDEC_ERR_INVALID_ARG;
-    const int st = route_args_ok(T, H, E, n_group, topk_group, top_k, n_shared, routed_scaling_factor);
-    if (st != MOEDEC_OK) return st;
-    if (!aligned16(x) || !aligned16(router_w)) return MOEDEC_ERR_INVALID_ARG;
-    return device_status(launch_route(x, router_w, bias, T, H, E, n_group, topk_group, top_k, n_shared,
-                                      routed_scaling_factor, scores, topk_idx, topk_w, wl,
-                                      static_cast<hipStream_t>(stream)));
+    return route(x, router_w, bias, T, H, E, n_group, topk_group, top_k, n_shared, routed_scaling_factor, 1.0f,
+                 scores, topk_idx, topk_w, wl, stream);
+}
+
+MOEDEC_API int moe_route_topp(const float* x, const float* router_w, const float* bias, int T, int H, int E,
+                              int n_group, int topk_group, int top_k, int n_shared, float routed_scaling_factor,
+                              float top_p, float* scores, int32_t* topk_idx, float* topk_w,
+                              const moedec_worklist* wl, void* stream) {
+    return route(x, router_w, bias, T, H, E, n_group, topk_group, top_k, n_shared, routed_scaling_factor, top_p,
+                 scores, topk_idx, topk_w, wl, stream);
 }
 
 MOEDEC_API int moe_expert_gate_up_silu_q4(const float* x, const moedec_experts* ex, const moedec_worklist* wl,
@@ -264,20 +284,44 @@ MOEDEC_API int moe_layer_fused_q4(const float* x, const float* router_w, const f
                                   int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
-    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
-                       topk_idx, topk_w, wl, h, y, workspace, stream);
+    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_topp_q4(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
                                   int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
-    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
-                       topk_idx, topk_w, wl, h, y, workspace, stream);
+    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_topp_q8(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
                                   int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
-    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, scores,
-                       topk_idx, topk_w, wl, h, y, workspace, stream);
+    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_topp_q2(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }

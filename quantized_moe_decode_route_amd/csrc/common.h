@@ -178,7 +178,7 @@ struct ExpertArgs {
 };
 
 hipError_t launch_route(const float* x, const float* router_w, const float* bias, int T, int H,
-                        int E, int n_group, int topk_group, int top_k, int n_shared, float rsf,
+                        int E, int n_group, int topk_group, int top_k, int n_shared, float rsf, float top_p,
                         float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                         hipStream_t stream);
 
@@ -208,6 +208,7 @@ struct FusedLayerArgs {
     int32_t* workspace;
     int T, E, n_group, topk_group, n_shared;
     float rsf;
+    float top_p;               // >= 1: plain top-k
 };
 
 hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);

@@ -90,7 +90,7 @@ struct FusedArgs {
     float* y;
     int32_t* ws;
     int E, n_group, topk_group, n_shared;
-    float rsf;
+    float rsf, top_p;
     int qc;                        // assignments staged at once for down
     int rb;                        // gate/up blocks whose partial sums LDS holds at once
     int deferred;                  // 1: every block has its own slot and is finalised after the segment
@@ -752,7 +752,8 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         if (q > 0) dn_prep(q);        // chunk 0's tables were built during the setup
         const int q0 = q * qc, nq = min(A, q0 + qc) - q0;
         if (q == 0) gate.wait(2);     // every workgroup's h is out
-        stage_h<BITS>(f.h, A * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl);
+        // h rows are assignment indices t * slots + slot (< T * slots; A is fewer under top-p)
+        stage_h<BITS>(f.h, T * slots * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl);
         __syncthreads();
         chunk_first = mw_upper_index(seg, n_act, q0);
         cj = -1;                      // the computing cursor reloads its expert's column map
@@ -885,7 +886,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     }
 }
 
-template <int BITS>
+template <int BITS, bool kTopP>
 __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     constexpr int NM = I8Codec<BITS>::NM;
     extern __shared__ __align__(16) unsigned char dyn[];
@@ -910,7 +911,8 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
-    route_select_block<kCols, kFusedExperts, kMW, true>(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S, f.rsf, r);
+    route_select_block<kCols, kFusedExperts, kMW, true, kTopP>(f.scores, f.bias, T, E, f.n_group, f.topk_group, K, S,
+                                                             f.rsf, f.top_p, r);
 
     // ---- phase 3: the stream
     stream<BITS>(f, r, dyn, xu, gate);
@@ -929,7 +931,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
             if (j < n) f.wl_expert_id[j] = r.eid[j];
             f.wl_seg[j] = r.seg[j];
         }
-        for (int i = threadIdx.x; i < T * a.slots; i += kMT) f.wl_assign[i] = r.assign[i];
+        for (int i = threadIdx.x; i < r.n_assign; i += kMT) f.wl_assign[i] = r.assign[i];
     }
 }
 
@@ -940,7 +942,7 @@ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 // starts][chunk tables]; the chunk size qc is the largest that fits.
 template <int BITS>
 hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st) {
-    auto k = layer_fused_kernel<BITS>;
+    auto k = f.top_p < 1.f ? layer_fused_kernel<BITS, true> : layer_fused_kernel<BITS, false>;
     static size_t static_lds = 0;        // the kernel's static LDS, read once
     if (static_lds == 0) {
         hipFuncAttributes attr;
@@ -1027,6 +1029,7 @@ hipError_t launch_layer_fused(int bits, const FusedLayerArgs& l, hipStream_t st)
     f.topk_group = l.topk_group;
     f.n_shared = l.n_shared;
     f.rsf = l.rsf;
+    f.top_p = l.top_p;
     switch (bits) {
         case 4: return layer_fused_bits<4>(f, l, st);
         case 8: return layer_fused_bits<8>(f, l, st);

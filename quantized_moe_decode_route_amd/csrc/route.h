@@ -29,6 +29,7 @@ struct RouteLdsT {
     int seg[EM + 9];                       //           offsets into assign
     int assign[TM * 40];                   //           assignments by expert
     int n_active;
+    int n_assign;                          // assignments (dropped top-p slots have none)
 };
 
 // (v, i) beats (u, j) if v > u, or v == u and i < j: a strict total order.
@@ -55,6 +56,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 //      round k's winner is slot k, and the total of the chosen s is summed
 //      in slot order as the rounds go;
 //   5. lane k < top_k: weight k = s_k / total * rsf.
+// With top_p < 1 (adaptive expert top-p; Show HN page, run options), step 5
+// becomes: rank the slots by s (descending, NaN last, ties to the lower
+// index), add s in that order until the sum reaches top_p * total, keep that
+// prefix (at least one slot), move the kept slots to the front in their slot
+// order, weight them s_k / (their slot-order sum) * rsf, and mark the rest
+// index -1, weight 0 -- such slots get no assignment.
 // The worklist is then a rank sort of the assignments by (expert, assignment)
 // (one wave when they fit its lanes, else the whole workgroup).
 // A NaN corrected score or group score ranks below every number (as -inf,
@@ -62,10 +69,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // inputs hold.
 // kCoherentScores: read the scores with device-coherent loads (scores that
 // other workgroups of the same launch have just written), else plain loads.
-template <int TM, int EM, int NW, bool kCoherentScores = false>
+// kTopP: compile the top-p step in (top_p is read only then; without it the
+// selection is plain top-k and the code stays as small as before).
+template <int TM, int EM, int NW, bool kCoherentScores = false, bool kTopP = false>
 __device__ __forceinline__ void route_select_block(const float* scores, const float* __restrict__ bias, int T,
                                                    int E, int n_group, int topk_group, int top_k, int n_shared,
-                                                   float rsf, RouteLdsT<TM, EM, NW>& r) {
+                                                   float rsf, float top_p, RouteLdsT<TM, EM, NW>& r) {
     constexpr int NV = EM / kWave;                    // experts per lane
     static_assert(NV <= 32, "the candidate mask is 32 bits");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -135,6 +144,7 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
         // round k: each lane's best (largest key, lowest j on ties), the
         // wave's largest key, then the lowest expert index holding it
         float total = 0.f, my_s = 0.f;
+        int my_e = 0;
         for (int k = 0; k < top_k; ++k) {
             unsigned bk = key[NV - 1];
             int bj = NV - 1;
@@ -153,10 +163,51 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
 #pragma unroll
             for (int j = 0; j < NV; ++j) key[j] = (lane == owner && j == jw) ? 0u : key[j];
             if (lane == 0) r.sel[t * top_k + k] = win;
-            if (lane == k) my_s = sw;
+            if (lane == k) {
+                my_s = sw;
+                my_e = win;
+            }
             total += sw;                               // slot order
         }
-        if (lane < top_k) r.selw[t * top_k + lane] = (my_s / total) * rsf;
+        if (!kTopP || !(top_p < 1.f)) {
+            if (lane < top_k) r.selw[t * top_k + lane] = (my_s / total) * rsf;
+            continue;
+        }
+        // adaptive top-p: rank of slot `lane` by (s descending, NaN last, index)
+        const unsigned us = __float_as_uint(my_s + 0.0f);
+        const unsigned ks = my_s == my_s ? ((us & 0x80000000u) ? ~us : (us | 0x80000000u)) : 0u;
+        int wr = 0;
+        for (int j = 0; j < top_k; ++j) {
+            const unsigned kj = __builtin_amdgcn_readlane(ks, j);
+            const int ej = __builtin_amdgcn_readlane(my_e, j);
+            wr += (kj > ks) || (kj == ks && ej < my_e);
+        }
+        const float thr = top_p * total;
+        float cum = 0.f;
+        int m = top_k;
+        for (int i = 0; i < top_k; ++i) {              // the ranks are a permutation of 0 .. top_k-1
+            const int ln = (int)__builtin_ctzll(__ballot(lane < top_k && wr == i));
+            cum += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), ln));
+            if (cum >= thr) {
+                m = i + 1;
+                break;
+            }
+        }
+        const bool keep = lane < top_k && wr < m;
+        const unsigned long long kb = __ballot(keep);
+        float kept_total = 0.f;
+        for (int j = 0; j < top_k; ++j)                // slot order
+            if ((kb >> j) & 1ull) kept_total += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), j));
+        // rewrite the token's slots (LDS writes of one wave land in order)
+        const int ns = __popcll(kb & ((1ull << lane) - 1ull));
+        if (keep) {
+            r.sel[t * top_k + ns] = my_e;
+            r.selw[t * top_k + ns] = (my_s / kept_total) * rsf;
+        }
+        if (lane >= m && lane < top_k) {
+            r.sel[t * top_k + lane] = -1;
+            r.selw[t * top_k + lane] = 0.f;
+        }
     }
     __syncthreads();
 
@@ -165,23 +216,25 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
     const int A = T * slots;
     if (A <= kWave) {                  // one wave, no workgroup barriers
         if (wave == 0) {
-            int k = INT_MAX;
+            int k = INT_MAX;                   // a dropped slot keeps INT_MAX: sorted last, not written
             if (lane < A) {
                 const int tt = lane / slots, s = lane - tt * slots;
                 const int e = s < top_k ? r.sel[tt * top_k + s] : E + (s - top_k);
-                k = (e << 16) | lane;
+                k = e >= 0 ? (e << 16) | lane : INT_MAX;
                 r.key[lane] = k;
             }
             wave_lds_sync();
             int rank = 0;
             for (int b = 0; b < A; ++b) rank += r.key[b] < k;
-            if (lane < A) {
+            const bool valid = lane < A && (!kTopP || k != INT_MAX);
+            const int Av = kTopP ? __popcll(__ballot(valid)) : A;
+            if (valid) {
                 r.assign[rank] = lane;
                 r.sexp[rank] = k >> 16;
             }
             wave_lds_sync();
-            const int ex = lane < A ? r.sexp[lane] : -1;
-            const bool first = lane < A && (lane == 0 || r.sexp[max(lane - 1, 0)] != ex);
+            const int ex = lane < Av ? r.sexp[lane] : -1;
+            const bool first = lane < Av && (lane == 0 || r.sexp[max(lane - 1, 0)] != ex);
             const unsigned long long fm = __ballot(first);
             const int sidx = __popcll(fm & ((1ull << lane) - 1ull));
             if (first) {
@@ -191,7 +244,8 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
             if (lane == 0) {
                 const int n = __popcll(fm);
                 r.n_active = n;
-                r.seg[n] = A;
+                r.n_assign = Av;
+                r.seg[n] = Av;
             }
         }
         __syncthreads();
@@ -200,23 +254,31 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
     for (int a = threadIdx.x; a < A; a += blockDim.x) {
         const int t = a / slots, s = a - t * slots;
         const int e = s < top_k ? r.sel[t * top_k + s] : E + (s - top_k);
-        r.key[a] = (e << 16) | a;
+        r.key[a] = (!kTopP || e >= 0) ? (e << 16) | a : INT_MAX;   // dropped top-p slot: sorted last, not written
     }
     __syncthreads();
     for (int a = threadIdx.x; a < A; a += blockDim.x) {
         const int k = r.key[a];
+        if (kTopP && k == INT_MAX) continue;
         int rank = 0;
 #pragma unroll 8
         for (int b = 0; b < A; ++b) rank += r.key[b] < k;
         r.assign[rank] = a;
         r.sexp[rank] = k >> 16;
     }
+    if (threadIdx.x == 0) {
+        int n = A;
+        if (kTopP)
+            for (int a = 0; a < A; ++a) n -= r.key[a] == INT_MAX;
+        r.n_assign = n;
+    }
     __syncthreads();
+    const int Av = r.n_assign;
     int* first = r.key;                  // the keys are no longer needed
-    for (int p = threadIdx.x; p < A; p += blockDim.x)
+    for (int p = threadIdx.x; p < Av; p += blockDim.x)
         first[p] = (p == 0 || r.sexp[p - 1] != r.sexp[p]) ? 1 : 0;
     __syncthreads();
-    for (int p = threadIdx.x; p < A; p += blockDim.x) {
+    for (int p = threadIdx.x; p < Av; p += blockDim.x) {
         if (first[p]) {
             int sidx = 0;
 #pragma unroll 8
@@ -228,9 +290,9 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
     if (threadIdx.x == 0) {
         int n = 0;
 #pragma unroll 8
-        for (int p = 0; p < A; ++p) n += first[p];
+        for (int p = 0; p < Av; ++p) n += first[p];
         r.n_active = n;
-        r.seg[n] = A;
+        r.seg[n] = Av;
     }
     __syncthreads();
 }

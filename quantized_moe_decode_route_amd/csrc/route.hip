@@ -58,13 +58,15 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* 
     }
 }
 
+template <bool kTopP>
 __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, int T, int E, int n_group, int topk_group,
-    int top_k, int n_shared, float rsf, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int top_k, int n_shared, float rsf, float top_p, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ wl_n_active, int32_t* __restrict__ wl_expert_id, int32_t* __restrict__ wl_seg,
     int32_t* __restrict__ wl_assign) {
     __shared__ RouteLdsT<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS, kSelThreads / kWave> r;
-    route_select_block(scores, bias, T, E, n_group, topk_group, top_k, n_shared, rsf, r);
+    route_select_block<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS, kSelThreads / kWave, false, kTopP>(
+        scores, bias, T, E, n_group, topk_group, top_k, n_shared, rsf, top_p, r);
     // outputs
     for (int i = threadIdx.x; i < T * top_k; i += blockDim.x) {
         topk_idx[i] = r.sel[i];
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     }
     if (wl_n_active == nullptr) return;
     const int n = r.n_active;
-    const int A = T * (top_k + n_shared);
+    const int A = r.n_assign;                          // = seg[n]
     if (threadIdx.x == 0) *wl_n_active = n;
     for (int j = threadIdx.x; j <= n; j += blockDim.x) {
         if (j < n) wl_expert_id[j] = r.eid[j];
@@ -84,13 +86,15 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
 }  // namespace
 
 hipError_t launch_route(const float* x, const float* router_w, const float* bias, int T, int H, int E,
-                        int n_group, int topk_group, int top_k, int n_shared, float rsf, float* scores,
-                        int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, hipStream_t st) {
+                        int n_group, int topk_group, int top_k, int n_shared, float rsf, float top_p,
+                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                        hipStream_t st) {
     hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_select_kernel, dim3(1), dim3(kSelThreads), 0, st, scores, bias, T, E, n_group,
-                       topk_group, top_k, n_shared, rsf, topk_idx, topk_w, wl ? wl->n_active : nullptr,
+    auto k = top_p < 1.f ? route_select_kernel<true> : route_select_kernel<false>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(kSelThreads), 0, st, scores, bias, T, E, n_group,
+                       topk_group, top_k, n_shared, rsf, top_p, topk_idx, topk_w, wl ? wl->n_active : nullptr,
                        wl ? wl->expert_id : nullptr, wl ? wl->seg : nullptr, wl ? wl->assign : nullptr);
     return hipGetLastError();
 }

@@ -51,6 +51,7 @@ _SIGS = {
     "moedec_status_string": ([_I], ctypes.c_char_p),
     "moedec_abi_version": ([], _I),
     "moe_route_topk": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P], _I),
+    "moe_route_topp": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P], _I),
     "moe_residual_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
 }
 for _b in ("q4", "q8", "q2"):
@@ -61,6 +62,8 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_quantize_rows_{_b}"] = ([_P, _P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_quantize_pack_rows_{_b}"] = ([_P, _P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
+    _SIGS[f"moe_layer_fused_topp_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P],
+                                           _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
 
@@ -190,8 +193,9 @@ class Route:
 # ------------------------------------------------------------------- calls
 
 def route_topk(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, *, n_group: int, topk_group: int,
-               top_k: int, n_shared: int, rsf: float, out: Route | None = None) -> Route:
-    """moe_route_topk: sigmoid scores, group-limited top-k, weights, worklist."""
+               top_k: int, n_shared: int, rsf: float, out: Route | None = None, top_p: float | None = None) -> Route:
+    """moe_route_topk: sigmoid scores, group-limited top-k, weights, worklist
+    (moe_route_topp when top_p is given: adaptive expert top-p after top-k)."""
     T, H = x.shape
     E = router_w.shape[0]
     if router_w.shape != (E, H) or bias.shape != (E,):
@@ -203,12 +207,14 @@ def route_topk(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, *, n
                     torch.empty((T, top_k), dtype=torch.float32, device=dev),
                     Worklist.empty(T, top_k, E, n_shared, dev))
     wl = out.worklist.struct()
-    st = lib().moe_route_topk(_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"),
-                              _dev(bias, torch.float32, "bias"), T, H, E, n_group, topk_group, top_k, n_shared,
-                              float(rsf), _dev(out.scores, torch.float32, "scores"),
-                              _dev(out.topk_idx, torch.int32, "topk_idx"), _dev(out.topk_w, torch.float32, "topk_w"),
-                              ctypes.byref(wl), _stream(x))
-    _check("moe_route_topk", st)
+    head = (_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"), _dev(bias, torch.float32, "bias"),
+            T, H, E, n_group, topk_group, top_k, n_shared, float(rsf))
+    tail = (_dev(out.scores, torch.float32, "scores"), _dev(out.topk_idx, torch.int32, "topk_idx"),
+            _dev(out.topk_w, torch.float32, "topk_w"), ctypes.byref(wl), _stream(x))
+    if top_p is None:
+        _check("moe_route_topk", lib().moe_route_topk(*head, *tail))
+    else:
+        _check("moe_route_topp", lib().moe_route_topp(*head, float(top_p), *tail))
     return out
 
 
@@ -337,8 +343,9 @@ def fused_supported(T: int, ex: Experts) -> bool:
 
 
 def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
-                topk_group: int, top_k: int, rsf: float, buf: LayerBuffers) -> LayerBuffers:
-    """moe_layer_fused_q{bits}: the whole layer in one launch (outputs in buf)."""
+                topk_group: int, top_k: int, rsf: float, buf: LayerBuffers, top_p: float | None = None) -> LayerBuffers:
+    """moe_layer_fused_q{bits} (moe_layer_fused_topp_q{bits} when top_p is
+    given): the whole layer in one launch (outputs in buf)."""
     T, H = x.shape
     E = ex.n_experts
     if router_w.shape != (E, H) or bias.shape != (E,) or H != ex.hidden:
@@ -348,19 +355,21 @@ def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex:
             buf.h.shape != (T * (top_k + ex.n_shared), ex.inter) or buf.workspace.numel() < FUSED_WORKSPACE_INTS:
         raise ValueError("buffers do not match the call's shapes")
     s_ex, s_wl = ex.struct(), r.worklist.struct()
-    fn = getattr(lib(), f"moe_layer_fused_{_suffix(ex.bits)}")
+    name = f"moe_layer_fused_{_suffix(ex.bits)}" if top_p is None else f"moe_layer_fused_topp_{_suffix(ex.bits)}"
+    fn = getattr(lib(), name)
+    pre = (float(rsf),) if top_p is None else (float(rsf), float(top_p))
     st = fn(_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"), _dev(bias, torch.float32, "bias"),
-            ctypes.byref(s_ex), T, n_group, topk_group, top_k, float(rsf),
+            ctypes.byref(s_ex), T, n_group, topk_group, top_k, *pre,
             _dev(r.scores, torch.float32, "scores"), _dev(r.topk_idx, torch.int32, "topk_idx"),
             _dev(r.topk_w, torch.float32, "topk_w"), ctypes.byref(s_wl), _dev(buf.h, torch.float32, "h"),
             _dev(buf.y, torch.float32, "y"), _dev(buf.workspace, torch.int32, "workspace"), _stream(x))
-    _check(fn.__name__, st)
+    _check(name, st)
     return buf
 
 
 def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
               topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None,
-              fused: bool | None = None) -> LayerBuffers:
+              fused: bool | None = None, top_p: float | None = None) -> LayerBuffers:
     """One layer on x's stream; returns the buffers (y in .y).  fused=None takes
     the single-launch path where its limits allow, else route_topk ->
     gate_up_silu -> down_combine; True / False force one of them."""
@@ -371,15 +380,15 @@ def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: E
         if fused_supported(T, ex):
             try:
                 return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k,
-                                   rsf=rsf, buf=buf)
+                                   rsf=rsf, buf=buf, top_p=top_p)
             except MoedecError as err:
                 if err.status != MOEDEC_ERR_UNSUPPORTED:   # the shape does not fit the fused plan
                     raise
     elif fused:
         return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
-                           buf=buf)
+                           buf=buf, top_p=top_p)
     route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
-               rsf=rsf, out=buf.route)
+               rsf=rsf, out=buf.route, top_p=top_p)
     gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)
     down_combine(buf.h, ex, buf.route.worklist, buf.route.topk_w, top_k, out=buf.y)
     return buf

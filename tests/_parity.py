@@ -11,6 +11,8 @@ the GPU side.  Tolerances:
     below those margins fp32 rounding may legitimately flip a near-tie, and
     the GPU's choice is then only checked to be valid: its own fp32 scores,
     which lie within 2e-6 of the oracle's, select exactly that set;
+  * with adaptive top-p, a token's set also needs the oracle's top-p margin
+    (prefix sums and score gaps away from the cut by 1e-5 of the total);
   * worklist (batch union): bit-exact when every token's order is
     certified; otherwise checked to be the batch union of the GPU's ids;
   * h rows and y rows: max|gpu - oracle| / max|oracle| <= 1e-3 per row
@@ -43,15 +45,16 @@ def experts_dev(cfg, lay) -> ops.Experts:
     return ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits)
 
 
-def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None) -> dict:
+def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None, top_p: float | None = None) -> dict:
     """One layer on the GPU (fused: the single-launch call; False: route +
-    gate/up + down; None: whichever moe_layer picks); results on the host."""
+    gate/up + down; None: whichever moe_layer picks; top_p: the adaptive
+    top-p calls); results on the host."""
     dev = lay["router_w"].device
     xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
     ex = experts_dev(cfg, lay)
     try:
         buf = ops.moe_layer(xt, lay["router_w"], lay["bias"], ex, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                            top_k=cfg.top_k, rsf=cfg.rsf, fused=fused)
+                            top_k=cfg.top_k, rsf=cfg.rsf, fused=fused, top_p=top_p)
     except ops.MoedecError as err:
         if fused and err.status == ops.MOEDEC_ERR_UNSUPPORTED:
             pytest.skip("the activations of this batch do not fit the fused call's LDS plan")
@@ -60,10 +63,11 @@ def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None) -> dict:
     assert not buf.fused_error(), "a grid barrier of the fused launch timed out"
     wl = buf.route.worklist
     n = int(wl.n_active.item())
+    seg = wl.seg[:n + 1].cpu().numpy()
     return dict(scores=buf.route.scores.cpu().numpy(), idx=buf.route.topk_idx.cpu().numpy(),
                 w=buf.route.topk_w.cpu().numpy(), n_active=n, expert_id=wl.expert_id[:n].cpu().numpy(),
-                seg=wl.seg[:n + 1].cpu().numpy(), assign=wl.assign.cpu().numpy(), h=buf.h.cpu().numpy(),
-                y=buf.y.cpu().numpy())
+                seg=seg, assign=wl.assign[:int(seg[-1])].cpu().numpy(), h=buf.h.cpu().numpy(),
+                y=buf.y.cpu().numpy(), top_p=top_p)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
@@ -74,16 +78,18 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float((np.abs(got - ref).max(axis=-1) / den).max())
 
 
-def oracle_layer(cfg, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray, expert_fn) -> orc.LayerResult:
+def oracle_layer(cfg, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray, expert_fn,
+                 top_p: float | None = None) -> orc.LayerResult:
     return orc.moe_layer(x, router_w, bias, expert_fn, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                         top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits)
+                         top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits,
+                         top_p=1.0 if top_p is None else top_p)
 
 
 def check_routing(cfg, g: dict, r: orc.LayerResult, bias: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Returns (set_certified, order_certified) per token after checking."""
     err = np.abs(g["scores"].astype(np.float64) - r.scores64).max()
     assert err <= SCORE_ATOL, f"scores off by {err}"
-    set_ok = r.margin >= MARGIN
+    set_ok = (r.margin >= MARGIN) & (r.topp >= MARGIN)       # top-p: the kept prefix is certified too
     order_ok = set_ok & (r.order >= MARGIN)
     for t in range(len(set_ok)):
         if set_ok[t]:
@@ -93,8 +99,8 @@ def check_routing(cfg, g: dict, r: orc.LayerResult, bias: np.ndarray) -> tuple[n
             np.testing.assert_allclose(g["w"][t], r.w[t], rtol=W_RTOL)
         if not order_ok[t]:
             # near-tie: the GPU's choice must be what its own (checked) scores select
-            i_v, w_v = orc.select_experts(g["scores"][t:t + 1], bias, cfg.n_group, cfg.topk_group, cfg.top_k,
-                                          cfg.rsf)
+            i_v, w_v, _ = orc.select_experts_topp(g["scores"][t:t + 1], bias, cfg.n_group, cfg.topk_group,
+                                                  cfg.top_k, cfg.rsf, 1.0 if g["top_p"] is None else g["top_p"])
             np.testing.assert_array_equal(g["idx"][t], i_v[0])
             np.testing.assert_array_equal(g["w"][t], w_v[0])
     if order_ok.all():
@@ -114,7 +120,9 @@ def check_layer(cfg, g: dict, r: orc.LayerResult, set_ok: np.ndarray, order_ok: 
     """h rows of order-certified tokens and y rows of set-certified tokens."""
     assert set_ok.any(), "no token has a certified selection"
     slots = cfg.top_k + cfg.n_shared
-    rows = [t * slots + s for t in range(len(order_ok)) if order_ok[t] for s in range(slots)]
+    # rows of the slots that hold an expert (top-p leaves dropped slots unwritten)
+    rows = [t * slots + s for t in range(len(order_ok)) if order_ok[t] for s in range(slots)
+            if s >= cfg.top_k or r.idx[t, s] >= 0]
     eh = rel_err(g["h"][rows], r.h[rows]) if rows else 0.0
     ey = rel_err(g["y"][set_ok], r.y[set_ok])
     say(f"  outputs: h err {eh:.2e} ({len(rows)} rows), y err {ey:.2e} ({int(set_ok.sum())} tokens)")
@@ -123,7 +131,7 @@ def check_layer(cfg, g: dict, r: orc.LayerResult, set_ok: np.ndarray, order_ok: 
 
 
 def check_all(cfg, g: dict, x, router_w, bias, expert_fn) -> orc.LayerResult:
-    r = oracle_layer(cfg, x, router_w, bias, expert_fn)
+    r = oracle_layer(cfg, x, router_w, bias, expert_fn, g.get("top_p"))
     set_ok, order_ok = check_routing(cfg, g, r, bias)
     check_layer(cfg, g, r, set_ok, order_ok)
     return r

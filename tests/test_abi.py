@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 25
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
 
@@ -159,6 +159,12 @@ def test_quantize_validation(lib, bits, pack):
     if not pack or bits != 2:
         assert fn(FAKE, FAKE + 1, FAKE, 2, 8, None) == 1          # codes / packed words misaligned
     assert fn(None, None, None, 0, 8, None) == 0                  # no rows: nothing to do
+
+
+def test_topp_rejects_nan(lib):
+    import math
+    args = (FAKE, FAKE, FAKE, 1, 256, 16, 4, 2, 4, 1, 2.5, math.nan, FAKE, FAKE, FAKE, None, None)
+    assert lib.moe_route_topp(*args) == 1
 
 
 def test_rmsnorm_validation(lib):
