@@ -226,6 +226,137 @@ def bench_quantize(args) -> None:
     print(json.dumps(out), flush=True)
 
 
+def bench_stack(args, cfg) -> None:
+    """A stack of cfg.layers resident layers (x <- x + MoE(rmsnorm(x)) per
+    layer, the pre-norm residual form) on cfg.tokens tokens; a step is the
+    whole stack, captured as one HIP graph per token batch and replayed.
+    Bytes per step = the per-layer step bytes summed over the layers."""
+    import torch
+
+    from quantized_moe_decode_route_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, H, L = cfg.tokens, cfg.hidden, cfg.layers
+    kw = dict(n_group=cfg.n_group, topk_group=cfg.topk_group, top_k=cfg.top_k, rsf=cfg.rsf)
+    layers, experts = [], []
+    for l in range(L):
+        layers.append(synth.layer_device(cfg, l, dev))
+        experts.append(ops.Experts.from_layer(layers[-1], cfg.n_experts, cfg.n_shared, cfg.bits))
+        print(f"[bench] layer {l} resident", file=sys.stderr, flush=True)
+    bufs = [ops.LayerBuffers.allocate(T, H, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared, dev) for _ in range(L)]
+    n_batch = cfg.pool // T
+    pool = torch.from_numpy(synth.token_pool(cfg)).to(dev)
+    x = torch.empty((T, H), dtype=torch.float32, device=dev)
+    xn = torch.empty_like(x)
+    fused = ops.fused_supported(T, experts[0])
+    if fused:
+        try:
+            ops.residual_rmsnorm(x.copy_(pool[:T]), None, xn)
+            ops.layer_fused(xn, layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0],
+                            top_p=args.top_p, **kw)
+        except ops.MoedecError as err:
+            if err.status != ops.MOEDEC_ERR_UNSUPPORTED:
+                raise
+            fused = False            # this batch does not fit the fused call's LDS plan
+
+    def step(b):
+        x.copy_(pool[b * T:(b + 1) * T])
+        ops.residual_rmsnorm(x, None, xn)
+        for l in range(L):
+            ops.moe_layer(xn, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], fused=fused,
+                          top_p=args.top_p, **kw)
+            ops.residual_rmsnorm(x, bufs[l].y, xn)
+
+    # unique experts per layer for each token batch (routing depends on the batch only)
+    sbytes = np.zeros(n_batch)
+    active = np.zeros((n_batch, L), np.int64)
+    for b in range(n_batch):
+        step(b)
+        torch.cuda.synchronize()
+        for l in range(L):
+            active[b, l] = int(bufs[l].route.worklist.n_active.item())
+        sbytes[b] = sum(step_bytes(cfg, int(n)) for n in active[b])
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        step(0)
+    stream.synchronize()
+    for b in range(n_batch):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(b)
+        graphs.append(g)
+    steps, warm = max(args.steps // 100, 8), max(args.warmup // 100, 2)
+    for i in range(warm):
+        graphs[i % n_batch].replay()
+    torch.cuda.synchronize()
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev_a.record()
+    for i in range(steps):
+        graphs[(warm + i) % n_batch].replay()
+    ev_b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region = ev_a.elapsed_time(ev_b) * 1e-3
+    idx = (np.arange(warm, warm + steps) % n_batch)
+    total = float(sbytes[idx].sum())
+    gbs = total / wall / 1e9
+    print(f"[bench] {steps} stack steps in {wall * 1e3:.1f} ms (events {region * 1e3:.1f} ms): "
+          f"{wall / steps * 1e3:.3f} ms/step, {gbs:.0f} GB/s, {steps * T / wall:.0f} tok/s through {L} layers; "
+          f"unique experts per layer {active.mean():.1f}", file=sys.stderr, flush=True)
+
+    # the dominant kernel (gate/up of the split path, or the fused launch), timed
+    # eagerly with HIP events per launch, each after a read of a 1 GiB buffer
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+    kb = []
+    for k in range(2 * L):
+        l, b = k % L, (k // L) % n_batch
+        x.copy_(pool[b * T:(b + 1) * T])
+        ops.residual_rmsnorm(x, None, xn)
+        sink += flush.sum()
+        if fused:
+            ev0[k].record()
+            ops.layer_fused(xn, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l],
+                            top_p=args.top_p, **kw)
+            ev1[k].record()
+            kb.append(fused_bytes(cfg, int(active[b, l])))
+        else:
+            ops.route_topk(xn, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route,
+                           top_p=args.top_p, **kw)
+            ev0[k].record()
+            ops.gate_up_silu(xn, experts[l], bufs[l].route.worklist, cfg.top_k, out=bufs[l].h)
+            ev1[k].record()
+            kb.append(gate_up_bytes(cfg, int(bufs[l].route.worklist.n_active.item())))
+    torch.cuda.synchronize()
+    dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3
+    achieved = float(np.mean(kb) / dur.mean() / 1e9)
+    kname = f"layer_fused_kernel<{cfg.bits}, ...>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
+    print(f"[bench] {kname} avg {dur.mean() * 1e6:.1f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
+    out = {
+        "metric": METRIC + " (16-layer stack)", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "tokens_per_s": round(steps * T / wall, 1),
+        "bytes_per_step": int(sbytes[idx].mean()),
+        "config": {"workload": cfg.name, "path": "fused" if fused else "split", "tokens": T, "layers": L,
+                   "hidden": H, "inter": cfg.inter, "routed_experts": cfg.n_experts, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "top_k": cfg.top_k, "shared_experts": cfg.n_shared,
+                   "bits": cfg.bits, "zipf_bias": cfg.zipf_s, "graph": "one per step over every layer",
+                   "unique_experts_per_layer": float(active[idx].mean()), "top_p": args.top_p},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(float(dur.mean() * 1e6), 2), "bytes_per_launch": int(np.mean(kb))},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +364,7 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="glm_t1")
     ap.add_argument("--layers", type=int, default=4, help="resident layers the steps rotate over")
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's batch (stack workloads)")
     ap.add_argument("--graph-steps", type=int, default=8)
     ap.add_argument("--kernel-steps", type=int, default=100, help="eager gate/up launches timed (split path)")
     ap.add_argument("--split", action="store_true", help="time the three separate calls instead of the fused one")
@@ -269,8 +401,13 @@ def main() -> None:
         return
 
     cfg = synth.CONFIGS[args.workload]
+    if args.tokens is not None:
+        if cfg.layers == 1:
+            raise SystemExit("--tokens applies to the stack workloads only")
+        cfg = synth.scaled(cfg, tokens=args.tokens, name=f"{cfg.name}_t{args.tokens}")
     if cfg.layers != 1:
-        raise SystemExit("bench.py times single-layer workloads; the 16-layer stack is a parity case")
+        bench_stack(args, cfg)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L, T, G = args.layers, cfg.tokens, args.graph_steps

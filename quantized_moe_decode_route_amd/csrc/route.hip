@@ -9,7 +9,8 @@
 //
 // Kernel 1 (router_gemv): one workgroup per expert row; every thread issues all
 // of its 16-byte loads of the row before using them, then the row is dotted
-// with each token and s = sigmoid(W_r[e] . x_t) is written.
+// with the tokens, four at a time with their loads issued together, and
+// s = sigmoid(W_r[e] . x_t) is written.
 // Kernel 2 (route_select): one workgroup running route_select_block (see
 // route.h): each wave routes its tokens with wave-wide arg-max rounds, then
 // the expert-ascending worklist comes from a rank sort in LDS.
@@ -20,9 +21,13 @@ namespace moedec {
 namespace {
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvMaxF4 = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 per thread
-constexpr int kSelThreads = 256;
+constexpr int kGemvMaxF4 = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 per thread at most
+constexpr int kGemvTB = 4;                                        // tokens whose x loads go out together
+constexpr int kSelThreads = 512;                                   // 8 waves (1024 would spill)
 
+// NF float4 of the row per thread; tokens in batches of kGemvTB whose x loads
+// all go out before any is used (the row's loads went out first of all).
+template <int NF>
 __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* __restrict__ x,
                                                                    const float* __restrict__ W, int T, int H,
                                                                    int E, float* __restrict__ scores) {
@@ -31,25 +36,29 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const float4* w4 = reinterpret_cast<const float4*>(W + (size_t)e * H);
     const int n4 = H >> 2;
-    float4 wr[kGemvMaxF4];
+    float4 wr[NF];
 #pragma unroll
-    for (int k = 0; k < kGemvMaxF4; ++k) {
-        const int i = threadIdx.x + k * kGemvThreads;
-        wr[k] = i < n4 ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    for (int t = 0; t < T; ++t) {
-        const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * H);
-        float acc = 0.f;
+    for (int k = 0; k < NF; ++k) wr[k] = w4[min((int)threadIdx.x + k * kGemvThreads, n4 - 1)];
 #pragma unroll
-        for (int k = 0; k < kGemvMaxF4; ++k) {
-            const int i = threadIdx.x + k * kGemvThreads;
-            if (i < n4) {
-                const float4 v = x4[i];
-                acc += (wr[k].x * v.x + wr[k].y * v.y) + (wr[k].z * v.z + wr[k].w * v.w);
-            }
+    for (int k = 0; k < NF; ++k)          // columns past the row's end count as zero
+        if ((int)threadIdx.x + k * kGemvThreads >= n4) wr[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t0 = 0; t0 < T; t0 += kGemvTB) {
+        float4 xv[kGemvTB][NF];
+#pragma unroll
+        for (int b = 0; b < kGemvTB; ++b) {
+            const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)min(t0 + b, T - 1) * H);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) xv[b][k] = x4[min((int)threadIdx.x + k * kGemvThreads, n4 - 1)];
         }
-        acc = group_sum<kWave>(acc);
-        if (lane == 0) red[t][wave] = acc;
+#pragma unroll
+        for (int b = 0; b < kGemvTB; ++b) {
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < NF; ++k)
+                acc += (wr[k].x * xv[b][k].x + wr[k].y * xv[b][k].y) + (wr[k].z * xv[b][k].z + wr[k].w * xv[b][k].w);
+            acc = group_sum<kWave>(acc);
+            if (lane == 0 && t0 + b < T) red[t0 + b][wave] = acc;
+        }
     }
     __syncthreads();
     for (int t = threadIdx.x; t < T; t += kGemvThreads) {
@@ -89,7 +98,18 @@ hipError_t launch_route(const float* x, const float* router_w, const float* bias
                         int n_group, int topk_group, int top_k, int n_shared, float rsf, float top_p,
                         float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                         hipStream_t st) {
-    hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    const int per = (H / 4 + kGemvThreads - 1) / kGemvThreads;
+    if (per <= 2)
+        hipLaunchKernelGGL(router_gemv_kernel<2>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    else if (per <= 4)
+        hipLaunchKernelGGL(router_gemv_kernel<4>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    else if (per <= 6)
+        hipLaunchKernelGGL(router_gemv_kernel<6>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    else if (per <= 8)
+        hipLaunchKernelGGL(router_gemv_kernel<8>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
+    else
+        hipLaunchKernelGGL(router_gemv_kernel<kGemvMaxF4>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E,
+                           scores);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     auto k = top_p < 1.f ? route_select_kernel<true> : route_select_kernel<false>;

@@ -148,6 +148,25 @@ def test_unpack_every_byte(bits):
     np.testing.assert_array_equal(got, orc.unpack_rows(b, bits))
 
 
+@pytest.mark.parametrize("T,H,offset", [(1, 4, 0), (3, 2048, 0), (16, 6144, 0), (2, 16384, 0), (4, 1000, 0),
+                                         (2, 6143, 0), (3, 512, 1)])
+def test_residual_rmsnorm_shapes(T, H, offset):
+    """Every launch shape of the norm: float4 rows of 1-16 float4 per thread,
+    odd row lengths and misaligned rows (the scalar kernel)."""
+    rng = np.random.default_rng(H + T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    y = (rng.standard_normal((T, H)) * 3).astype(np.float32)
+    bx = torch.zeros(T * H + offset, device=DEV)
+    by = torch.zeros(T * H + offset, device=DEV)
+    xt, yt = bx[offset:].view(T, H), by[offset:].view(T, H)
+    xt.copy_(torch.from_numpy(x))
+    yt.copy_(torch.from_numpy(y))
+    xn = torch.empty((T, H), device=DEV)
+    ops.residual_rmsnorm(xt, yt, xn)
+    np.testing.assert_array_equal(xt.cpu().numpy(), x + y)
+    assert np.abs(xn.cpu().numpy() - orc.rmsnorm(x.astype(np.float64) + y)).max() <= 1e-5
+
+
 def test_residual_rmsnorm():
     rng = np.random.default_rng(0)
     x = rng.standard_normal((5, 6144)).astype(np.float32)
