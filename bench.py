@@ -249,24 +249,14 @@ def bench_stack(args, cfg) -> None:
     pool = torch.from_numpy(synth.token_pool(cfg)).to(dev)
     x = torch.empty((T, H), dtype=torch.float32, device=dev)
     xn = torch.empty_like(x)
-    fused = ops.fused_supported(T, experts[0])
-    if fused:
-        try:
-            ops.residual_rmsnorm(x.copy_(pool[:T]), None, xn)
-            ops.layer_fused(xn, layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0],
-                            top_p=args.top_p, **kw)
-        except ops.MoedecError as err:
-            if err.status != ops.MOEDEC_ERR_UNSUPPORTED:
-                raise
-            fused = False            # this batch does not fit the fused call's LDS plan
+    stack = [(lay["router_w"], lay["bias"], ex) for lay, ex in zip(layers, experts)]
+    # fused: one residual-form launch per layer (norm and residual inside);
+    # else the separate calls with the norm kernel between layers
+    fused = ops.stack_forward(x.copy_(pool[:T]), stack, bufs, top_p=args.top_p, xn=xn, **kw)
 
     def step(b):
         x.copy_(pool[b * T:(b + 1) * T])
-        ops.residual_rmsnorm(x, None, xn)
-        for l in range(L):
-            ops.moe_layer(xn, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], fused=fused,
-                          top_p=args.top_p, **kw)
-            ops.residual_rmsnorm(x, bufs[l].y, xn)
+        ops.stack_forward(x, stack, bufs, top_p=args.top_p, fused=fused, xn=xn, **kw)
 
     # unique experts per layer for each token batch (routing depends on the batch only)
     sbytes = np.zeros(n_batch)
@@ -321,10 +311,10 @@ def bench_stack(args, cfg) -> None:
         sink += flush.sum()
         if fused:
             ev0[k].record()
-            ops.layer_fused(xn, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l],
-                            top_p=args.top_p, **kw)
+            ops.layer_fused(x, layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l],
+                            top_p=args.top_p, x_out=xn, **kw)
             ev1[k].record()
-            kb.append(fused_bytes(cfg, int(active[b, l])))
+            kb.append(fused_bytes(cfg, int(bufs[l].route.worklist.n_active.item())))
         else:
             ops.route_topk(xn, layers[l]["router_w"], layers[l]["bias"], n_shared=cfg.n_shared, out=bufs[l].route,
                            top_p=args.top_p, **kw)
@@ -335,7 +325,8 @@ def bench_stack(args, cfg) -> None:
     torch.cuda.synchronize()
     dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
-    kname = f"layer_fused_kernel<{cfg.bits}, ...>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
+    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, "
+             f"true>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
     print(f"[bench] {kname} avg {dur.mean() * 1e6:.1f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
     base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
     out = {
@@ -348,6 +339,8 @@ def bench_stack(args, cfg) -> None:
                    "hidden": H, "inter": cfg.inter, "routed_experts": cfg.n_experts, "n_group": cfg.n_group,
                    "topk_group": cfg.topk_group, "top_k": cfg.top_k, "shared_experts": cfg.n_shared,
                    "bits": cfg.bits, "zipf_bias": cfg.zipf_s, "graph": "one per step over every layer",
+                   "layer_form": "one residual-form fused launch per layer" if fused else
+                   "separate calls + residual/RMSNorm kernel per layer",
                    "unique_experts_per_layer": float(active[idx].mean()), "top_p": args.top_p},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

@@ -246,6 +246,34 @@ int moe_layer_fused_topp_q2(const float* x, const float* router_w, const float* 
                             const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
 
 /*
+ * One layer of a pre-norm residual stack in one launch: x_out = x +
+ * MoE(rmsnorm(x)), rmsnorm(x) = x / sqrt(mean(x^2) + eps) per token,
+ * weightless.  The pages describe the MoE layer alone; this form is the
+ * reading used to chain layers (as moe_residual_rmsnorm between separate
+ * calls), fused so that a stack of layers is one launch per layer.  The norm
+ * is computed inside the launch (every workgroup, identically), the router and
+ * the experts see the normalised tokens, and the last phase adds x.
+ *   x     : fp32 [T, H] the residual stream (not normalised)
+ *   x_out : fp32 [T, H] may be x itself (every read of x precedes the first
+ *           write of x_out); y still receives MoE(rmsnorm(x))
+ *   eps   : >= 0, finite
+ * Other arguments, outputs and limits as for moe_layer_fused_topp_q*
+ * (top_p >= 1: plain top-k).
+ */
+int moe_layer_fused_resid_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                             int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                             float top_p, float eps, float* x_out, float* scores, int32_t* topk_idx, float* topk_w,
+                             const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_resid_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                             int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                             float top_p, float eps, float* x_out, float* scores, int32_t* topk_idx, float* topk_w,
+                             const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
+int moe_layer_fused_resid_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
+                             int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
+                             float top_p, float eps, float* x_out, float* scores, int32_t* topk_idx, float* topk_w,
+                             const moedec_worklist* wl, float* h, float* y, int32_t* workspace, void* stream);
+
+/*
  * Packing of codes (ideipro.ru: packing checked bit for bit; Show HN page,
  * "implemented features": int8, packed int4, packed int2).
  *   codes  : int8  [rows, row_len]                 one code per int8

@@ -93,12 +93,13 @@ int route_args_ok(int T, int H, int E, int n_group, int topk_group, int top_k, i
 }
 
 int layer_fused(int bits, const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
-                int T, int n_group, int topk_group, int top_k, float rsf, float top_p, float* scores,
-                int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, float* h, float* y, int32_t* workspace,
-                void* stream) {
+                int T, int n_group, int topk_group, int top_k, float rsf, float top_p, float* x_out, float eps,
+                float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                int32_t* workspace, void* stream) {
     if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w || !h || !y || !workspace)
         return MOEDEC_ERR_INVALID_ARG;
     if (isnan(top_p)) return MOEDEC_ERR_INVALID_ARG;
+    if (x_out && !(eps >= 0.0f && isfinite(eps))) return MOEDEC_ERR_INVALID_ARG;
     FusedLayerArgs f{};
     int st = check_experts(ex, wl, bits, T, top_k, f.ex);
     if (st != MOEDEC_OK) return st;
@@ -127,6 +128,8 @@ int layer_fused(int bits, const float* x, const float* router_w, const float* bi
     f.n_shared = ex->n_shared;
     f.rsf = rsf;
     f.top_p = top_p;
+    f.x_out = x_out;
+    f.eps = eps;
     const hipError_t err = launch_layer_fused(bits, f, static_cast<hipStream_t>(stream));
     if (err == hipErrorInvalidValue) return MOEDEC_ERR_UNSUPPORTED;   // shapes the LDS plan cannot hold
     return device_status(err);
@@ -285,7 +288,7 @@ MOEDEC_API int moe_layer_fused_q4(const float* x, const float* router_w, const f
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
     return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_topp_q4(const float* x, const float* router_w, const float* bias,
                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
@@ -293,14 +296,23 @@ MOEDEC_API int moe_layer_fused_topp_q4(const float* x, const float* router_w, co
                                        float* topk_w, const moedec_worklist* wl, float* h, float* y,
                                        int32_t* workspace, void* stream) {
     return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_resid_q4(const float* x, const float* router_w, const float* bias,
+                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                        float routed_scaling_factor, float top_p, float eps, float* x_out,
+                                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                        float* h, float* y, int32_t* workspace, void* stream) {
+    if (!x_out) return MOEDEC_ERR_INVALID_ARG;
+    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       x_out, eps, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_q8(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
                                   int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
     return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_topp_q8(const float* x, const float* router_w, const float* bias,
                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
@@ -308,14 +320,23 @@ MOEDEC_API int moe_layer_fused_topp_q8(const float* x, const float* router_w, co
                                        float* topk_w, const moedec_worklist* wl, float* h, float* y,
                                        int32_t* workspace, void* stream) {
     return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_resid_q8(const float* x, const float* router_w, const float* bias,
+                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                        float routed_scaling_factor, float top_p, float eps, float* x_out,
+                                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                        float* h, float* y, int32_t* workspace, void* stream) {
+    if (!x_out) return MOEDEC_ERR_INVALID_ARG;
+    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       x_out, eps, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_q2(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
                                   int T, int n_group, int topk_group, int top_k, float routed_scaling_factor,
                                   float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                                   float* h, float* y, int32_t* workspace, void* stream) {
     return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, 1.0f,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
 MOEDEC_API int moe_layer_fused_topp_q2(const float* x, const float* router_w, const float* bias,
                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
@@ -323,5 +344,14 @@ MOEDEC_API int moe_layer_fused_topp_q2(const float* x, const float* router_w, co
                                        float* topk_w, const moedec_worklist* wl, float* h, float* y,
                                        int32_t* workspace, void* stream) {
     return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
-                       scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_resid_q2(const float* x, const float* router_w, const float* bias,
+                                        const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                        float routed_scaling_factor, float top_p, float eps, float* x_out,
+                                        float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
+                                        float* h, float* y, int32_t* workspace, void* stream) {
+    if (!x_out) return MOEDEC_ERR_INVALID_ARG;
+    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       x_out, eps, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }

@@ -209,6 +209,8 @@ struct FusedLayerArgs {
     int T, E, n_group, topk_group, n_shared;
     float rsf;
     float top_p;               // >= 1: plain top-k
+    float* x_out;              // non-null: residual form, x_out = x + y with x normalised inside
+    float eps;                 // its RMSNorm epsilon
 };
 
 hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);

@@ -88,9 +88,10 @@ struct FusedArgs {
     int32_t* wl_assign;
     float* h;
     float* y;
+    float* x_out;                  // residual form: x_out = x + y (x is then the un-normalised stream)
     int32_t* ws;
     int E, n_group, topk_group, n_shared;
-    float rsf, top_p;
+    float rsf, top_p, eps;
     int qc;                        // assignments staged at once for down
     int rb;                        // gate/up blocks whose partial sums LDS holds at once
     int deferred;                  // 1: every block has its own slot and is finalised after the segment
@@ -164,10 +165,23 @@ struct GridGate {
 // Router rows e = part, part + nparts, ... for all T tokens: every thread holds
 // its float4s of the row, dots them with each token, the wave sums by DPP and
 // the 8 waves' sums are added in wave order.
-__device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int nparts, float (*red)[kMW]) {
+// Sum of squares of token t's row (kResid): every thread's float4 in k order,
+// fmaf chains, then the wave and the waves in fixed order -- the same bits in
+// every workgroup, whether or not it also computes router rows.
+__device__ __forceinline__ float ssq_part(const float4& v, float ss) {
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    return fmaf(v.w, v.w, ss);
+}
+
+template <bool kResid>
+__device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int nparts, float (*red)[kMW],
+                                            float (*ssq)[kMW], float* xinv) {
     const int H = f.a.H, T = f.a.T, E = f.E;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int n4 = H >> 2;
+    bool first = true;
     for (int e = part; e < E; e += nparts) {
         const float4* w4 = reinterpret_cast<const float4*>(f.router_w + (size_t)e * H);
         float4 wr[kRowF4];
@@ -178,7 +192,7 @@ __device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int np
         }
         for (int t = 0; t < T; ++t) {
             const float4* x4 = reinterpret_cast<const float4*>(f.x + (size_t)t * H);
-            float acc = 0.f;
+            float acc = 0.f, ss = 0.f;
 #pragma unroll
             for (int k = 0; k < kRowF4; ++k) {
                 const int i = threadIdx.x + k * kMT;
@@ -188,16 +202,50 @@ __device__ __forceinline__ void router_rows(const FusedArgs& f, int part, int np
                     acc = fmaf(wr[k].y, v.y, acc);
                     acc = fmaf(wr[k].z, v.z, acc);
                     acc = fmaf(wr[k].w, v.w, acc);
+                    if (kResid) ss = ssq_part(v, ss);
                 }
             }
             acc = group_sum<kWave>(acc);
             if (lane == 0) red[t][wave] = acc;
+            if (kResid && first) {
+                ss = group_sum<kWave>(ss);
+                if (lane == 0) ssq[t][wave] = ss;
+            }
         }
         __syncthreads();
         if ((int)threadIdx.x < T) {
             float z = 0.f;
             for (int w = 0; w < kMW; ++w) z += red[threadIdx.x][w];
+            if (kResid) {
+                if (first) {
+                    float q = 0.f;
+                    for (int w = 0; w < kMW; ++w) q += ssq[threadIdx.x][w];
+                    xinv[threadIdx.x] = 1.0f / sqrtf(q / (float)H + f.eps);
+                }
+                z *= xinv[threadIdx.x];                 // W . (x / rms) = (W . x) / rms
+            }
             store_device(f.scores + (size_t)threadIdx.x * E + e, 1.0f / (1.0f + expf(-z)));
+        }
+        __syncthreads();
+        first = false;
+    }
+    if (kResid && first) {                              // no router row here: the norms alone
+        for (int t = 0; t < T; ++t) {
+            const float4* x4 = reinterpret_cast<const float4*>(f.x + (size_t)t * H);
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < kRowF4; ++k) {
+                const int i = threadIdx.x + k * kMT;
+                if (i < n4) ss = ssq_part(x4[i], ss);
+            }
+            ss = group_sum<kWave>(ss);
+            if (lane == 0) ssq[t][wave] = ss;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < T) {
+            float q = 0.f;
+            for (int w = 0; w < kMW; ++w) q += ssq[threadIdx.x][w];
+            xinv[threadIdx.x] = 1.0f / sqrtf(q / (float)H + f.eps);
         }
         __syncthreads();
     }
@@ -284,9 +332,9 @@ __device__ __forceinline__ void zero_pad(int P, int NCH, int n, int ldn, i32x4* 
 // xu[t] = 2^-(e_t + kShift) undoes it and the code factor.  cmax[0..T) must
 // be zero on entry.  When all of x fits the registers (kStageX4 float4 per
 // thread) it is read once, else twice (a max pass and a convert pass).
-template <int BITS, typename Hook>
+template <int BITS, bool kResid, typename Hook>
 __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int T, i32x4* hi, i32x4* lo,
-                                        unsigned* cmax, float* xu, Hook&& after_loads) {
+                                        unsigned* cmax, float* xu, const float* xinv, Hook&& after_loads) {
     using C = I8Codec<BITS>;
     const int H4 = H >> 2, total4 = T * H4;
     const float4* x4 = reinterpret_cast<const float4*>(x);
@@ -311,6 +359,11 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int 
         }
     }
     __syncthreads();
+    // kResid: the staged values are x / rms, whose largest magnitude is the
+    // largest |x| times 1/rms (rounding is monotonic)
+    if (kResid && (int)threadIdx.x < T)
+        cmax[threadIdx.x] = __float_as_uint(__uint_as_float(cmax[threadIdx.x]) * xinv[threadIdx.x]);
+    if (kResid) __syncthreads();
     if ((int)threadIdx.x < T) xu[threadIdx.x] = ldexpf(1.0f, -q16_exponent(__uint_as_float(cmax[threadIdx.x])) - C::kShift);
     uint8_t* h8 = reinterpret_cast<uint8_t*>(hi);
     uint8_t* l8 = reinterpret_cast<uint8_t*>(lo);
@@ -325,7 +378,12 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int 
             if (i4 < total4) {
                 const int t = i4 / H4;
                 const float sc = ldexpf(1.0f, q16_exponent(__uint_as_float(cmax[t])));
-                scatter4<BITS>(v[u], sc, (i4 - t * H4) * 4, t, T, h8, l8);
+                float4 vv = v[u];
+                if (kResid) {
+                    const float r = xinv[t];
+                    vv = make_float4(vv.x * r, vv.y * r, vv.z * r, vv.w * r);
+                }
+                scatter4<BITS>(vv, sc, (i4 - t * H4) * 4, t, T, h8, l8);
             }
         }
     }
@@ -417,7 +475,7 @@ __device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
 // computed against zero activations.  Every load is issued at a clamped
 // (valid) address, so every item issues exactly two loads and the wait
 // counts before each use are static.
-template <int BITS>
+template <int BITS, bool kResid>
 __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, const float* xu,
                                        GridGate& gate) {
     using C = I8Codec<BITS>;
@@ -882,18 +940,22 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         const int bb = rr >> 4, r16 = rr & 15;
         float s = 0.f;
         for (int w = 0; w < kMW; ++w) s += dred[((w * kNBD + bb) * 16 + r16) * 16 + t];
-        f.y[(size_t)t * H + dr0 + rr] = s;
+        const size_t o = (size_t)t * H + dr0 + rr;
+        f.y[o] = s;
+        if (kResid) f.x_out[o] = f.x[o] + s;            // every workgroup read x before the h exchange
     }
 }
 
-template <int BITS, bool kTopP>
+template <int BITS, bool kTopP, bool kResid>
 __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     constexpr int NM = I8Codec<BITS>::NM;
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ FusedRoute r;
     __shared__ float gemv_red[kCols][kMW];
+    __shared__ float gemv_ssq[kResid ? kCols : 1][kMW];
     __shared__ unsigned xmax[kCols];
     __shared__ float xu[kCols];
+    __shared__ float xinv[kCols];                     // kResid: 1 / rms of each token's x
 
     const ExpertArgs& a = f.a;
     const int T = a.T, H = a.H, K = a.top_k, S = f.n_shared, E = f.E;
@@ -905,9 +967,9 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     gate.init();
 
     // ---- phase 1
-    router_rows(f, blockIdx.x, gridDim.x, gemv_red);
+    router_rows<kResid>(f, blockIdx.x, gridDim.x, gemv_red, gemv_ssq, xinv);
     gate.settle();
-    stage_x<BITS>(f.x, H, T, xhi, xlo, xmax, xu, [&] { gate.count(); });   // x loads go out before the count
+    stage_x<BITS, kResid>(f.x, H, T, xhi, xlo, xmax, xu, xinv, [&] { gate.count(); });   // x loads out before the count
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
@@ -915,7 +977,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
                                                              f.rsf, f.top_p, r);
 
     // ---- phase 3: the stream
-    stream<BITS>(f, r, dyn, xu, gate);
+    stream<BITS, kResid>(f, r, dyn, xu, gate);
 
     // Workgroup 0 writes the routing outputs last, from LDS: stores issued
     // earlier would make the compiler wait for the stream's first loads
@@ -942,8 +1004,10 @@ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 // starts][chunk tables]; the chunk size qc is the largest that fits.
 template <int BITS>
 hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st) {
-    auto k = f.top_p < 1.f ? layer_fused_kernel<BITS, true> : layer_fused_kernel<BITS, false>;
-    static size_t static_lds = 0;        // the kernel's static LDS, read once
+    auto k = f.x_out ? (f.top_p < 1.f ? layer_fused_kernel<BITS, true, true> : layer_fused_kernel<BITS, false, true>)
+                     : (f.top_p < 1.f ? layer_fused_kernel<BITS, true, false> : layer_fused_kernel<BITS, false, false>);
+    static size_t static_cache[2][2] = {{0, 0}, {0, 0}};   // each variant's static LDS, read once
+    size_t& static_lds = static_cache[f.top_p < 1.f][f.x_out != nullptr];
     if (static_lds == 0) {
         hipFuncAttributes attr;
         hipError_t err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k));
@@ -1030,6 +1094,8 @@ hipError_t launch_layer_fused(int bits, const FusedLayerArgs& l, hipStream_t st)
     f.n_shared = l.n_shared;
     f.rsf = l.rsf;
     f.top_p = l.top_p;
+    f.x_out = l.x_out;
+    f.eps = l.eps;
     switch (bits) {
         case 4: return layer_fused_bits<4>(f, l, st);
         case 8: return layer_fused_bits<8>(f, l, st);

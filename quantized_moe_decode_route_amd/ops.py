@@ -64,6 +64,8 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
     _SIGS[f"moe_layer_fused_topp_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P],
                                            _I)
+    _SIGS[f"moe_layer_fused_resid_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P], _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
 
@@ -343,9 +345,11 @@ def fused_supported(T: int, ex: Experts) -> bool:
 
 
 def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
-                topk_group: int, top_k: int, rsf: float, buf: LayerBuffers, top_p: float | None = None) -> LayerBuffers:
+                topk_group: int, top_k: int, rsf: float, buf: LayerBuffers, top_p: float | None = None,
+                x_out: torch.Tensor | None = None, eps: float = 1e-6) -> LayerBuffers:
     """moe_layer_fused_q{bits} (moe_layer_fused_topp_q{bits} when top_p is
-    given): the whole layer in one launch (outputs in buf)."""
+    given): the whole layer in one launch (outputs in buf).  With x_out:
+    moe_layer_fused_resid_q{bits}, x_out = x + MoE(rmsnorm(x)) (x_out may be x)."""
     T, H = x.shape
     E = ex.n_experts
     if router_w.shape != (E, H) or bias.shape != (E,) or H != ex.hidden:
@@ -355,9 +359,16 @@ def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex:
             buf.h.shape != (T * (top_k + ex.n_shared), ex.inter) or buf.workspace.numel() < FUSED_WORKSPACE_INTS:
         raise ValueError("buffers do not match the call's shapes")
     s_ex, s_wl = ex.struct(), r.worklist.struct()
-    name = f"moe_layer_fused_{_suffix(ex.bits)}" if top_p is None else f"moe_layer_fused_topp_{_suffix(ex.bits)}"
+    if x_out is not None:
+        if x_out.shape != (T, H):
+            raise ValueError("x_out must be [T, hidden]")
+        name = f"moe_layer_fused_resid_{_suffix(ex.bits)}"
+        pre = (float(rsf), 1.0 if top_p is None else float(top_p), float(eps), _dev(x_out, torch.float32, "x_out"))
+    elif top_p is None:
+        name, pre = f"moe_layer_fused_{_suffix(ex.bits)}", (float(rsf),)
+    else:
+        name, pre = f"moe_layer_fused_topp_{_suffix(ex.bits)}", (float(rsf), float(top_p))
     fn = getattr(lib(), name)
-    pre = (float(rsf),) if top_p is None else (float(rsf), float(top_p))
     st = fn(_dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"), _dev(bias, torch.float32, "bias"),
             ctypes.byref(s_ex), T, n_group, topk_group, top_k, *pre,
             _dev(r.scores, torch.float32, "scores"), _dev(r.topk_idx, torch.int32, "topk_idx"),
@@ -392,3 +403,42 @@ def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: E
     gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)
     down_combine(buf.h, ex, buf.route.worklist, buf.route.topk_w, top_k, out=buf.y)
     return buf
+
+
+def stack_forward(x: torch.Tensor, layers: list, bufs: list, *, n_group: int, topk_group: int, top_k: int,
+                  rsf: float, eps: float = 1e-6, top_p: float | None = None, fused: bool | None = None,
+                  xn: torch.Tensor | None = None) -> bool:
+    """x <- x + MoE_l(rmsnorm(x)) for every layer l, in place on x (the
+    pre-norm residual stack).  layers[l] = (router_w, bias, Experts); bufs[l]
+    a LayerBuffers.  Fused: one moe_layer_fused_resid launch per layer (the
+    norm and the residual inside it); else the separate calls with
+    moe_residual_rmsnorm between them (xn: a [T, H] scratch for the normalised
+    tokens).  fused=None tries the fused form on the first layer and keeps
+    whichever runs; returns whether the fused form ran."""
+    T, H = x.shape
+    kw = dict(n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf)
+    if fused is None:
+        fused = fused_supported(T, layers[0][2])
+        if fused:
+            try:
+                rw, b, ex = layers[0]
+                layer_fused(x, rw, b, ex, buf=bufs[0], top_p=top_p, x_out=x, eps=eps, **kw)
+            except MoedecError as err:
+                if err.status != MOEDEC_ERR_UNSUPPORTED:
+                    raise
+                fused = False
+            else:
+                for (rw, b, ex), buf in zip(layers[1:], bufs[1:]):
+                    layer_fused(x, rw, b, ex, buf=buf, top_p=top_p, x_out=x, eps=eps, **kw)
+                return True
+    if fused:
+        for (rw, b, ex), buf in zip(layers, bufs):
+            layer_fused(x, rw, b, ex, buf=buf, top_p=top_p, x_out=x, eps=eps, **kw)
+        return True
+    if xn is None:
+        xn = torch.empty_like(x)
+    residual_rmsnorm(x, None, xn, eps)
+    for (rw, b, ex), buf in zip(layers, bufs):
+        moe_layer(xn, rw, b, ex, buf=buf, fused=False, top_p=top_p, **kw)
+        residual_rmsnorm(x, buf.y, xn, eps)
+    return False

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 29
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,6 +124,21 @@ def _fused(lib, suffix, ex, wl, **kw):
 def test_fused_call_rejects(lib, suffix, bits, ekw, kw, status):
     ekw = dict(ekw, bits=ekw.get("bits", bits))
     assert _fused(lib, suffix, _experts(**ekw), _wl(), **kw) == status
+
+
+@pytest.mark.parametrize("suffix", ["q4", "q8", "q2"])
+def test_fused_resid_and_topp_reject(lib, suffix):
+    import math
+    ex, wl = _experts(bits=int(suffix[1:])), _wl()
+    resid = getattr(lib, f"moe_layer_fused_resid_{suffix}")
+    topp = getattr(lib, f"moe_layer_fused_topp_{suffix}")
+    head = (FAKE, FAKE, FAKE, ctypes.byref(ex), 1, 4, 2, 4, 2.5)
+    tail = (FAKE, FAKE, FAKE, ctypes.byref(wl), FAKE, FAKE, FAKE, None)
+    assert resid(*head, 1.0, 1e-6, None, *tail) == 1                 # no x_out
+    assert resid(*head, 1.0, -1.0, FAKE, *tail) == 1                 # negative eps
+    assert resid(*head, 1.0, math.inf, FAKE, *tail) == 1
+    assert resid(*head, math.nan, 1e-6, FAKE, *tail) == 1            # NaN top_p
+    assert topp(*head, math.nan, *tail) == 1
 
 
 def test_fused_call_requires_structs(lib):
