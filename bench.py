@@ -525,7 +525,7 @@ def main() -> None:
         dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
     traffic = traffic_from_profile(kind, cfg.name) if args.top_p is None else None
-    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}>"
+    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, false>"
              if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
