@@ -52,6 +52,13 @@ Readings (the pages are silent on these):
      zero row gets s = 0 and codes 0.  Decided in fp32.
  R21 a row holding a NaN or an infinity gets s = NaN and codes 0, so that the
      problem shows in every output computed from it.
+ R23 Q8_0-style int8 activations (the integer-dot item): the activations that
+     meet the weights -- each token's x, and each assignment's h times its
+     routing weight (fp32) -- are quantised in blocks of 512/bits consecutive
+     input columns (64 / 128 / 256 for int8 / int4 / int2 weights: one
+     K-chunk of the matrix-core tile; Q8_0 itself uses 32) by R20's rule
+     with qmax 127 (d = absmax / 127, q = rint(v / d) half to even); the dot
+     products are then exact integer sums scaled by d.
  R22 adaptive expert top-p (the run options' --topp): after the top-k
      selection, order the K chosen experts by unbiased score s descending
      (a NaN s last, ties to the lower index), add their s in that order in
@@ -130,6 +137,11 @@ def unpack_rows(packed: np.ndarray, bits: int) -> np.ndarray:
     return out.astype(np.int8)
 
 
+def act8_block(bits: int) -> int:
+    """Input columns per activation block for weights of `bits` (R23)."""
+    return 512 // bits
+
+
 def dequantize(packed: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
     """W[r, c] = code[r, c] * scale[r], exact in fp64 (dequant-on-use, R10)."""
     w = unpack_rows(packed, bits).astype(np.float64)
@@ -173,6 +185,17 @@ def quantize_rows(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
         q = np.rint(ratio)                                 # half to even
         codes[r] = np.clip(q, lo, hi).astype(np.int8)
     return codes, scales
+
+
+def quantize_act8(v: np.ndarray, block: int) -> np.ndarray:
+    """fp32 activation rows [rows, n] -> the values q * d they stand for after
+    Q8_0-style quantisation in blocks of `block` columns (R23; R20's rule with
+    qmax 127 applied to each block), exact in fp64."""
+    v32 = np.asarray(v, dtype=np.float32)
+    rows, n = v32.shape
+    assert n % block == 0
+    q, d = quantize_rows(v32.reshape(rows * n // block, block), 8)
+    return (q.astype(np.float64) * d.astype(np.float64)[:, None]).reshape(rows, n)
 
 
 # --------------------------------------------------------------------- router
@@ -393,13 +416,15 @@ class LayerResult:
 
 def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
               expert: Callable[[int], dict], *, n_group: int, topk_group: int, top_k: int,
-              n_shared: int, rsf: float, bits: int, top_p: float = 1.0) -> LayerResult:
+              n_shared: int, rsf: float, bits: int, top_p: float = 1.0, act8: bool = False) -> LayerResult:
     """One routed-MoE layer on T tokens.
 
     expert(e) returns the packed codes and row scales of expert e
     ({q_gate, q_up, q_down, s_gate, s_up, s_down}); routed experts are
     0..E-1, shared ones E..E+S-1.  The selection is taken on the fp64 scores
-    rounded to fp32.  top_p < 1 adds the adaptive top-p prefix (R22)."""
+    rounded to fp32.  top_p < 1 adds the adaptive top-p prefix (R22); act8
+    quantises the activations that meet the weights (R23): x before gate/up,
+    and fp32(h) times the slot's fp32 weight before down."""
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     E = router_w.shape[0]
@@ -407,6 +432,8 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
     idx, w, _ = select_experts_topp(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf, top_p)
     wl = batch_union(idx, E, n_shared)
     slots = top_k + n_shared
+    blk = act8_block(bits)
+    xin = quantize_act8(x, blk) if act8 else x
     y = np.zeros((T, router_w.shape[1]), np.float64)
     h_all = None
     for j, e in enumerate(wl.expert_id):
@@ -418,10 +445,14 @@ def moe_layer(x: np.ndarray, router_w: np.ndarray, bias: np.ndarray,
             h_all = np.zeros((T * slots, wg.shape[0]), np.float64)
         for a in wl.assign[wl.seg[j]:wl.seg[j + 1]]:
             t, slot = divmod(int(a), slots)
-            o, h = swiglu_expert(x[t], wg, wu, wd)
+            o, h = swiglu_expert(xin[t], wg, wu, wd)
             h_all[a] = h
             coef = float(w[t, slot]) if slot < top_k else 1.0
-            y[t] += coef * o
+            if act8:
+                hw = (h.astype(np.float32) * np.float32(coef)).astype(np.float32)
+                y[t] += wd @ quantize_act8(hw[None, :], blk)[0]
+            else:
+                y[t] += coef * o
     margin = selection_margin(s64, bias, n_group, topk_group, top_k)
     idx_k, _ = select_experts(s64.astype(np.float32), bias, n_group, topk_group, top_k, rsf) if top_p < 1.0 \
         else (idx, None)
