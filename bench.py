@@ -86,7 +86,7 @@ def traffic_from_profile(kind: str, workload: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s: float, top_p: float | None = None) -> dict:
+def cpu_baseline(cfg, budget_s: float, top_p: float | None = None, act8: bool = False) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_limits
 
@@ -114,7 +114,7 @@ def cpu_baseline(cfg, budget_s: float, top_p: float | None = None) -> dict:
             t0 = time.perf_counter()
             r = orc.moe_layer(x, rw, b, cache.__getitem__, n_group=cfg.n_group, topk_group=cfg.topk_group,
                               top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits,
-                              top_p=1.0 if top_p is None else top_p)
+                              top_p=1.0 if top_p is None else top_p, act8=act8)
             elapsed += time.perf_counter() - t0
             nbytes += step_bytes(cfg, len(r.worklist.expert_id))
             ntok += cfg.tokens
@@ -364,6 +364,8 @@ def main() -> None:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--top-p", type=float, default=None,
                     help="route with adaptive expert top-p at this p (moe_layer_fused_topp / moe_route_topp)")
+    ap.add_argument("--act8", action="store_true",
+                    help="the fused layer with Q8_0-style int8 activations (moe_layer_fused_act8)")
     ap.add_argument("--quantize", action="store_true",
                     help="time the row quantiser instead (fp32 expert matrices -> packed codes + row scales)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -421,7 +423,7 @@ def main() -> None:
     if fused:
         try:
             ops.layer_fused(tokens(0), layers[0]["router_w"], layers[0]["bias"], experts[0], buf=bufs[0],
-                            top_p=args.top_p, **kw)
+                            top_p=args.top_p, act8=args.act8, **kw)
         except ops.MoedecError as err:
             if err.status != ops.MOEDEC_ERR_UNSUPPORTED:
                 raise
@@ -430,7 +432,7 @@ def main() -> None:
     def step(i):
         l = i % L
         ops.moe_layer(tokens(i), layers[l]["router_w"], layers[l]["bias"], experts[l], buf=bufs[l], fused=fused,
-                      top_p=args.top_p, **kw)
+                      top_p=args.top_p, act8=args.act8, **kw)
 
     # unique experts of every step of the period (routing is a function of (layer, token))
     n_active = np.zeros(period, np.int64)
@@ -524,16 +526,16 @@ def main() -> None:
         torch.cuda.synchronize()
         dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3   # seconds
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
-    traffic = traffic_from_profile(kind, cfg.name) if args.top_p is None else None
-    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, false>"
-             if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
+    traffic = traffic_from_profile(kind, cfg.name) if args.top_p is None and not args.act8 else None
+    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, "
+             f"false, {'true' if args.act8 else 'false'}>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_us": round(float(dur.mean() * 1e6), 2),
                 "bytes_per_launch": int(np.mean(kb))}
     print(f"[bench] {kname} avg {dur.mean() * 1e6:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
-    base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
+    base = cpu_baseline(cfg, args.cpu_budget, args.top_p, args.act8) if args.cpu_budget > 0 else None
 
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -545,7 +547,7 @@ def main() -> None:
                    "routed_experts": cfg.n_experts, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
                    "top_k": cfg.top_k, "shared_experts": cfg.n_shared, "bits": cfg.bits,
                    "resident_layers": L, "unique_experts_per_step": float(n_active[idx].mean()),
-                   "top_p": args.top_p},
+                   "top_p": args.top_p, "activations": "int8 blocks" if args.act8 else "int16 per token"},
         "roofline": roofline, "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

@@ -95,7 +95,7 @@ int route_args_ok(int T, int H, int E, int n_group, int topk_group, int top_k, i
 int layer_fused(int bits, const float* x, const float* router_w, const float* bias, const moedec_experts* ex,
                 int T, int n_group, int topk_group, int top_k, float rsf, float top_p, float* x_out, float eps,
                 float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl, float* h, float* y,
-                int32_t* workspace, void* stream) {
+                int32_t* workspace, void* stream, int act8 = 0) {
     if (!x || !router_w || !bias || !scores || !topk_idx || !topk_w || !h || !y || !workspace)
         return MOEDEC_ERR_INVALID_ARG;
     if (isnan(top_p)) return MOEDEC_ERR_INVALID_ARG;
@@ -130,6 +130,7 @@ int layer_fused(int bits, const float* x, const float* router_w, const float* bi
     f.top_p = top_p;
     f.x_out = x_out;
     f.eps = eps;
+    f.act8 = act8;
     const hipError_t err = launch_layer_fused(bits, f, static_cast<hipStream_t>(stream));
     if (err == hipErrorInvalidValue) return MOEDEC_ERR_UNSUPPORTED;   // shapes the LDS plan cannot hold
     return device_status(err);
@@ -298,6 +299,14 @@ MOEDEC_API int moe_layer_fused_topp_q4(const float* x, const float* router_w, co
     return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
                        nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
+MOEDEC_API int moe_layer_fused_act8_q4(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(4, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream, 1);
+}
 MOEDEC_API int moe_layer_fused_resid_q4(const float* x, const float* router_w, const float* bias,
                                         const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
                                         float routed_scaling_factor, float top_p, float eps, float* x_out,
@@ -322,6 +331,14 @@ MOEDEC_API int moe_layer_fused_topp_q8(const float* x, const float* router_w, co
     return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
                        nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
 }
+MOEDEC_API int moe_layer_fused_act8_q8(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(8, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream, 1);
+}
 MOEDEC_API int moe_layer_fused_resid_q8(const float* x, const float* router_w, const float* bias,
                                         const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
                                         float routed_scaling_factor, float top_p, float eps, float* x_out,
@@ -345,6 +362,14 @@ MOEDEC_API int moe_layer_fused_topp_q2(const float* x, const float* router_w, co
                                        int32_t* workspace, void* stream) {
     return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
                        nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream);
+}
+MOEDEC_API int moe_layer_fused_act8_q2(const float* x, const float* router_w, const float* bias,
+                                       const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,
+                                       float routed_scaling_factor, float top_p, float* scores, int32_t* topk_idx,
+                                       float* topk_w, const moedec_worklist* wl, float* h, float* y,
+                                       int32_t* workspace, void* stream) {
+    return layer_fused(2, x, router_w, bias, ex, T, n_group, topk_group, top_k, routed_scaling_factor, top_p,
+                       nullptr, 0.0f, scores, topk_idx, topk_w, wl, h, y, workspace, stream, 1);
 }
 MOEDEC_API int moe_layer_fused_resid_q2(const float* x, const float* router_w, const float* bias,
                                         const moedec_experts* ex, int T, int n_group, int topk_group, int top_k,

@@ -211,6 +211,7 @@ struct FusedLayerArgs {
     float top_p;               // >= 1: plain top-k
     float* x_out;              // non-null: residual form, x_out = x + y with x normalised inside
     float eps;                 // its RMSNorm epsilon
+    int act8;                  // 1: Q8_0-style int8 activations in blocks
 };
 
 hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);

@@ -92,6 +92,7 @@ struct FusedArgs {
     int32_t* ws;
     int E, n_group, topk_group, n_shared;
     float rsf, top_p, eps;
+    int act8;                      // 1: Q8_0-style int8 activations (block scales) instead of int16
     int qc;                        // assignments staged at once for down
     int rb;                        // gate/up blocks whose partial sums LDS holds at once
     int deferred;                  // 1: every block has its own slot and is finalised after the segment
@@ -327,19 +328,129 @@ __device__ __forceinline__ void zero_pad(int P, int NCH, int n, int ldn, i32x4* 
     }
 }
 
+// ---- int8 activations in blocks (Q8_0 style): a block is one K-chunk of
+// the B layout, 4 groups of CW columns = 512/BITS columns, so one wave item
+// covers exactly one block of every column and the block's scale applies to
+// the item's integer MFMA sums.  d = absmax / 127 and q = rint(v / d) in IEEE
+// fp32 (d = 0: all zero; a NaN or an infinity in the block: d = NaN, q = 0).
+
+// Largest |value| (and non-finite flag) over the GL lanes of this lane's group.
+template <int GL>
+__device__ __forceinline__ float group_absmax(float m, bool& bad) {
+    float b = bad ? 1.f : 0.f;
+#pragma unroll
+    for (int o = GL / 2; o >= 1; o >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, o, kWave));
+        b = fmaxf(b, __shfl_xor(b, o, kWave));
+    }
+    bad = b != 0.f;
+    return m;
+}
+
+// The block scale of a group and the int8 codes of 4 of its values.
+__device__ __forceinline__ float q8_scale(const float4& v, bool valid, int gl_log2, bool& ok) {
+    float m = valid ? fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))) : 0.f;
+    bool bad = valid && !(m <= 3.402823466e38f) ;
+    bad = bad || (valid && (v.x != v.x || v.y != v.y || v.z != v.z || v.w != v.w));
+    if (gl_log2 == 4) m = group_absmax<16>(m, bad);
+    else if (gl_log2 == 5) m = group_absmax<32>(m, bad);
+    else m = group_absmax<64>(m, bad);
+    const float d = bad ? __uint_as_float(0x7FC00000u) : m / 127.0f;
+    ok = !bad && d != 0.f;
+    return d;
+}
+
+__device__ __forceinline__ int q8_code(float x, float d) {
+    return (int)fminf(fmaxf(rintf(x / d), -127.f), 127.f);
+}
+
+// Four codes of consecutive columns col0.. of row k into the hi bytes of the
+// B layout (the placement of scatter4).
+template <int BITS>
+__device__ __forceinline__ void place4_q8(int h0, int h1, int h2, int h3, int col0, int k, int ldn, uint8_t* hi) {
+    using C = I8Codec<BITS>;
+    const int g = col0 / C::CW, p0 = col0 - g * C::CW;
+    const int unit = (g * ldn + k) * C::NM * 16;
+    if constexpr (BITS == 4) {
+        const int s0 = unit + 4 * (p0 >> 3) + ((p0 >> 1) & 3);
+        *reinterpret_cast<uint16_t*>(hi + s0) = (uint16_t)pack_bytes(h0, h2, 0, 0);
+        *reinterpret_cast<uint16_t*>(hi + s0 + 16) = (uint16_t)pack_bytes(h1, h3, 0, 0);
+    } else if constexpr (BITS == 8) {
+        *reinterpret_cast<uint32_t*>(hi + unit + p0) = pack_bytes(h0, h1, h2, h3);
+    } else {
+        const int s0 = unit + 4 * (p0 >> 4) + ((p0 >> 2) & 3);
+        hi[s0] = (uint8_t)h0;
+        hi[s0 + 16] = (uint8_t)h1;
+        hi[s0 + 32] = (uint8_t)h2;
+        hi[s0 + 48] = (uint8_t)h3;
+    }
+}
+
+// Quantise and place one float4 (value i4 of a row-major [rows][cols4]
+// layout) whose lane group shares a block: writes the codes, and the group's
+// first lane writes the block scale times 2^-kShift to qd[blk * qld + row].
+template <int BITS>
+__device__ __forceinline__ void stage_q8(float4 v, bool valid, int row, int c4, int ldn, uint8_t* hi, float* qd,
+                                         int qld) {
+    using C = I8Codec<BITS>;
+    constexpr int GL = 128 / BITS;                 // float4 per block: 512 / BITS columns
+    constexpr int GLOG = BITS == 8 ? 4 : BITS == 4 ? 5 : 6;
+    bool ok;
+    const float d = q8_scale(v, valid, GLOG, ok);
+    if (!valid) return;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (ok) {
+        q0 = q8_code(v.x, d);
+        q1 = q8_code(v.y, d);
+        q2 = q8_code(v.z, d);
+        q3 = q8_code(v.w, d);
+    }
+    place4_q8<BITS>(q0, q1, q2, q3, c4 * 4, row, ldn, hi);
+    if ((c4 & (GL - 1)) == 0) qd[(c4 / GL) * qld + row] = d * (1.0f / (float)(1 << C::kShift));
+}
+
 // Stage the T token rows of x (row-major [T][H]) as int8 hi/lo B operands,
 // unit ((g*T + t)*NM + m); column t = token t has its own exponent, and
 // xu[t] = 2^-(e_t + kShift) undoes it and the code factor.  cmax[0..T) must
 // be zero on entry.  When all of x fits the registers (kStageX4 float4 per
 // thread) it is read once, else twice (a max pass and a convert pass).
-template <int BITS, bool kResid, typename Hook>
+template <int BITS, bool kResid, bool kQ8, typename Hook>
 __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int T, i32x4* hi, i32x4* lo,
-                                        unsigned* cmax, float* xu, const float* xinv, Hook&& after_loads) {
+                                        unsigned* cmax, float* xu, const float* xinv, float* qdx,
+                                        Hook&& after_loads) {
     using C = I8Codec<BITS>;
     const int H4 = H >> 2, total4 = T * H4;
     const float4* x4 = reinterpret_cast<const float4*>(x);
     const bool single = total4 <= kStageX4 * kMT;
     float4 v[kStageX4];
+    if constexpr (kQ8) {
+        // one pass: each lane group of a block finds its scale and writes its codes
+        uint8_t* h8 = reinterpret_cast<uint8_t*>(hi);
+        for (int b0 = 0; b0 < total4; b0 += kStageX4 * kMT) {
+#pragma unroll
+            for (int u = 0; u < kStageX4; ++u) v[u] = x4[min(b0 + (int)threadIdx.x + u * kMT, total4 - 1)];
+            if (b0 == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                after_loads();
+            }
+#pragma unroll
+            for (int u = 0; u < kStageX4; ++u) {
+                const int i4 = b0 + (int)threadIdx.x + u * kMT;
+                const bool ok = i4 < total4;
+                const int t = ok ? i4 / H4 : 0;
+                float4 vv = v[u];
+                if (kResid && ok) {
+                    const float r = xinv[t];
+                    vv = make_float4(vv.x * r, vv.y * r, vv.z * r, vv.w * r);
+                }
+                stage_q8<BITS>(vv, ok, t, i4 - t * H4, T, h8, qdx, kCols);
+            }
+        }
+        if ((int)threadIdx.x < T) xu[threadIdx.x] = 1.0f;      // the block scales carry the unscale
+        const int P = H / C::CW;
+        zero_pad<BITS>(P, (P + 3) / 4, T, T, hi, lo);
+        return;
+    }
     for (int b0 = 0; b0 < total4; b0 += kStageX4 * kMT) {
 #pragma unroll
         for (int u = 0; u < kStageX4; ++u) {           // every load first, then use
@@ -397,9 +508,10 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int 
 // device-coherent 16-byte loads, consecutive lanes reading consecutive 16
 // bytes (all kStageV4 loads of a thread issued before any is used).
 // n * I <= kStageV4 * 4 * kMT; cmax[0..n) must be zero on entry.
-template <int BITS>
+template <int BITS, bool kQ8>
 __device__ __forceinline__ void stage_h(const float* h, int h_bytes, int I, const int* qrow, const float* qmul,
-                                        int n, int ldn, i32x4* hi, i32x4* lo, unsigned* cmax, float* dsl) {
+                                        int n, int ldn, i32x4* hi, i32x4* lo, unsigned* cmax, float* dsl,
+                                        float* qdh) {
     using C = I8Codec<BITS>;
     const int I4 = I >> 2, total4 = n * I4;
     const __amdgpu_buffer_rsrc_t rs =
@@ -411,6 +523,23 @@ __device__ __forceinline__ void stage_h(const float* h, int h_bytes, int I, cons
         const int k = min(i4 / I4, n - 1), c4 = i4 - (i4 / I4) * I4;
         const int off = i4 < total4 ? (qrow[k] * I4 + c4) * 16 : 0;
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent);
+    }
+    if constexpr (kQ8) {
+        // blocks of the rows h * weight: qdh[blk * ldn + k] = scale * 2^-kShift
+        uint8_t* h8 = reinterpret_cast<uint8_t*>(hi);
+#pragma unroll
+        for (int u = 0; u < kStageV4; ++u) {
+            const int i4 = threadIdx.x + u * kMT;
+            const bool ok = i4 < total4;
+            const int k = ok ? i4 / I4 : 0;
+            const float w = qmul[k];
+            const float4 f4 = make_float4(__uint_as_float(v[u].x) * w, __uint_as_float(v[u].y) * w,
+                                          __uint_as_float(v[u].z) * w, __uint_as_float(v[u].w) * w);
+            stage_q8<BITS>(f4, ok, k, i4 - k * I4, ldn, h8, qdh, ldn);
+        }
+        const int P = I / C::CW;
+        zero_pad<BITS>(P, (P + 3) / 4, n, ldn, hi, lo);
+        return;
     }
 #pragma unroll
     for (int u = 0; u < kStageV4; ++u) {
@@ -475,9 +604,9 @@ __device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
 // computed against zero activations.  Every load is issued at a clamped
 // (valid) address, so every item issues exactly two loads and the wait
 // counts before each use are static.
-template <int BITS, bool kResid>
+template <int BITS, bool kResid, bool kQ8>
 __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, const float* xu,
-                                       GridGate& gate) {
+                                       const float* qdx, GridGate& gate) {
     using C = I8Codec<BITS>;
     constexpr int NM = C::NM;
     constexpr int W = kStreamW;
@@ -528,6 +657,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     float* dsl = reinterpret_cast<float*>(qmax + qc);             // [qc]
     int* amap = reinterpret_cast<int*>(dsl + qc);                 // [qc][16]
     int* ctab = amap + qc * kCols;                                 // [chunks + 1][3]
+    // kQ8: block scales of the staged h rows, [NCHd][qc], after the chunk tables
 
     // Positions: the gate/up items, then each down chunk's items, every segment
     // padded to a multiple of W, so a segment starts at ring slot 0 and its
@@ -537,6 +667,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int Ngu = nbg * nkg;
     const int Gpad = (Ngu + W - 1) / W * W;
     const int nchunk = rd > 0 ? (A + qc - 1) / qc : 0;
+    float* qdh = reinterpret_cast<float*>(ctab + 3 * ((T * slots + qc - 1) / qc + 1));
 
     // Two cursors walk the positions in order, one W positions ahead issuing
     // loads, one computing; a cursor advances by counting (no division or
@@ -621,13 +752,15 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     };
 
     const i32x4 zero4 = {0, 0, 0, 0};
+    const floatx4 zerof4 = {0.f, 0.f, 0.f, 0.f};
     i32x4 gh = zero4, gl = zero4, uh = zero4, ul = zero4;     // gate / up, hi / lo parts
     i32x4 ah[kNBD], al[kNBD];
     floatx4 tot[kNBD];
+    floatx4 gf = zerof4, uf = zerof4, af[kNBD];              // kQ8: block-scaled sums
 #pragma unroll
     for (int bb = 0; bb < kNBD; ++bb) {
         ah[bb] = al[bb] = zero4;
-        tot[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        tot[bb] = af[bb] = zerof4;
     }
     int chunk_first = 0;            // first expert of the staged chunk
     // per-expert state of the computing cursor: this lane's staged column and its unscale
@@ -639,7 +772,23 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const int tcol = min(ln, T - 1);              // this lane's token column in B
     auto gu_item = [&](const Cursor& c, const uint4* cur) {
         const int ch = wave * nkg + c.k;
-        if (ch < NCHg) {
+        if (kQ8 && ch < NCHg) {
+            i32x4 bq[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) bq[m] = xhi[((ch * 4 + lq) * T + tcol) * NM + m];
+            i32x4 g8 = zero4, u8 = zero4;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                g8 = mma(operand<BITS>(cur[0], m), bq[m], g8);
+                u8 = mma(operand<BITS>(cur[1], m), bq[m], u8);
+            }
+            const float dq = qdx[ch * kCols + tcol];          // the block's scale for this lane's token
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                gf[ii] = fmaf(dq, (float)g8[ii], gf[ii]);
+                uf[ii] = fmaf(dq, (float)u8[ii], uf[ii]);
+            }
+        } else if (!kQ8 && ch < NCHg) {
             i32x4 bh[NM], bl[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -664,11 +813,12 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
-                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? gf[ii] : combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? uf[ii] : combine(uh[ii], ul[ii]);
                 }
             }
             gh = gl = uh = ul = zero4;
+            gf = uf = zerof4;
         } else if (c.k == nkg - 1) {
             // This wave's part of the block is done.  No workgroup barrier here
             // (every one would wait for the slowest wave's loads): the wave leaves
@@ -693,11 +843,12 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
-                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? gf[ii] : combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? uf[ii] : combine(uh[ii], ul[ii]);
                 }
             }
             gh = gl = uh = ul = zero4;
+            gf = uf = zerof4;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             int arrived = 0;
             if (lane == 0)
@@ -740,7 +891,21 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             du = cbq >= 0 ? dsl[cbq] : 0.f;
         }
         const int ch = wave * nkd + c.k;
-        if (ch < NCHd) {
+        if (kQ8 && ch < NCHd) {
+            const int slot = max(cbq, 0);
+            i32x4 bq[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) bq[m] = hhi[((ch * 4 + lq) * qc + slot) * NM + m];
+            const float dq = qdh[ch * qc + slot];
+#pragma unroll
+            for (int bb = 0; bb < kNBD; ++bb) {
+                i32x4 a8 = zero4;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) a8 = mma(operand<BITS>(cur[bb], m), bq[m], a8);
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) af[bb][i2] = fmaf(dq, (float)a8[i2], af[bb][i2]);
+            }
+        } else if (!kQ8 && ch < NCHd) {
             const int slot = max(cbq, 0);
             i32x4 bh[NM], bl[NM];
 #pragma unroll
@@ -766,12 +931,18 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) {
                         const int rr = min(bb * 16 + 4 * lq + i2, rd - 1);
-                        tot[bb][i2] += (dsc[cj * rd + rr] * du) * combine(ah[bb][i2], al[bb][i2]);
+                        if (kQ8)
+                            tot[bb][i2] += dsc[cj * rd + rr] * af[bb][i2];
+                        else
+                            tot[bb][i2] += (dsc[cj * rd + rr] * du) * combine(ah[bb][i2], al[bb][i2]);
                     }
                 }
             }
 #pragma unroll
-            for (int bb = 0; bb < kNBD; ++bb) ah[bb] = al[bb] = zero4;
+            for (int bb = 0; bb < kNBD; ++bb) {
+                ah[bb] = al[bb] = zero4;
+                af[bb] = zerof4;
+            }
         }
     };
 
@@ -811,7 +982,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         const int q0 = q * qc, nq = min(A, q0 + qc) - q0;
         if (q == 0) gate.wait(2);     // every workgroup's h is out
         // h rows are assignment indices t * slots + slot (< T * slots; A is fewer under top-p)
-        stage_h<BITS>(f.h, T * slots * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl);
+        stage_h<BITS, kQ8>(f.h, T * slots * I * (int)sizeof(float), I, qrow, qmul, nq, qc, hhi, hlo, qmax, dsl, qdh);
         __syncthreads();
         chunk_first = mw_upper_index(seg, n_act, q0);
         cj = -1;                      // the computing cursor reloads its expert's column map
@@ -946,7 +1117,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     }
 }
 
-template <int BITS, bool kTopP, bool kResid>
+template <int BITS, bool kTopP, bool kResid, bool kQ8>
 __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     constexpr int NM = I8Codec<BITS>::NM;
     extern __shared__ __align__(16) unsigned char dyn[];
@@ -956,6 +1127,8 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     __shared__ unsigned xmax[kCols];
     __shared__ float xu[kCols];
     __shared__ float xinv[kCols];                     // kResid: 1 / rms of each token's x
+    // kQ8: the block scales of the staged x, [chunk][token]
+    __shared__ float qdx[kQ8 ? MOEDEC_MAX_DIM * BITS / 512 * kCols : 1];
 
     const ExpertArgs& a = f.a;
     const int T = a.T, H = a.H, K = a.top_k, S = f.n_shared, E = f.E;
@@ -969,7 +1142,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     // ---- phase 1
     router_rows<kResid>(f, blockIdx.x, gridDim.x, gemv_red, gemv_ssq, xinv);
     gate.settle();
-    stage_x<BITS, kResid>(f.x, H, T, xhi, xlo, xmax, xu, xinv, [&] { gate.count(); });   // x loads out before the count
+    stage_x<BITS, kResid, kQ8>(f.x, H, T, xhi, xlo, xmax, xu, xinv, qdx, [&] { gate.count(); });   // loads, then count
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
@@ -977,7 +1150,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
                                                              f.rsf, f.top_p, r);
 
     // ---- phase 3: the stream
-    stream<BITS, kResid>(f, r, dyn, xu, gate);
+    stream<BITS, kResid, kQ8>(f, r, dyn, xu, qdx, gate);
 
     // Workgroup 0 writes the routing outputs last, from LDS: stores issued
     // earlier would make the compiler wait for the stream's first loads
@@ -1004,10 +1177,13 @@ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 // starts][chunk tables]; the chunk size qc is the largest that fits.
 template <int BITS>
 hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st) {
-    auto k = f.x_out ? (f.top_p < 1.f ? layer_fused_kernel<BITS, true, true> : layer_fused_kernel<BITS, false, true>)
-                     : (f.top_p < 1.f ? layer_fused_kernel<BITS, true, false> : layer_fused_kernel<BITS, false, false>);
-    static size_t static_cache[2][2] = {{0, 0}, {0, 0}};   // each variant's static LDS, read once
-    size_t& static_lds = static_cache[f.top_p < 1.f][f.x_out != nullptr];
+    const bool topp = f.top_p < 1.f, resid = f.x_out != nullptr, q8 = f.act8 != 0;
+    if (q8 && resid) return hipErrorInvalidValue;                   // not instantiated together
+    auto k = q8 ? (topp ? layer_fused_kernel<BITS, true, false, true> : layer_fused_kernel<BITS, false, false, true>)
+        : resid ? (topp ? layer_fused_kernel<BITS, true, true, false> : layer_fused_kernel<BITS, false, true, false>)
+                : (topp ? layer_fused_kernel<BITS, true, false, false> : layer_fused_kernel<BITS, false, false, false>);
+    static size_t static_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};      // each variant's static LDS, read once
+    size_t& static_lds = static_cache[topp][q8 ? 2 : resid ? 1 : 0];
     if (static_lds == 0) {
         hipFuncAttributes attr;
         hipError_t err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k));
@@ -1018,6 +1194,8 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const int H = l.ex.H, I = l.ex.I, T = l.T;
     const int rd = (H + nwg - 1) / nwg;
     if (rd > kNBD * 16) return hipErrorInvalidValue;             // more output rows than a pass holds
+    if (q8 && (H % (512 / BITS) || I % (512 / BITS))) return hipErrorInvalidValue;   // whole activation blocks
+    const int NCHd = ((I * BITS / 8) / 16 + 3) / 4;
     const int A = T * l.ex.slots;
     const int max_active = l.ex.max_active;
     if (static_lds + kLdsOnePerCu > kLdsMax) return hipErrorInvalidValue;
@@ -1045,7 +1223,10 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     };
     auto total = [&](int q) {
         const size_t chunks = (size_t)(A + q - 1) / q;
-        return staging(q) + fixed + align16(((size_t)q * (4 + kCols) + 3 * (chunks + 1)) * sizeof(int));
+        const size_t q8_scales = q8 ? (size_t)q * NCHd : 0;       // the staged h rows' block scales
+        const size_t all_chunks = (size_t)(T * l.ex.slots + q - 1) / q;
+        return staging(q) + fixed +
+               align16(((size_t)q * (4 + kCols) + 3 * ((q8 ? all_chunks : chunks) + 1) + q8_scales) * sizeof(int));
     };
     int qc = A;
     if ((size_t)qc * I > (size_t)kStageV4 * 4 * kMT) qc = kStageV4 * 4 * kMT / I;   // a chunk's h fits registers
@@ -1096,6 +1277,7 @@ hipError_t launch_layer_fused(int bits, const FusedLayerArgs& l, hipStream_t st)
     f.top_p = l.top_p;
     f.x_out = l.x_out;
     f.eps = l.eps;
+    f.act8 = l.act8;
     switch (bits) {
         case 4: return layer_fused_bits<4>(f, l, st);
         case 8: return layer_fused_bits<8>(f, l, st);

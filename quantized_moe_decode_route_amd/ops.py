@@ -64,6 +64,8 @@ for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_layer_fused_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P], _I)
     _SIGS[f"moe_layer_fused_topp_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P],
                                            _I)
+    _SIGS[f"moe_layer_fused_act8_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P],
+                                           _I)
     _SIGS[f"moe_layer_fused_resid_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P], _I)
 
@@ -346,10 +348,11 @@ def fused_supported(T: int, ex: Experts) -> bool:
 
 def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
                 topk_group: int, top_k: int, rsf: float, buf: LayerBuffers, top_p: float | None = None,
-                x_out: torch.Tensor | None = None, eps: float = 1e-6) -> LayerBuffers:
+                x_out: torch.Tensor | None = None, eps: float = 1e-6, act8: bool = False) -> LayerBuffers:
     """moe_layer_fused_q{bits} (moe_layer_fused_topp_q{bits} when top_p is
     given): the whole layer in one launch (outputs in buf).  With x_out:
-    moe_layer_fused_resid_q{bits}, x_out = x + MoE(rmsnorm(x)) (x_out may be x)."""
+    moe_layer_fused_resid_q{bits}, x_out = x + MoE(rmsnorm(x)) (x_out may be x).
+    act8: moe_layer_fused_act8_q{bits} (Q8_0-style int8 activations)."""
     T, H = x.shape
     E = ex.n_experts
     if router_w.shape != (E, H) or bias.shape != (E,) or H != ex.hidden:
@@ -359,7 +362,12 @@ def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex:
             buf.h.shape != (T * (top_k + ex.n_shared), ex.inter) or buf.workspace.numel() < FUSED_WORKSPACE_INTS:
         raise ValueError("buffers do not match the call's shapes")
     s_ex, s_wl = ex.struct(), r.worklist.struct()
-    if x_out is not None:
+    if act8:
+        if x_out is not None:
+            raise ValueError("the int8-activation call has no residual form")
+        name = f"moe_layer_fused_act8_{_suffix(ex.bits)}"
+        pre = (float(rsf), 1.0 if top_p is None else float(top_p))
+    elif x_out is not None:
         if x_out.shape != (T, H):
             raise ValueError("x_out must be [T, hidden]")
         name = f"moe_layer_fused_resid_{_suffix(ex.bits)}"
@@ -380,13 +388,16 @@ def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex:
 
 def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
               topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None,
-              fused: bool | None = None, top_p: float | None = None) -> LayerBuffers:
+              fused: bool | None = None, top_p: float | None = None, act8: bool = False) -> LayerBuffers:
     """One layer on x's stream; returns the buffers (y in .y).  fused=None takes
     the single-launch path where its limits allow, else route_topk ->
     gate_up_silu -> down_combine; True / False force one of them."""
     T = x.shape[0]
     if buf is None:
         buf = LayerBuffers.allocate(T, ex.hidden, ex.inter, ex.n_experts, top_k, ex.n_shared, x.device)
+    if act8:                        # only the fused call has int8 activations
+        return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
+                           buf=buf, top_p=top_p, act8=True)
     if fused is None:
         if fused_supported(T, ex):
             try:

@@ -45,7 +45,8 @@ def experts_dev(cfg, lay) -> ops.Experts:
     return ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits)
 
 
-def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None, top_p: float | None = None) -> dict:
+def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None, top_p: float | None = None,
+              act8: bool = False) -> dict:
     """One layer on the GPU (fused: the single-launch call; False: route +
     gate/up + down; None: whichever moe_layer picks; top_p: the adaptive
     top-p calls); results on the host."""
@@ -54,9 +55,9 @@ def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None, top_p: float |
     ex = experts_dev(cfg, lay)
     try:
         buf = ops.moe_layer(xt, lay["router_w"], lay["bias"], ex, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                            top_k=cfg.top_k, rsf=cfg.rsf, fused=fused, top_p=top_p)
+                            top_k=cfg.top_k, rsf=cfg.rsf, fused=fused, top_p=top_p, act8=act8)
     except ops.MoedecError as err:
-        if fused and err.status == ops.MOEDEC_ERR_UNSUPPORTED:
+        if (fused or act8) and err.status == ops.MOEDEC_ERR_UNSUPPORTED:
             pytest.skip("the activations of this batch do not fit the fused call's LDS plan")
         raise
     torch.cuda.synchronize()
@@ -67,7 +68,7 @@ def run_layer(cfg, lay, x: np.ndarray, fused: bool | None = None, top_p: float |
     return dict(scores=buf.route.scores.cpu().numpy(), idx=buf.route.topk_idx.cpu().numpy(),
                 w=buf.route.topk_w.cpu().numpy(), n_active=n, expert_id=wl.expert_id[:n].cpu().numpy(),
                 seg=seg, assign=wl.assign[:int(seg[-1])].cpu().numpy(), h=buf.h.cpu().numpy(),
-                y=buf.y.cpu().numpy(), top_p=top_p)
+                y=buf.y.cpu().numpy(), top_p=top_p, act8=act8)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
@@ -79,10 +80,10 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def oracle_layer(cfg, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray, expert_fn,
-                 top_p: float | None = None) -> orc.LayerResult:
+                 top_p: float | None = None, act8: bool = False) -> orc.LayerResult:
     return orc.moe_layer(x, router_w, bias, expert_fn, n_group=cfg.n_group, topk_group=cfg.topk_group,
                          top_k=cfg.top_k, n_shared=cfg.n_shared, rsf=cfg.rsf, bits=cfg.bits,
-                         top_p=1.0 if top_p is None else top_p)
+                         top_p=1.0 if top_p is None else top_p, act8=act8)
 
 
 def check_routing(cfg, g: dict, r: orc.LayerResult, bias: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -131,7 +132,7 @@ def check_layer(cfg, g: dict, r: orc.LayerResult, set_ok: np.ndarray, order_ok: 
 
 
 def check_all(cfg, g: dict, x, router_w, bias, expert_fn) -> orc.LayerResult:
-    r = oracle_layer(cfg, x, router_w, bias, expert_fn, g.get("top_p"))
+    r = oracle_layer(cfg, x, router_w, bias, expert_fn, g.get("top_p"), g.get("act8", False))
     set_ok, order_ok = check_routing(cfg, g, r, bias)
     check_layer(cfg, g, r, set_ok, order_ok)
     return r

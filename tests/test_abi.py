@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 32
+    assert len(names) == 35
     for n in names:
         assert hasattr(lib, n), n
 
@@ -139,6 +139,9 @@ def test_fused_resid_and_topp_reject(lib, suffix):
     assert resid(*head, 1.0, math.inf, FAKE, *tail) == 1
     assert resid(*head, math.nan, 1e-6, FAKE, *tail) == 1            # NaN top_p
     assert topp(*head, math.nan, *tail) == 1
+    act8 = getattr(lib, f"moe_layer_fused_act8_{suffix}")
+    assert act8(*head, math.nan, *tail) == 1                          # NaN top_p
+    assert act8(FAKE, FAKE, FAKE, None, 1, 4, 2, 4, 2.5, 1.0, *tail) == 1   # no experts
 
 
 def test_fused_call_requires_structs(lib):
