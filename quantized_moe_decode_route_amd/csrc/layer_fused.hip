@@ -63,6 +63,7 @@ constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a co
 constexpr int kStreamW = 3;                             // stream items in flight per wave (3 measured best)
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
 constexpr int kStageX4 = 4;                             // float4 of x a thread holds at once
+constexpr int kShPref = 8;                              // K-chunks of the shared tile a prefetching wave holds
 constexpr size_t kDeferLds = 48 * 1024;                 // partial sums of all gate/up blocks at most
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
@@ -93,10 +94,12 @@ struct FusedArgs {
     int E, n_group, topk_group, n_shared;
     float rsf, top_p, eps;
     int act8;                      // 1: Q8_0-style int8 activations (block scales) instead of int16
+    int shp;                       // 1: the shared experts' gate/up rows are fetched during routing
     int qc;                        // assignments staged at once for down
     int rb;                        // gate/up blocks whose partial sums LDS holds at once
     int deferred;                  // 1: every block has its own slot and is finalised after the segment
     int off_gured, off_gsc, off_dsc, off_pairs, off_chunk, off_hprod;   // dynamic LDS layout (bytes)
+    int off_shpart;                                                     // shp: the shared tile's partial sums
 };
 
 // Workgroup barrier for LDS only: loads in flight to registers stay in flight.
@@ -604,9 +607,56 @@ __device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
 // computed against zero activations.  Every load is issued at a clamped
 // (valid) address, so every item issues exactly two loads and the wait
 // counts before each use are static.
+// The shared experts (always active, known before routing) need not wait for
+// it: with shp, workgroup b takes the pairs [b*SP/nwg, (b+1)*SP/nwg) of the
+// SP = S*I (gate row, up row) pairs, at most 8, as one 16-row tile -- rows
+// 0-7 the pairs' gate rows, rows 8-15 their up rows -- and the waves that
+// neither route a token nor poll the grid counters (waves T .. kMW-2) load
+// its K-chunks, kShPref each, right after staging x.  Those waves issue no
+// other loads before the stream, so the loads stay in flight through the
+// routing; the tile is multiplied once the routing is done.
+struct SharedTile {
+    uint4 pref[kShPref];
+    float scale;                   // first prefetching wave, lanes 0-15: the tile's gate (0-7) / up row scale
+    int pw;                        // this wave's index among the prefetching waves, or -1
+};
+
+__device__ __forceinline__ void shared_pairs(int S, int I, int& p0, int& np) {
+    const long long SP = (long long)S * I;
+    p0 = (int)(SP * blockIdx.x / gridDim.x);
+    np = (int)(SP * (blockIdx.x + 1) / gridDim.x) - p0;
+}
+
+template <int BITS>
+__device__ __forceinline__ void shared_prefetch(const FusedArgs& f, SharedTile& st) {
+    const ExpertArgs& a = f.a;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int ln = lane & 15, lq = lane >> 4;
+    const int T = a.T, I = a.I, H = a.H;
+    st.pw = (wave >= T && wave < kMW - 1) ? wave - T : -1;
+    if (st.pw < 0) return;
+    int p0, np;
+    shared_pairs(f.n_shared, I, p0, np);
+    const int pair = p0 + min(ln & 7, max(np - 1, 0));          // spare rows repeat a real one
+    const int j = pair / I, row = pair - j * I;
+    const size_t rbg = (size_t)H * BITS / 8;
+    const uint8_t* base = (ln < 8 ? a.w_gate : a.w_up) + ((size_t)(f.E + j) * I + row) * rbg;
+    const int Pg = (int)(rbg >> 4), NCHg = (Pg + 3) >> 2;
+#pragma unroll
+    for (int k = 0; k < kShPref; ++k) {
+        const int ch = min(st.pw * kShPref + k, NCHg - 1);
+        const int grp = min(ch * 4 + lq, Pg - 1);
+        st.pref[k] = ld16(base + (size_t)grp * 16);
+    }
+    if (st.pw == 0 && lane < 16) {
+        const size_t src = (size_t)(f.E + j) * I + row;            // lane l < 16 has pair p0 + min(l & 7, np - 1)
+        st.scale = lane < 8 ? a.s_gate[src] : a.s_up[src];
+    }
+}
+
 template <int BITS, bool kResid, bool kQ8>
 __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, const float* xu,
-                                       const float* qdx, GridGate& gate) {
+                                       const float* qdx, GridGate& gate, const SharedTile& shtile) {
     using C = I8Codec<BITS>;
     constexpr int NM = C::NM;
     constexpr int W = kStreamW;
@@ -627,7 +677,8 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     // blocks; a block may hold rows of two experts: B carries every token,
     // and each row keeps only the columns of tokens routed to its expert
     const int rbg = H * BITS / 8, Pg = rbg >> 4, NCHg = (Pg + 3) >> 2, nkg = (NCHg + kMW - 1) / kMW;
-    const long long NRT = (long long)n_act * I;
+    const int n_gu = f.shp ? n_act - f.n_shared : n_act;       // experts in the gate/up stretch
+    const long long NRT = (long long)n_gu * I;
     const int g0 = (int)(NRT * b / nwg);
     const int NR = (int)(NRT * (b + 1) / nwg) - g0;
     const int nbg = (NR + 15) >> 4;
@@ -649,6 +700,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     int* slot_done = slot_cnt + rb;
     float* gsc = reinterpret_cast<float*>(dyn + f.off_gsc);       // [NR][2]: gate, up row scales
     float* hprod = reinterpret_cast<float*>(dyn + f.off_hprod);   // [NR][T]: this workgroup's h
+    float* shpart = reinterpret_cast<float*>(dyn + f.off_shpart); // shp: [prefetching wave][16][T] + 16 scales
     float* dsc = reinterpret_cast<float*>(dyn + f.off_dsc);       // [n_act][rd]
     int* pstart = reinterpret_cast<int*>(dyn + f.off_pairs);      // [n_act + 1]
     int* qrow = reinterpret_cast<int*>(dyn + f.off_chunk);        // [qc]
@@ -1009,6 +1061,43 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     __builtin_amdgcn_s_waitcnt(0);
     if (early) fill();
 
+    // shp: multiply the prefetched shared tile (its loads are complete: the
+    // wait above) while the ring's loads are in flight; partial sums to LDS
+    const int npw = kMW - 1 - T;                                   // prefetching waves
+    float* ssc = shpart + (size_t)kMW * 16 * T;                    // the tile's 8 gate and 8 up row scales
+    int sh_p0 = 0, sh_np = 0;
+    if (f.shp) {
+        shared_pairs(f.n_shared, I, sh_p0, sh_np);
+        if (shtile.pw >= 0) {
+            i32x4 sh = zero4, sl = zero4;
+#pragma unroll
+            for (int k = 0; k < kShPref; ++k) {
+                const int ch = shtile.pw * kShPref + k;
+                if (ch < NCHg) {
+                    i32x4 bh[NM], bl[NM];
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        const int src = ((ch * 4 + lq) * T + tcol) * NM + m;
+                        bh[m] = xhi[src];
+                        bl[m] = xlo[src];
+                    }
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        const i32x4 av = operand<BITS>(shtile.pref[k], m);
+                        sh = mma(av, bh[m], sh);
+                        sl = mma(av, bl[m], sl);
+                    }
+                }
+            }
+            if (ln < T) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    shpart[(shtile.pw * 16 + 4 * lq + ii) * T + ln] = combine(sh[ii], sl[ii]);
+            }
+            if (shtile.pw == 0 && lane < 16) ssc[lane] = shtile.scale;
+        }
+    }
+
     // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc
     block_prefix(n_act, [&](int j) { return (seg[j + 1] - 1) / qc - seg[j] / qc + 1; }, pstart);
     if (threadIdx.x == 0) {
@@ -1025,6 +1114,23 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         ctab[3 * nchunk] = run;
     }
     __syncthreads();
+    // shp: h of the shared pairs (every workgroup, whatever else it has to
+    // do), straight to global memory with device-scope stores, which complete
+    // before this workgroup's h-exchange arrival
+    if (f.shp) {
+        for (int idx = threadIdx.x; idx < sh_np * T; idx += kMT) {
+            const int i = idx / T, t = idx - i * T;
+            float gs = 0.f, vs = 0.f;
+            for (int w = 0; w < npw; ++w) {
+                gs += shpart[(w * 16 + i) * T + t];
+                vs += shpart[(w * 16 + 8 + i) * T + t];
+            }
+            const float gv = gs * xu[t] * ssc[i];
+            const float uv = vs * xu[t] * ssc[8 + i];
+            const int pair = sh_p0 + i, j = pair / I, row = pair - j * I;
+            store_device(f.h + (size_t)(t * slots + K + j) * I + row, gv / (1.0f + __expf(-gv)) * uv);
+        }
+    }
     const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
     if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
     if (Np == 0) return;
@@ -1143,6 +1249,9 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     router_rows<kResid>(f, blockIdx.x, gridDim.x, gemv_red, gemv_ssq, xinv);
     gate.settle();
     stage_x<BITS, kResid, kQ8>(f.x, H, T, xhi, xlo, xmax, xu, xinv, qdx, [&] { gate.count(); });   // loads, then count
+    SharedTile shtile;
+    shtile.pw = -1;
+    if (!kQ8 && f.shp) shared_prefetch<BITS>(f, shtile);   // in flight through the routing
     gate.wait(1);
 
     // ---- phase 2: routing (every workgroup, identically)
@@ -1150,7 +1259,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
                                                              f.rsf, f.top_p, r);
 
     // ---- phase 3: the stream
-    stream<BITS, kResid, kQ8>(f, r, dyn, xu, qdx, gate);
+    stream<BITS, kResid, kQ8>(f, r, dyn, xu, qdx, gate, shtile);
 
     // Workgroup 0 writes the routing outputs last, from LDS: stores issued
     // earlier would make the compiler wait for the stream's first loads
@@ -1214,7 +1323,12 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const size_t dsc = align16((size_t)max_active * rd * sizeof(float));
     const size_t pairs = align16((size_t)(max_active + 1) * sizeof(int));
     const size_t hprod = align16((size_t)nr_max * T * sizeof(float));
-    const size_t fixed = gured + gsc + dsc + pairs + hprod;
+    // the shared tile during routing: free waves to load it, whole pairs per workgroup
+    const int NCHg = ((H * BITS / 8) / 16 + 3) / 4;
+    const bool shp = !q8 && l.n_shared >= 1 && T <= kMW - 2 && (long long)l.n_shared * I <= 8LL * nwg &&
+                     (kMW - 1 - T) * kShPref >= NCHg;
+    const size_t shpart = shp ? align16(((size_t)kMW * 16 * T + 16) * sizeof(float)) : 0;
+    const size_t fixed = gured + gsc + dsc + pairs + hprod + shpart;
     auto staging = [&](int q) {
         size_t s = align16(staged_row_bytes_i8<BITS>(I) * q);
         if (s < x_bytes) s = x_bytes;
@@ -1241,6 +1355,8 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     f.off_dsc = (int)(stg + gured + gsc);
     f.off_pairs = (int)(stg + gured + gsc + dsc);
     f.off_hprod = (int)(stg + gured + gsc + dsc + pairs);
+    f.off_shpart = (int)(stg + gured + gsc + dsc + pairs + hprod);
+    f.shp = shp ? 1 : 0;
     f.off_chunk = (int)(stg + fixed);
     size_t lds = total(qc);
     if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
