@@ -64,6 +64,7 @@ constexpr int kStreamW = 3;                             // stream items in fligh
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
 constexpr int kStageX4 = 4;                             // float4 of x a thread holds at once
 constexpr int kShPref = 8;                              // K-chunks of the shared tile a prefetching wave holds
+constexpr int kScaleRegs = 2;                           // row scales a thread fetches early (per kind)
 constexpr size_t kDeferLds = 48 * 1024;                 // partial sums of all gate/up blocks at most
 constexpr int kBufWord3 = 0x00020000;                   // raw buffer resource: 32-bit data format
 constexpr int kCoherent = 16;                           // buffer load cache policy: device-coherent (sc1)
@@ -1059,10 +1060,10 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     // loads); saying so here keeps later register reuse from waiting for
     // the ring's loads.
     __builtin_amdgcn_s_waitcnt(0);
-    if (early) fill();
 
     // shp: multiply the prefetched shared tile (its loads are complete: the
-    // wait above) while the ring's loads are in flight; partial sums to LDS
+    // wait above; only the waves that loaded it work here, the others go on
+    // to issue the ring at once); partial sums to LDS
     const int npw = kMW - 1 - T;                                   // prefetching waves
     float* ssc = shpart + (size_t)kMW * 16 * T;                    // the tile's 8 gate and 8 up row scales
     int sh_p0 = 0, sh_np = 0;
@@ -1095,6 +1096,30 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                     shpart[(shtile.pw * 16 + 4 * lq + ii) * T + ln] = combine(sh[ii], sl[ii]);
             }
             if (shtile.pw == 0 && lane < 16) ssc[lane] = shtile.scale;
+        }
+    }
+    if (early) fill();
+    // The row scales of this workgroup's gate/up rows and down rows, into
+    // registers now (their loads queue right behind the ring's), to LDS just
+    // before the stream starts: kScaleRegs per thread, the rest loaded there.
+    float gs_r[kScaleRegs], us_r[kScaleRegs], ds_r[kScaleRegs];
+    const int n_dsc = n_act * rd;
+    if (NR > 0) {
+#pragma unroll
+        for (int u = 0; u < kScaleRegs; ++u) {
+            const int i = min((int)threadIdx.x + u * kMT, NR - 1);
+            const int g = g0 + i, j = g / I;
+            const size_t src = (size_t)eid[j] * I + (g - j * I);
+            gs_r[u] = a.s_gate[src];
+            us_r[u] = a.s_up[src];
+        }
+    }
+    if (n_dsc > 0) {
+#pragma unroll
+        for (int u = 0; u < kScaleRegs; ++u) {
+            const int i = min((int)threadIdx.x + u * kMT, n_dsc - 1);
+            const int j = i / rd, rr = i - j * rd;
+            ds_r[u] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
         }
     }
 
@@ -1137,17 +1162,26 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     if (nchunk > 0) dn_prep(0);       // while the ring's first loads are in flight
     if (!early) fill();
     for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
-    // Row scales of every active expert for this workgroup's rows, to LDS:
-    // loaded after the ring is filled, so their latency overlaps the ring's
-    // (the first items wait for the ring anyway).
+    // Row scales of every active expert for this workgroup's rows, to LDS
+    // (fetched right after the ring fill; the first items wait for the ring
+    // anyway, and the scales' loads retire right behind it).
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = threadIdx.x; i < NR; i += kMT) {
+#pragma unroll
+    for (int u = 0; u < kScaleRegs; ++u) {
+        const int i = (int)threadIdx.x + u * kMT;
+        if (i < NR) {
+            gsc[i * 2 + 0] = gs_r[u];
+            gsc[i * 2 + 1] = us_r[u];
+        }
+        if (i < n_dsc) dsc[i] = ds_r[u];
+    }
+    for (int i = threadIdx.x + kScaleRegs * kMT; i < NR; i += kMT) {
         const int g = g0 + i, j = g / I;
         const size_t src = (size_t)eid[j] * I + (g - j * I);
         gsc[i * 2 + 0] = a.s_gate[src];
         gsc[i * 2 + 1] = a.s_up[src];
     }
-    for (int i = threadIdx.x; i < n_act * rd; i += kMT) {
+    for (int i = threadIdx.x + kScaleRegs * kMT; i < n_dsc; i += kMT) {
         const int j = i / rd, rr = i - j * rd;
         dsc[i] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
     }
