@@ -573,32 +573,6 @@ __device__ __forceinline__ void stage_h(const float* h, int h_bytes, int I, cons
     zero_pad<BITS>(P, (P + 3) / 4, n, ldn, hi, lo);
 }
 
-// Exclusive prefix over j < n of cnt(j) into out[0..n] (out[n] = total).
-template <typename Cnt>
-__device__ __forceinline__ void block_prefix(int n, Cnt cnt, int* out) {
-    __shared__ int wtot[kMW];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int per = (n + 1 + kMT - 1) / kMT;
-    const int j0 = threadIdx.x * per, j1 = min(j0 + per, n);
-    int local = 0;
-    for (int j = j0; j < j1; ++j) local += cnt(j);
-    int inc = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int u = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += u;
-    }
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    int run = inc - local;
-    for (int w = 0; w < wave; ++w) run += wtot[w];
-    for (int j = j0; j < min(j0 + per, n + 1); ++j) {
-        out[j] = run;
-        if (j < n) run += cnt(j);
-    }
-    __syncthreads();
-}
-
 // Phase 3 (see the file comment).  Items of a wave, all waves alike:
 //   gate/up: for each active expert j, each 16-row block of this workgroup's
 //            rows, each of the wave's K-chunks -> loads of gate and up;
@@ -1031,7 +1005,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     };
     auto dn_stage = [&](int q) {
         lds_barrier();                // everyone is done with the previous chunk
-        if (q > 0) dn_prep(q);        // chunk 0's tables were built during the setup
+        dn_prep(q);                   // chunk 0's: after this workgroup's h is out, during the exchange
         const int q0 = q * qc, nq = min(A, q0 + qc) - q0;
         if (q == 0) gate.wait(2);     // every workgroup's h is out
         // h rows are assignment indices t * slots + slot (< T * slots; A is fewer under top-p)
@@ -1123,26 +1097,46 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         }
     }
 
-    // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc
-    block_prefix(n_act, [&](int j) { return (seg[j + 1] - 1) / qc - seg[j] / qc + 1; }, pstart);
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int q = 0; q < nchunk; ++q) {
-            const int jf = mw_upper_index(seg, n_act, q * qc);
-            const int jl = mw_upper_index(seg, n_act, min(A, (q + 1) * qc) - 1);
-            const int p0 = pstart[jf] + (q - seg[jf] / qc), p1 = pstart[jl] + (q - seg[jl] / qc);
-            ctab[3 * q] = run;                        // first position (after Gpad)
-            ctab[3 * q + 1] = (p1 - p0 + 1) * nkd;    // items
-            ctab[3 * q + 2] = p0;                     // first pair
-            run += (ctab[3 * q + 1] + W - 1) / W * W;
+    // (expert, chunk) pairs: expert j spans chunks seg[j]/qc .. (seg[j+1]-1)/qc.
+    // The pair starts and the chunk table are built by the last wave alone
+    // (it polls the grid counters and has no other work here), so the only
+    // barrier before the stream is the one that publishes them.
+    if (wave == kMW - 1) {
+        int carry = 0;
+        for (int j0 = 0; j0 <= n_act; j0 += kWave) {       // pstart[0 .. n_act], exclusive
+            const int j = j0 + lane;
+            const int cnt = j < n_act ? (seg[j + 1] - 1) / qc - seg[j] / qc + 1 : 0;
+            int inc = cnt;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int u = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += u;
+            }
+            if (j <= n_act) pstart[j] = carry + inc - cnt;
+            carry += __shfl(inc, kWave - 1, kWave);
         }
-        ctab[3 * nchunk] = run;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane == 0) {
+            int run = 0;
+            for (int q = 0; q < nchunk; ++q) {
+                const int jf = mw_upper_index(seg, n_act, q * qc);
+                const int jl = mw_upper_index(seg, n_act, min(A, (q + 1) * qc) - 1);
+                const int p0 = pstart[jf] + (q - seg[jf] / qc), p1 = pstart[jl] + (q - seg[jl] / qc);
+                ctab[3 * q] = run;                        // first position (after Gpad)
+                ctab[3 * q + 1] = (p1 - p0 + 1) * nkd;    // items
+                ctab[3 * q + 2] = p0;                     // first pair
+                run += (ctab[3 * q + 1] + W - 1) / W * W;
+            }
+            ctab[3 * nchunk] = run;
+        }
     }
     __syncthreads();
-    // shp: h of the shared pairs (every workgroup, whatever else it has to
-    // do), straight to global memory with device-scope stores, which complete
-    // before this workgroup's h-exchange arrival
-    if (f.shp) {
+    // shp: h of the shared pairs, straight to global memory with device-scope
+    // stores, which complete before this workgroup's h-exchange arrival
+    auto shared_finalize = [&]() {
+        if (!f.shp) return;
         for (int idx = threadIdx.x; idx < sh_np * T; idx += kMT) {
             const int i = idx / T, t = idx - i * T;
             float gs = 0.f, vs = 0.f;
@@ -1155,37 +1149,43 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             const int pair = sh_p0 + i, j = pair / I, row = pair - j * I;
             store_device(f.h + (size_t)(t * slots + K + j) * I + row, gv / (1.0f + __expf(-gv)) * uv);
         }
-    }
-    const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
-    if (Ngu == 0) gate.arrive();      // no h of ours: counted as done at once
-    if (Np == 0) return;
-    if (nchunk > 0) dn_prep(0);       // while the ring's first loads are in flight
-    if (!early) fill();
-    for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
-    // Row scales of every active expert for this workgroup's rows, to LDS
-    // (fetched right after the ring fill; the first items wait for the ring
-    // anyway, and the scales' loads retire right behind it).
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    // The row scales to LDS, from the registers (and past kScaleRegs per
+    // thread, loaded here): gate/up ones before the stream when the blocks
+    // are finalised in it, else, and the down ones always, after it.
+    auto scales_to_lds = [&](bool gu, bool dn) {
 #pragma unroll
-    for (int u = 0; u < kScaleRegs; ++u) {
-        const int i = (int)threadIdx.x + u * kMT;
-        if (i < NR) {
-            gsc[i * 2 + 0] = gs_r[u];
-            gsc[i * 2 + 1] = us_r[u];
+        for (int u = 0; u < kScaleRegs; ++u) {
+            const int i = (int)threadIdx.x + u * kMT;
+            if (gu && i < NR) {
+                gsc[i * 2 + 0] = gs_r[u];
+                gsc[i * 2 + 1] = us_r[u];
+            }
+            if (dn && i < n_dsc) dsc[i] = ds_r[u];
         }
-        if (i < n_dsc) dsc[i] = ds_r[u];
+        for (int i = threadIdx.x + kScaleRegs * kMT; gu && i < NR; i += kMT) {
+            const int g = g0 + i, j = g / I;
+            const size_t src = (size_t)eid[j] * I + (g - j * I);
+            gsc[i * 2 + 0] = a.s_gate[src];
+            gsc[i * 2 + 1] = a.s_up[src];
+        }
+        for (int i = threadIdx.x + kScaleRegs * kMT; dn && i < n_dsc; i += kMT) {
+            const int j = i / rd, rr = i - j * rd;
+            dsc[i] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
+        }
+    };
+    const int Np = Gpad + (nchunk > 0 ? ctab[3 * nchunk] : 0);
+    if (Ngu == 0) {                   // no gate/up rows here: the shared pairs' h, then counted as done
+        shared_finalize();
+        gate.arrive();
     }
-    for (int i = threadIdx.x + kScaleRegs * kMT; i < NR; i += kMT) {
-        const int g = g0 + i, j = g / I;
-        const size_t src = (size_t)eid[j] * I + (g - j * I);
-        gsc[i * 2 + 0] = a.s_gate[src];
-        gsc[i * 2 + 1] = a.s_up[src];
+    if (Np == 0) return;
+    if (!early) fill();
+    if (!f.deferred) {                // blocks finalised in the stream need their counters and scales now
+        for (int i = threadIdx.x; i < 2 * rb; i += kMT) slot_cnt[i] = 0;
+        scales_to_lds(true, false);
+        __syncthreads();
     }
-    for (int i = threadIdx.x + kScaleRegs * kMT; i < n_dsc; i += kMT) {
-        const int j = i / rd, rr = i - j * rd;
-        dsc[i] = a.s_down[(size_t)eid[j] * H + dr0 + rr];
-    }
-    __syncthreads();
     // gate/up segment, then the down chunks: two loops, so each hot loop holds
     // one kind of item (the ring and both cursors carry over, Gpad % W == 0)
     for (int base = 0; base < Gpad; base += W) {
@@ -1198,6 +1198,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             advance(cc_);
         }
     }
+    scales_to_lds(f.deferred != 0, true);
     __syncthreads();                  // every block's partial sums are in (and, ring slots: finalised)
     if (f.deferred) {                 // h = silu(g) * v of every row and routed token, in parallel
         for (int idx = threadIdx.x; idx < NR * T; idx += kMT) {
@@ -1221,7 +1222,10 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
         }
         __syncthreads();
     }
-    if (Ngu > 0) flush_h();
+    if (Ngu > 0) {
+        shared_finalize();
+        flush_h();
+    }
     cj = -1;
     int next_chunk = 0;
     for (int base = Gpad; base < Np; base += W) {
