@@ -184,6 +184,28 @@ int moe_expert_down_combine_q2(const float* h, const moedec_experts* ex, const m
                                const float* topk_w, int T, int top_k, float* y, void* stream);
 
 /*
+ * moe_expert_down_combine in expert-major order, for larger batches (the
+ * same result up to the order of the fp32 sums): each expert's down rows are
+ * streamed with only that expert's assignments' h staged (rather than every
+ * row range with the whole batch's h), each assignment's partial output is
+ * written to part, and a second kernel adds them per token in slot order.
+ *   part     : fp32 [T*(top_k+S), hidden] scratch the caller owns (every row
+ *              of an assignment is overwritten; nothing is read back later)
+ *   topk_idx : int32 [T, top_k] from the router, or NULL when every slot has
+ *              an assignment; slots with index -1 (top-p) are skipped
+ * Other arguments, layouts and errors as for moe_expert_down_combine_q*.
+ */
+int moe_expert_down_combine_em_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                  const float* topk_w, const int32_t* topk_idx, int T, int top_k, float* part,
+                                  float* y, void* stream);
+int moe_expert_down_combine_em_q8(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                  const float* topk_w, const int32_t* topk_idx, int T, int top_k, float* part,
+                                  float* y, void* stream);
+int moe_expert_down_combine_em_q2(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                  const float* topk_w, const int32_t* topk_idx, int T, int top_k, float* part,
+                                  float* y, void* stream);
+
+/*
  * The whole layer step in one launch: moe_route_topk (with the worklist),
  * then the gate/up and down calls, fused (same passages as those three calls;
  * Show HN page, "implemented features").  Arguments and outputs are those of

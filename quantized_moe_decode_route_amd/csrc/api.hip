@@ -80,6 +80,16 @@ int down(int bits, const float* h, const moedec_experts* ex, const moedec_workli
     return device_status(launch_down(bits, h, topk_w, a, y, static_cast<hipStream_t>(stream)));
 }
 
+int down_em(int bits, const float* h, const moedec_experts* ex, const moedec_worklist* wl, const float* topk_w,
+            const int32_t* topk_idx, int T, int top_k, float* part, float* y, void* stream) {
+    if (!h || !topk_w || !y || !part) return MOEDEC_ERR_INVALID_ARG;
+    ExpertArgs a;
+    const int st = check_experts(ex, wl, bits, T, top_k, a);
+    if (st != MOEDEC_OK) return st;
+    if (!aligned16(h)) return MOEDEC_ERR_INVALID_ARG;
+    return device_status(launch_down_em(bits, h, topk_w, topk_idx, a, part, y, static_cast<hipStream_t>(stream)));
+}
+
 int route_args_ok(int T, int H, int E, int n_group, int topk_group, int top_k, int n_shared, float rsf) {
     if (T < 1 || H < 4 || H % 4 || E < 2 || n_group < 1 || E % n_group || E / n_group < 2)
         return MOEDEC_ERR_INVALID_ARG;
@@ -222,13 +232,28 @@ MOEDEC_API int moe_expert_gate_up_silu_q2(const float* x, const moedec_experts* 
     return gate_up(2, x, ex, wl, T, top_k, h, stream);
 }
 
+MOEDEC_API int moe_expert_down_combine_em_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                             const float* topk_w, const int32_t* topk_idx, int T, int top_k,
+                                             float* part, float* y, void* stream) {
+    return down_em(4, h, ex, wl, topk_w, topk_idx, T, top_k, part, y, stream);
+}
 MOEDEC_API int moe_expert_down_combine_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
                                           const float* topk_w, int T, int top_k, float* y, void* stream) {
     return down(4, h, ex, wl, topk_w, T, top_k, y, stream);
 }
+MOEDEC_API int moe_expert_down_combine_em_q8(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                             const float* topk_w, const int32_t* topk_idx, int T, int top_k,
+                                             float* part, float* y, void* stream) {
+    return down_em(8, h, ex, wl, topk_w, topk_idx, T, top_k, part, y, stream);
+}
 MOEDEC_API int moe_expert_down_combine_q8(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
                                           const float* topk_w, int T, int top_k, float* y, void* stream) {
     return down(8, h, ex, wl, topk_w, T, top_k, y, stream);
+}
+MOEDEC_API int moe_expert_down_combine_em_q2(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                             const float* topk_w, const int32_t* topk_idx, int T, int top_k,
+                                             float* part, float* y, void* stream) {
+    return down_em(2, h, ex, wl, topk_w, topk_idx, T, top_k, part, y, stream);
 }
 MOEDEC_API int moe_expert_down_combine_q2(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
                                           const float* topk_w, int T, int top_k, float* y, void* stream) {

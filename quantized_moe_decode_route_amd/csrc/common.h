@@ -187,6 +187,8 @@ hipError_t launch_gate_up_valu(int bits, const float* x, const ExpertArgs& a, fl
 hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                             hipStream_t stream);
 
+hipError_t launch_down_em(int bits, const float* h, const float* topk_w, const int32_t* topk_idx, const ExpertArgs& a,
+                          float* part, float* y, hipStream_t stream);
 hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                        hipStream_t stream);
 

@@ -50,6 +50,60 @@ __global__ __launch_bounds__(kMT) void down_mfma_kernel(const float* __restrict_
     down_rows<BITS>(h, topk_w, a, y, r0, r1, qc, dyn, eid, seg, a.assign, n_act, scratch, gate);
 }
 
+// Down, expert-major: this workgroup's share of the (segment, row) units, each
+// segment staging only its own assignments' h; partial outputs to part.
+template <int BITS>
+__global__ __launch_bounds__(kMT) void down_em_kernel(const float* __restrict__ h, const float* __restrict__ topk_w,
+                                                      const ExpertArgs a, float* __restrict__ part, int ns) {
+    constexpr int NCALL = MfmaCodec<BITS>::NCALL;
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ int eid[kMaxActive];
+    __shared__ int seg[kMaxActive + 1];
+    __shared__ DownEmLds s;
+    const int NCH = ((a.I * BITS / 8) / 16 + 3) / 4;
+    half8* hhi = reinterpret_cast<half8*>(dyn);
+    half8* hlo = hhi + (size_t)NCH * 4 * ns * NCALL;
+    float* red = reinterpret_cast<float*>(hlo + (size_t)NCH * 4 * ns * NCALL);
+    const int n_act = mw_load_worklist(a, eid, seg);
+    down_em_units<BITS>(a, h, topk_w, part, eid, seg, a.assign, n_act, ns, blockIdx.x, gridDim.x, hhi, hlo, red, s);
+}
+
+// y[t][r] = sum over token t's slots, in slot order, of part[t*slots + slot][r]
+// (routed slots without an expert -- dropped by top-p -- skipped).
+__global__ __launch_bounds__(256) void down_reduce_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ topk_idx, int T, int H, int K,
+                                                          int slots, float* __restrict__ y) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)T * H) return;
+    const int t = (int)(i / H), r = (int)(i - (long long)t * H);
+    float acc = 0.f;
+    for (int sl = 0; sl < slots; ++sl)
+        if (sl >= K || topk_idx == nullptr || topk_idx[t * K + sl] >= 0) acc += part[((size_t)t * slots + sl) * H + r];
+    y[i] = acc;
+}
+
+template <int BITS>
+hipError_t down_em_bits(const float* h, const float* topk_w, const int32_t* topk_idx, const ExpertArgs& a, float* part,
+                        float* y, hipStream_t st) {
+    const size_t per_col = down_em_lds_per_col<BITS>(a.I);
+    int fit = (int)((kLdsMax - kStatic) / per_col);
+    if (fit > kCols) fit = kCols;
+    if (fit < 1) return hipErrorInvalidValue;
+    const int ns = fit;
+    size_t lds = (size_t)ns * per_col;
+    if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
+    auto k = down_em_kernel<BITS>;
+    hipError_t err = allow_lds(k, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k, dim3(cu_count()), dim3(kMT), lds, st, h, topk_w, a, part, ns);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const long long n = (long long)a.T * a.H;
+    hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, topk_idx, a.T,
+                       a.H, a.top_k, a.slots, y);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t gate_up_mfma_bits(const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
     // per staged token: hi + lo B operands and the reduction buffer
@@ -95,6 +149,16 @@ hipError_t launch_gate_up(int bits, const float* x, const ExpertArgs& a, float* 
         case 4: return gate_up_mfma_bits<4>(x, a, h, st);
         case 8: return gate_up_mfma_bits<8>(x, a, h, st);
         case 2: return gate_up_mfma_bits<2>(x, a, h, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_down_em(int bits, const float* h, const float* topk_w, const int32_t* topk_idx, const ExpertArgs& a,
+                          float* part, float* y, hipStream_t st) {
+    switch (bits) {
+        case 4: return down_em_bits<4>(h, topk_w, topk_idx, a, part, y, st);
+        case 8: return down_em_bits<8>(h, topk_w, topk_idx, a, part, y, st);
+        case 2: return down_em_bits<2>(h, topk_w, topk_idx, a, part, y, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -57,6 +57,7 @@ _SIGS = {
 for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_expert_gate_up_silu_{_b}"] = ([_P, _P, _P, _I, _I, _P, _P], _I)
     _SIGS[f"moe_expert_down_combine_{_b}"] = ([_P, _P, _P, _P, _I, _I, _P, _P], _I)
+    _SIGS[f"moe_expert_down_combine_em_{_b}"] = ([_P, _P, _P, _P, _P, _I, _I, _P, _P, _P], _I)
     _SIGS[f"moe_pack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_unpack_{_b}"] = ([_P, _P, _I64, _I64, _P], _I)
     _SIGS[f"moe_quantize_rows_{_b}"] = ([_P, _P, _P, _I64, _I64, _P], _I)
@@ -70,6 +71,10 @@ for _b in ("q4", "q8", "q2"):
                                              _P, _P], _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
+
+# batches from which the separate calls use the expert-major down (each
+# workgroup stages only the h of the experts it streams)
+DOWN_EM_MIN_TOKENS = 8
 
 # limits of the fused layer call (include/moedec.h)
 FUSED_MAX_TOKENS = 16
@@ -245,14 +250,27 @@ def gate_up_silu(x: torch.Tensor, ex: Experts, wl: Worklist, top_k: int, out: to
 
 
 def down_combine(h: torch.Tensor, ex: Experts, wl: Worklist, topk_w: torch.Tensor, top_k: int,
-                 out: torch.Tensor | None = None):
-    """moe_expert_down_combine_q{bits}: y[t] = sum_k w[t,k] o(t,k) + sum_shared o."""
+                 out: torch.Tensor | None = None, part: torch.Tensor | None = None,
+                 topk_idx: torch.Tensor | None = None):
+    """moe_expert_down_combine_q{bits}: y[t] = sum_k w[t,k] o(t,k) + sum_shared o.
+    With part (fp32 [T*(top_k+S), hidden] scratch): the expert-major form,
+    moe_expert_down_combine_em_q{bits} (topk_idx: skip top-p's dropped slots)."""
     T = topk_w.shape[0]
     if out is None:
         out = torch.empty((T, ex.hidden), dtype=torch.float32, device=h.device)
     if out.shape != (T, ex.hidden) or h.shape != (T * (top_k + ex.n_shared), ex.inter):
         raise ValueError("shape mismatch between h, topk_w and y")
     s_ex, s_wl = ex.struct(), wl.struct()
+    if part is not None:
+        if part.shape != (T * (top_k + ex.n_shared), ex.hidden):
+            raise ValueError("part must be [T*(top_k+S), hidden]")
+        name = f"moe_expert_down_combine_em_{_suffix(ex.bits)}"
+        idx = _dev(topk_idx, torch.int32, "topk_idx") if topk_idx is not None else None
+        st = getattr(lib(), name)(_dev(h, torch.float32, "h"), ctypes.byref(s_ex), ctypes.byref(s_wl),
+                                  _dev(topk_w, torch.float32, "topk_w"), idx, T, top_k,
+                                  _dev(part, torch.float32, "part"), _dev(out, torch.float32, "y"), _stream(h))
+        _check(name, st)
+        return out
     fn = getattr(lib(), f"moe_expert_down_combine_{_suffix(ex.bits)}")
     st = fn(_dev(h, torch.float32, "h"), ctypes.byref(s_ex), ctypes.byref(s_wl),
             _dev(topk_w, torch.float32, "topk_w"), T, top_k, _dev(out, torch.float32, "y"), _stream(h))
@@ -321,14 +339,16 @@ class LayerBuffers:
     h: torch.Tensor
     y: torch.Tensor
     workspace: torch.Tensor   # int32 [FUSED_WORKSPACE_INTS]
+    part: torch.Tensor | None = None   # fp32 [T*(K+S), H]: the expert-major down's partial outputs
 
     @staticmethod
     def allocate(T: int, H: int, I: int, E: int, top_k: int, n_shared: int, device) -> "LayerBuffers":
         f = dict(dtype=torch.float32, device=device)
         route = Route(torch.empty((T, E), **f), torch.empty((T, top_k), dtype=torch.int32, device=device),
                       torch.empty((T, top_k), **f), Worklist.empty(T, top_k, E, n_shared, device))
+        part = torch.empty((T * (top_k + n_shared), H), **f) if T >= DOWN_EM_MIN_TOKENS else None
         return LayerBuffers(route, torch.empty((T * (top_k + n_shared), I), **f), torch.empty((T, H), **f),
-                            torch.zeros(FUSED_WORKSPACE_INTS, dtype=torch.int32, device=device))
+                            torch.zeros(FUSED_WORKSPACE_INTS, dtype=torch.int32, device=device), part)
 
     def fused_error(self) -> bool:
         """True if a fused launch's wait timed out (synchronises)."""
@@ -412,7 +432,8 @@ def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: E
     route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
                rsf=rsf, out=buf.route, top_p=top_p)
     gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)
-    down_combine(buf.h, ex, buf.route.worklist, buf.route.topk_w, top_k, out=buf.y)
+    down_combine(buf.h, ex, buf.route.worklist, buf.route.topk_w, top_k, out=buf.y, part=buf.part,
+                 topk_idx=buf.route.topk_idx if buf.part is not None else None)
     return buf
 
 
