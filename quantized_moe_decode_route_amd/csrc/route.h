@@ -43,11 +43,153 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One token's group-limited top-k (wave-wide operations only; the whole wave
+// calls this).  NVT experts per lane, contiguous: lane l holds experts
+// l*NVT .. l*NVT + NVT - 1, so the lowest lane holding the round's largest
+// key also holds the lowest expert index among those with that key.
+template <int NVT, int TM, int EM, int NW, bool kCoherentScores, bool kTopP>
+__device__ __forceinline__ void route_one_token(const float* scores, const float* __restrict__ bias, int t, int E,
+                                                int n_group, int topk_group, int top_k, float rsf, float top_p,
+                                                RouteLdsT<TM, EM, NW>& r) {
+    static_assert(NVT <= 32, "the candidate mask is 32 bits");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int per = E / n_group;
+    float* cw = r.c[wave];
+    float cl[NVT], sl[NVT], bl[NVT];
+#pragma unroll
+    for (int j = 0; j < NVT; ++j) {                    // every load first (clamped index), then use
+        const int e = min(lane * NVT + j, E - 1);
+        if constexpr (kCoherentScores)
+            sl[j] = __int_as_float(__hip_atomic_load(reinterpret_cast<const int*>(scores + (size_t)t * E + e),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        else
+            sl[j] = scores[(size_t)t * E + e];
+        bl[j] = bias[e];
+    }
+    unsigned live = 0;                                 // bit j: expert lane * NVT + j exists
+#pragma unroll
+    for (int j = 0; j < NVT; ++j) {
+        const int e = lane * NVT + j;
+        const float v = sl[j] + bl[j];
+        cl[j] = v == v ? v : -INFINITY;
+        if (e < E) {
+            cw[e] = cl[j];
+            live |= 1u << j;
+        }
+    }
+    wave_lds_sync();
+    float gsv = -INFINITY;
+    if (lane < n_group) {
+        float m1 = -INFINITY, m2 = -INFINITY;
+        const float* cg = cw + lane * per;
+#pragma unroll 8
+        for (int k = 0; k < per; ++k) {                // branch-free, so the reads issue back to back
+            const float v = cg[k];
+            m2 = fmaxf(m2, fminf(m1, v));
+            m1 = fmaxf(m1, v);
+        }
+        const float gsum = m1 + m2;                     // NaN only from +inf + -inf
+        gsv = gsum == gsum ? gsum : -INFINITY;
+        r.gs[wave][lane] = gsv;
+    }
+    wave_lds_sync();
+    int grank = 0;
+    if (lane < n_group) {
+#pragma unroll 8
+        for (int h = 0; h < n_group; ++h) grank += beats(r.gs[wave][h], h, gsv, lane);
+    }
+    const unsigned long long kept = __ballot(lane < n_group && grank < topk_group);
+    // Candidates as order-preserving 32-bit keys of c (+0 for -0, so equal
+    // values tie and go by index); 0 (below -inf's key) marks an expert
+    // that is not, or no longer, a candidate.
+    const float inv_per = 1.0f / (float)per;
+    unsigned key[NVT];
+#pragma unroll
+    for (int j = 0; j < NVT; ++j) {
+        const int e = lane * NVT + j;
+        int g = (int)((float)e * inv_per);              // e / per, then corrected
+        g += (g + 1) * per <= e;
+        g -= g * per > e;
+        const unsigned u = __float_as_uint(cl[j] + 0.0f);
+        const unsigned ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        key[j] = (((live >> j) & 1u) && ((kept >> min(g, 63)) & 1ull)) ? ord : 0u;
+    }
+    // round k: each lane's best (largest key, lowest j on ties), the wave's
+    // largest key, then the lowest lane holding it (= the lowest expert index)
+    float total = 0.f, my_s = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < top_k; ++k) {
+        unsigned bk = key[NVT - 1];
+        int bj = NVT - 1;
+        float bs = sl[NVT - 1];
+#pragma unroll
+        for (int j = NVT - 2; j >= 0; --j) {
+            const bool better = key[j] >= bk;
+            bk = better ? key[j] : bk;
+            bj = better ? j : bj;
+            bs = better ? sl[j] : bs;
+        }
+        const unsigned m = wave_max_u(bk);
+        const int owner = (int)__builtin_ctzll(__ballot(bk == m));    // top_k <= candidates: m > 0
+        const int win = owner * NVT + __builtin_amdgcn_readlane(bj, owner);
+        const float sw = bits_f(__builtin_amdgcn_readlane(f_bits(bs), owner));
+        const bool mine = lane == owner;
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) key[j] = (mine && j == bj) ? 0u : key[j];
+        if (lane == 0) r.sel[t * top_k + k] = win;
+        if (lane == k) {
+            my_s = sw;
+            my_e = win;
+        }
+        total += sw;                                   // slot order
+    }
+    if (!kTopP || !(top_p < 1.f)) {
+        if (lane < top_k) r.selw[t * top_k + lane] = (my_s / total) * rsf;
+        return;
+    }
+    // adaptive top-p: rank of slot `lane` by (s descending, NaN last, index)
+    const unsigned us = __float_as_uint(my_s + 0.0f);
+    const unsigned ks = my_s == my_s ? ((us & 0x80000000u) ? ~us : (us | 0x80000000u)) : 0u;
+    int wr = 0;
+    for (int j = 0; j < top_k; ++j) {
+        const unsigned kj = __builtin_amdgcn_readlane(ks, j);
+        const int ej = __builtin_amdgcn_readlane(my_e, j);
+        wr += (kj > ks) || (kj == ks && ej < my_e);
+    }
+    const float thr = top_p * total;
+    float cum = 0.f;
+    int m = top_k;
+    for (int i = 0; i < top_k; ++i) {                  // the ranks are a permutation of 0 .. top_k-1
+        const int ln = (int)__builtin_ctzll(__ballot(lane < top_k && wr == i));
+        cum += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), ln));
+        if (cum >= thr) {
+            m = i + 1;
+            break;
+        }
+    }
+    const bool keep = lane < top_k && wr < m;
+    const unsigned long long kb = __ballot(keep);
+    float kept_total = 0.f;
+    for (int j = 0; j < top_k; ++j)                    // slot order
+        if ((kb >> j) & 1ull) kept_total += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), j));
+    // rewrite the token's slots (LDS writes of one wave land in order)
+    const int ns = __popcll(kb & ((1ull << lane) - 1ull));
+    if (keep) {
+        r.sel[t * top_k + ns] = my_e;
+        r.selw[t * top_k + ns] = (my_s / kept_total) * rsf;
+    }
+    if (lane >= m && lane < top_k) {
+        r.sel[t * top_k + lane] = -1;
+        r.selw[t * top_k + lane] = 0.f;
+    }
+}
+
 // Route T tokens whose sigmoid scores are in global memory (s[t][e]) and build
 // the batch union, all in LDS `r`; the whole workgroup (NW waves) calls this.
 // Each wave routes its own tokens with wave-wide operations only (no
 // workgroup barrier per token):
-//   1. lane l holds experts l, l+64, ...: s, and c = s + bias (also to LDS);
+//   1. lane l holds experts l*NV .. l*NV+NV-1: s, and c = s + bias (also to
+//      LDS); NV is 4 when E <= 256, else EM / 64;
 //   2. lane g < n_group: group score = largest + second largest c of group g;
 //   3. lane g: rank among the group scores; kept if rank < topk_group;
 //   4. top_k rounds of a wave arg-max over the kept groups' experts, by
@@ -75,139 +217,17 @@ template <int TM, int EM, int NW, bool kCoherentScores = false, bool kTopP = fal
 __device__ __forceinline__ void route_select_block(const float* scores, const float* __restrict__ bias, int T,
                                                    int E, int n_group, int topk_group, int top_k, int n_shared,
                                                    float rsf, float top_p, RouteLdsT<TM, EM, NW>& r) {
-    constexpr int NV = EM / kWave;                    // experts per lane
-    static_assert(NV <= 32, "the candidate mask is 32 bits");
+    constexpr int NV = EM / kWave;                    // experts per lane at most
+    constexpr int NV4 = NV < 4 ? NV : 4;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
-    const int per = E / n_group;
     for (int t = wave; t < T; t += nwaves) {
-        float* cw = r.c[wave];
-        float cl[NV], sl[NV], bl[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {                 // every load first (clamped index), then use
-            const int e = min(lane + kWave * j, E - 1);
-            if constexpr (kCoherentScores)
-                sl[j] = __int_as_float(__hip_atomic_load(reinterpret_cast<const int*>(scores + (size_t)t * E + e),
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            else
-                sl[j] = scores[(size_t)t * E + e];
-            bl[j] = bias[e];
-        }
-        unsigned live = 0;                             // bit j: expert lane + 64 j exists
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = lane + kWave * j;
-            const float v = sl[j] + bl[j];
-            cl[j] = v == v ? v : -INFINITY;
-            if (e < E) {
-                cw[e] = cl[j];
-                live |= 1u << j;
-            }
-        }
-        wave_lds_sync();
-        float gsv = -INFINITY;
-        if (lane < n_group) {
-            float m1 = -INFINITY, m2 = -INFINITY;
-            const float* cg = cw + lane * per;
-#pragma unroll 8
-            for (int k = 0; k < per; ++k) {            // branch-free, so the reads issue back to back
-                const float v = cg[k];
-                m2 = fmaxf(m2, fminf(m1, v));
-                m1 = fmaxf(m1, v);
-            }
-            const float gsum = m1 + m2;                 // NaN only from +inf + -inf
-            gsv = gsum == gsum ? gsum : -INFINITY;
-            r.gs[wave][lane] = gsv;
-        }
-        wave_lds_sync();
-        int grank = 0;
-        if (lane < n_group) {
-#pragma unroll 8
-            for (int h = 0; h < n_group; ++h) grank += beats(r.gs[wave][h], h, gsv, lane);
-        }
-        const unsigned long long kept = __ballot(lane < n_group && grank < topk_group);
-        // Candidates as order-preserving 32-bit keys of c (+0 for -0, so equal
-        // values tie and go by index); 0 (below -inf's key) marks an expert
-        // that is not, or no longer, a candidate.
-        const float inv_per = 1.0f / (float)per;
-        unsigned key[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = lane + kWave * j;
-            int g = (int)((float)e * inv_per);          // e / per, then corrected
-            g += (g + 1) * per <= e;
-            g -= g * per > e;
-            const unsigned u = __float_as_uint(cl[j] + 0.0f);
-            const unsigned ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-            key[j] = (((live >> j) & 1u) && ((kept >> min(g, 63)) & 1ull)) ? ord : 0u;
-        }
-        // round k: each lane's best (largest key, lowest j on ties), the
-        // wave's largest key, then the lowest expert index holding it
-        float total = 0.f, my_s = 0.f;
-        int my_e = 0;
-        for (int k = 0; k < top_k; ++k) {
-            unsigned bk = key[NV - 1];
-            int bj = NV - 1;
-            float bs = sl[NV - 1];
-#pragma unroll
-            for (int j = NV - 2; j >= 0; --j) {
-                const bool better = key[j] >= bk;
-                bk = better ? key[j] : bk;
-                bj = better ? j : bj;
-                bs = better ? sl[j] : bs;
-            }
-            const unsigned m = wave_max_u(bk);
-            const int win = wave_min(bk == m ? lane + kWave * bj : INT_MAX);   // top_k <= candidates
-            const int owner = win & (kWave - 1), jw = win / kWave;
-            const float sw = bits_f(__builtin_amdgcn_readlane(f_bits(bs), owner));
-#pragma unroll
-            for (int j = 0; j < NV; ++j) key[j] = (lane == owner && j == jw) ? 0u : key[j];
-            if (lane == 0) r.sel[t * top_k + k] = win;
-            if (lane == k) {
-                my_s = sw;
-                my_e = win;
-            }
-            total += sw;                               // slot order
-        }
-        if (!kTopP || !(top_p < 1.f)) {
-            if (lane < top_k) r.selw[t * top_k + lane] = (my_s / total) * rsf;
-            continue;
-        }
-        // adaptive top-p: rank of slot `lane` by (s descending, NaN last, index)
-        const unsigned us = __float_as_uint(my_s + 0.0f);
-        const unsigned ks = my_s == my_s ? ((us & 0x80000000u) ? ~us : (us | 0x80000000u)) : 0u;
-        int wr = 0;
-        for (int j = 0; j < top_k; ++j) {
-            const unsigned kj = __builtin_amdgcn_readlane(ks, j);
-            const int ej = __builtin_amdgcn_readlane(my_e, j);
-            wr += (kj > ks) || (kj == ks && ej < my_e);
-        }
-        const float thr = top_p * total;
-        float cum = 0.f;
-        int m = top_k;
-        for (int i = 0; i < top_k; ++i) {              // the ranks are a permutation of 0 .. top_k-1
-            const int ln = (int)__builtin_ctzll(__ballot(lane < top_k && wr == i));
-            cum += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), ln));
-            if (cum >= thr) {
-                m = i + 1;
-                break;
-            }
-        }
-        const bool keep = lane < top_k && wr < m;
-        const unsigned long long kb = __ballot(keep);
-        float kept_total = 0.f;
-        for (int j = 0; j < top_k; ++j)                // slot order
-            if ((kb >> j) & 1ull) kept_total += bits_f(__builtin_amdgcn_readlane(f_bits(my_s), j));
-        // rewrite the token's slots (LDS writes of one wave land in order)
-        const int ns = __popcll(kb & ((1ull << lane) - 1ull));
-        if (keep) {
-            r.sel[t * top_k + ns] = my_e;
-            r.selw[t * top_k + ns] = (my_s / kept_total) * rsf;
-        }
-        if (lane >= m && lane < top_k) {
-            r.sel[t * top_k + lane] = -1;
-            r.selw[t * top_k + lane] = 0.f;
-        }
+        if (NV == NV4 || E <= NV4 * kWave)
+            route_one_token<NV4, TM, EM, NW, kCoherentScores, kTopP>(scores, bias, t, E, n_group, topk_group, top_k,
+                                                                    rsf, top_p, r);
+        else
+            route_one_token<NV, TM, EM, NW, kCoherentScores, kTopP>(scores, bias, t, E, n_group, topk_group, top_k,
+                                                                   rsf, top_p, r);
     }
     __syncthreads();
 
