@@ -59,7 +59,8 @@ using namespace imma;
 constexpr int kFusedExperts = 512;                      // routed experts at most
 using FusedRoute = RouteLdsT<kCols, kFusedExperts, kMW>;
 constexpr int kRowF4 = MOEDEC_MAX_DIM / 4 / kMT;        // float4 of a router row per thread
-constexpr int kSpinDefault = 1 << 21;                   // ~1 us per round: a couple of seconds
+constexpr int kSpinDefault = 1 << 21;                   // ~1 us per poll: a couple of seconds
+constexpr int kPollRun = 24;                             // pipelined polls before the plain loop
 constexpr int kStreamW = 3;                             // stream items in flight per wave (3 measured best)
 constexpr int kStageV4 = 10;                            // float4 of h a thread stages at once
 constexpr int kStageX4 = 4;                             // float4 of x a thread holds at once
@@ -152,10 +153,36 @@ struct GridGate {
             const int i = (int)threadIdx.x - (kMT - kWave);
             const int m = i < kGates ? members(i) : 0;
             const unsigned long long target = (2ull * launch + (unsigned long long)x) * (unsigned long long)m;
-            int n = 0;
-            while (true) {
-                const bool done = m == 0 || __hip_atomic_load(counter(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
-                if (__ballot(!done) == 0) break;
+            // Four polls in flight: each step checks the oldest and issues the
+            // next, so the exchange is seen a fraction of a load's latency
+            // after it completes instead of up to a whole round trip later.
+            // Every lane loads (lanes past the counters re-read the last one):
+            // a branch around the loads would make each wait for all of them,
+            // and so would a loop back edge -- hence a straight run of steps
+            // first, then a plain polling loop for long waits.
+            unsigned long long* const cp = counter(i < kGates ? i : kGates - 1);
+            auto poll = [&]() -> unsigned long long {
+                return __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            unsigned long long p[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                p[k] = poll();
+                if (k < 3) __builtin_amdgcn_s_sleep(1);
+            }
+            bool done = false;
+#pragma unroll
+            for (int k = 0; k < kPollRun; ++k) {
+                if (__ballot(m != 0 && p[k & 3] < target) == 0) {
+                    done = true;
+                    break;
+                }
+                p[k & 3] = poll();
+                __builtin_amdgcn_s_sleep(1);
+            }
+            int n = kPollRun;
+            while (!done) {
+                if (__ballot(m != 0 && poll() < target) == 0) break;
                 if (++n >= spin_max) {
                     if (i == 0) __hip_atomic_store(ws + kWsError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
