@@ -532,153 +532,6 @@ __device__ __forceinline__ void gate_up_units(const ExpertArgs& a, const float* 
     }
 }
 
-// ------------------------------------------------- down, expert-major
-//
-// For larger batches: work units (segment, output row), a segment being an
-// expert and up to ns of its assignments; each segment stages only its own
-// assignments' h rows times their routing weights (as B columns), so a
-// workgroup reads h for the experts it streams, not for the whole batch.
-// Every unit writes its assignments' partial outputs part[a][r] =
-// s_down[r] * (Qd . h_a w_a)[r]; down_reduce adds them per token in slot
-// order afterwards.  No atomics: deterministic.
-
-// Rows [rlo, rhi) of expert e's down matrix for the nc staged columns.
-// red: LDS [kMW][NB][16][ns]; sd_s: LDS [NB*16].
-template <int BITS>
-__device__ __forceinline__ void down_em_rows(const ExpertArgs& a, float* __restrict__ part, int e, int rlo, int rhi,
-                                             int nc, const int* asg, const half8* hhi, const half8* hlo, int ns,
-                                             float unscale, float* red, float* sd_s) {
-    using M = MfmaCodec<BITS>;
-    constexpr int NCALL = M::NCALL;
-    constexpr int kNB = M::NB;
-    const int H = a.H, I = a.I;
-    const int row_bytes = I * BITS / 8;
-    const int P = row_bytes >> 4;
-    const int NCH = (P + 3) / 4;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int ln = lane & 15, lq = lane >> 4;
-    const int cw0 = wave * NCH / kMW, cw1 = (wave + 1) * NCH / kMW;
-    const int nk = cw1 - cw0;
-    const int bslot = ln < nc ? ln : -1;
-    const uint8_t* db = a.w_down + (size_t)e * H * row_bytes;
-
-    for (int g0 = rlo; g0 < rhi; g0 += kNB * 16) {
-        const int gn = min(rhi - g0, kNB * 16);
-        const int nb = (gn + 15) >> 4;
-        const int sr = min((int)threadIdx.x, gn - 1);
-        const float sdv = a.s_down[(size_t)e * H + g0 + sr];
-        floatx4 acc[kNB];
-#pragma unroll
-        for (int b = 0; b < kNB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-        auto issue = [&](int ch, uint4* dd) {
-            const int grp = min(ch * 4 + lq, P - 1);
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                const int r = min(g0 + b * 16 + ln, rhi - 1);
-                dd[b] = ld16(db + (size_t)r * row_bytes + grp * 16);
-            }
-        };
-        auto compute = [&](int ch, const uint4* dd) {
-            half8 bh[NCALL], bl[NCALL];
-#pragma unroll
-            for (int c = 0; c < NCALL; ++c) {
-                if (bslot >= 0) {
-                    const int src = ((ch * 4 + lq) * ns + bslot) * NCALL + c;
-                    bh[c] = hhi[src];
-                    bl[c] = hlo[src];
-                } else {
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) bh[c][e2] = bl[c][e2] = (_Float16)0.f;
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                if (b < nb) {
-#pragma unroll
-                    for (int c = 0; c < NCALL; ++c) {
-                        const half8 ad = a_operand<BITS>(dd[b], c);
-                        acc[b] = mfma(ad, bh[c], acc[b]);
-                        acc[b] = mfma(ad, bl[c], acc[b]);
-                    }
-                }
-            }
-        };
-        if (nk > 0) {
-            uint4 d0[kNB], d1[kNB];
-            issue(cw0, d0);
-            for (int t = 0; t < nk; t += 2) {          // two register buffers, alternating
-                issue(cw0 + min(t + 1, nk - 1), d1);
-                compute(cw0 + t, d0);
-                issue(cw0 + min(t + 2, nk - 1), d0);
-                if (t + 1 < nk) compute(cw0 + t + 1, d1);
-            }
-        }
-        if ((int)threadIdx.x < gn) sd_s[threadIdx.x] = sdv;
-        if (ln < nc) {
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                if (b < nb) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) red[((wave * kNB + b) * 16 + 4 * lq + i) * ns + ln] = acc[b][i];
-                }
-            }
-        }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < gn * nc; idx += kMT) {
-            const int r = idx / nc, n = idx - r * nc;
-            const int b = r >> 4, rr = r & 15;
-            float v = 0.f;
-            for (int w = 0; w < kMW; ++w) v += red[((w * kNB + b) * 16 + rr) * ns + n];
-            part[(size_t)asg[n] * H + g0 + r] = v * unscale * sd_s[r];
-        }
-        __syncthreads();
-    }
-}
-
-struct DownEmLds {
-    int cpre[kMaxActive + 1];
-    int asg[kCols];
-    float mul[kCols];
-    float scratch[kMW];
-    float sd[MfmaCodec<2>::NB * 16 > MfmaCodec<8>::NB * 16 ? MfmaCodec<2>::NB * 16 : MfmaCodec<8>::NB * 16];
-    int kexp;
-};
-
-// This workgroup's share `part` of `nparts` of the (segment, row) units.
-template <int BITS>
-__device__ __forceinline__ void down_em_units(const ExpertArgs& a, const float* __restrict__ h,
-                                              const float* __restrict__ topk_w, float* __restrict__ part_out,
-                                              const int* eid, const int* seg, const int* assign, int n_exp, int ns,
-                                              int part, int nparts, half8* hhi, half8* hlo, float* red,
-                                              DownEmLds& s) {
-    const int H = a.H, I = a.I;
-    mw_segment_prefix(seg, n_exp, ns, s.cpre);
-    const int n_seg = s.cpre[n_exp];
-    const long long n_units = (long long)n_seg * H;
-    const long long u0 = n_units * part / nparts;
-    const long long u1 = n_units * (part + 1) / nparts;
-    if (u0 >= u1) return;                        // uniform over the workgroup
-    for (int sidx = (int)(u0 / H); (long long)sidx * H < u1; ++sidx) {
-        const int rlo = (int)max(u0 - (long long)sidx * H, 0LL);
-        const int rhi = (int)min(u1 - (long long)sidx * H, (long long)H);
-        const int j = mw_upper_index(s.cpre, n_exp, sidx);
-        const int first = seg[j] + (sidx - s.cpre[j]) * ns;
-        const int nc = min(ns, seg[j + 1] - first);
-        __syncthreads();   // everyone is done with the previous segment's LDS
-        if ((int)threadIdx.x < nc) {
-            const int as = assign[first + threadIdx.x];
-            const int t = as / a.slots, sl = as - t * a.slots;
-            s.asg[threadIdx.x] = as;
-            s.mul[threadIdx.x] = sl < a.top_k ? topk_w[t * a.top_k + sl] : 1.0f;
-        }
-        __syncthreads();
-        const int k = stage_b<BITS>(h, I, I, s.asg, s.mul, nc, ns, hhi, hlo, s.scratch);
-        if (threadIdx.x == 0) s.kexp = k;
-        __syncthreads();
-        down_em_rows<BITS>(a, part_out, eid[j], rlo, rhi, nc, s.asg, hhi, hlo, ns, ldexpf(1.0f, -s.kexp), red, s.sd);
-    }
-}
-
 // LDS bytes gate_up_rows needs besides the staged activations, per staged token.
 template <int BITS>
 constexpr size_t gate_up_red_bytes_per_token() {
@@ -689,12 +542,6 @@ constexpr size_t gate_up_red_bytes_per_token() {
 template <int BITS>
 __host__ __device__ constexpr size_t staged_row_bytes(int ncols) {
     return (size_t)((ncols * BITS / 8 / 16 + 3) / 4) * 4 * MfmaCodec<BITS>::NCALL * 2 * 16;
-}
-
-// LDS per staged assignment of down_em_units: hi + lo B operands and the reduction.
-template <int BITS>
-__host__ __device__ constexpr size_t down_em_lds_per_col(int I) {
-    return staged_row_bytes<BITS>(I) + (size_t)kMW * MfmaCodec<BITS>::NB * 16 * sizeof(float);
 }
 
 // LDS per staged token of gate_up_units: hi + lo B operands and the reduction.
