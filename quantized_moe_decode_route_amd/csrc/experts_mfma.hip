@@ -44,22 +44,34 @@ __device__ __forceinline__ void down_em_rows(const ExpertArgs& a, float* __restr
     const int bslot = ln < nc ? ln : -1;
     const uint8_t* db = a.w_down + (size_t)e * H * row_bytes;
 
-    for (int g0 = rlo; g0 < rhi; g0 += kNB * 16) {
-        const int gn = min(rhi - g0, kNB * 16);
+    constexpr int G = kNB * 16;
+    // chunk ch of the group starting at row gs
+    auto issue_at = [&](int gs, int ch, uint4* dd) {
+        const int grp = min(ch * 4 + lq, P - 1);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            const int r = min(gs + b * 16 + ln, rhi - 1);
+            dd[b] = ld16(db + (size_t)r * row_bytes + grp * 16);
+        }
+    };
+    // With an even chunk count per wave the next group's first two chunks go
+    // out as soon as this group's buffers are free, ahead of its reduction
+    // (the last group re-reads its own first chunks instead).
+    const bool ahead = nk > 0 && (nk & 1) == 0;
+    uint4 d0[kNB], d1[kNB];
+    if (ahead) {
+        issue_at(rlo, cw0, d0);
+        issue_at(rlo, cw0 + 1, d1);
+    }
+    for (int g0 = rlo; g0 < rhi; g0 += G) {
+        const int gn = min(rhi - g0, G);
         const int nb = (gn + 15) >> 4;
         const int sr = min((int)threadIdx.x, gn - 1);
         const float sdv = a.s_down[(size_t)e * H + g0 + sr];
         floatx4 acc[kNB];
 #pragma unroll
         for (int b = 0; b < kNB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-        auto issue = [&](int ch, uint4* dd) {
-            const int grp = min(ch * 4 + lq, P - 1);
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                const int r = min(g0 + b * 16 + ln, rhi - 1);
-                dd[b] = ld16(db + (size_t)r * row_bytes + grp * 16);
-            }
-        };
+        auto issue = [&](int ch, uint4* dd) { issue_at(g0, ch, dd); };
         auto compute = [&](int ch, const uint4* dd) {
             half8 bh[NCALL], bl[NCALL];
 #pragma unroll
@@ -85,8 +97,16 @@ __device__ __forceinline__ void down_em_rows(const ExpertArgs& a, float* __restr
                 }
             }
         };
-        if (nk > 0) {
-            uint4 d0[kNB], d1[kNB];
+        if (ahead) {
+            const int gnx = g0 + G < rhi ? g0 + G : g0;
+            for (int t = 0; t < nk; t += 2) {          // chunks t, t+1 are in d0, d1
+                compute(cw0 + t, d0);
+                const bool in0 = t + 2 < nk;
+                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 2 : cw0, d0);
+                compute(cw0 + t + 1, d1);
+                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 3 : cw0 + 1, d1);
+            }
+        } else if (nk > 0) {
             issue(cw0, d0);
             for (int t = 0; t < nk; t += 2) {          // two register buffers, alternating
                 issue(cw0 + min(t + 1, nk - 1), d1);
