@@ -365,8 +365,29 @@ __device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restr
     const uint8_t* gb = a.w_gate + (size_t)e * I * row_bytes;
     const uint8_t* ub = a.w_up + (size_t)e * I * row_bytes;
 
-    for (int g0 = rlo; g0 < rhi; g0 += kNB * 16) {
-        const int gn = min(rhi - g0, kNB * 16);          // rows in this group
+    constexpr int G = kNB * 16;
+    // chunk ch of the group starting at row gs
+    auto issue_at = [&](int gs, int ch, uint4* dg, uint4* du) {
+        const int grp = min(ch * 4 + lq, P - 1);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            const int r = min(gs + b * 16 + ln, rhi - 1);
+            const size_t off = (size_t)r * row_bytes + grp * 16;
+            dg[b] = ld16(gb + off);
+            du[b] = ld16(ub + off);
+        }
+    };
+    // With an even chunk count per wave the next group's first two chunks go
+    // out as soon as this group's buffers are free, ahead of its reduction
+    // (the last group re-reads its own first chunks instead).
+    const bool ahead = nk > 0 && (nk & 1) == 0;
+    uint4 g0b[kNB], u0b[kNB], g1b[kNB], u1b[kNB];
+    if (ahead) {
+        issue_at(rlo, cw0, g0b, u0b);
+        issue_at(rlo, cw0 + 1, g1b, u1b);
+    }
+    for (int g0 = rlo; g0 < rhi; g0 += G) {
+        const int gn = min(rhi - g0, G);                 // rows in this group
         const int nb = (gn + 15) >> 4;
         // row scales: loaded now, used after the K loop (to LDS only then, so
         // nothing waits for them before the code loads are issued)
@@ -376,16 +397,7 @@ __device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restr
         floatx4 accg[kNB], accu[kNB];
 #pragma unroll
         for (int b = 0; b < kNB; ++b) accg[b] = accu[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-        auto issue = [&](int ch, uint4* dg, uint4* du) {
-            const int grp = min(ch * 4 + lq, P - 1);
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                const int r = min(g0 + b * 16 + ln, rhi - 1);
-                const size_t off = (size_t)r * row_bytes + grp * 16;
-                dg[b] = ld16(gb + off);
-                du[b] = ld16(ub + off);
-            }
-        };
+        auto issue = [&](int ch, uint4* dg, uint4* du) { issue_at(g0, ch, dg, du); };
         auto compute = [&](int ch, const uint4* dg, const uint4* du) {
             half8 bh[NCALL], bl[NCALL];
 #pragma unroll
@@ -414,8 +426,16 @@ __device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restr
                 }
             }
         };
-        if (nk > 0) {
-            uint4 g0b[kNB], u0b[kNB], g1b[kNB], u1b[kNB];
+        if (ahead) {
+            const int gnx = g0 + G < rhi ? g0 + G : g0;
+            for (int t = 0; t < nk; t += 2) {          // chunks t, t+1 are in buffers 0, 1
+                compute(cw0 + t, g0b, u0b);
+                const bool in0 = t + 2 < nk;
+                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 2 : cw0, g0b, u0b);
+                compute(cw0 + t + 1, g1b, u1b);
+                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 3 : cw0 + 1, g1b, u1b);
+            }
+        } else if (nk > 0) {
             issue(cw0, g0b, u0b);
             for (int t = 0; t < nk; t += 2) {          // two register buffers, alternating
                 issue(cw0 + min(t + 1, nk - 1), g1b, u1b);
