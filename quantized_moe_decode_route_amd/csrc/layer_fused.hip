@@ -46,7 +46,7 @@
 // with other work) ends with garbage outputs and a raised flag instead of
 // hanging.
 #include "imma.h"
-#include "mfma.h"
+#include "persist.h"
 #include "route.h"
 
 namespace moedec {
