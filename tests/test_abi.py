@@ -92,14 +92,22 @@ def test_expert_calls_reject(lib, suffix, bits, kw, wkw, call, status):
     T, K = call.get("T", 1), call.get("K", 4)
     gu = getattr(lib, f"moe_expert_gate_up_silu_{suffix}")
     dn = getattr(lib, f"moe_expert_down_combine_{suffix}")
+    em = getattr(lib, f"moe_expert_down_combine_em_{suffix}")
     assert gu(FAKE, ctypes.byref(ex), ctypes.byref(wl), T, K, FAKE, None) == status
     assert dn(FAKE, ctypes.byref(ex), ctypes.byref(wl), FAKE, T, K, FAKE, None) == status
+    assert em(FAKE, ctypes.byref(ex), ctypes.byref(wl), FAKE, FAKE, T, K, FAKE, FAKE, None) == status
 
 
 def test_expert_calls_reject_null_structs(lib):
     assert lib.moe_expert_gate_up_silu_q4(FAKE, None, ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
     assert lib.moe_expert_down_combine_q4(FAKE, ctypes.byref(_experts()), None, FAKE, 1, 4, FAKE, None) == 1
     assert lib.moe_expert_gate_up_silu_q4(None, ctypes.byref(_experts()), ctypes.byref(_wl()), 1, 4, FAKE, None) == 1
+    em = lib.moe_expert_down_combine_em_q4
+    ex, wl = ctypes.byref(_experts()), ctypes.byref(_wl())
+    assert em(FAKE, ex, wl, FAKE, FAKE, 1, 4, None, FAKE, None) == 1        # no partial-output buffer
+    assert em(FAKE, ex, wl, FAKE, FAKE, 1, 4, FAKE, None, None) == 1        # no y
+    assert em(FAKE, None, wl, FAKE, FAKE, 1, 4, FAKE, FAKE, None) == 1
+    assert em(FAKE + 4, ex, wl, FAKE, FAKE, 1, 4, FAKE, FAKE, None) == 1    # h not 16-byte aligned
 
 
 def _fused(lib, suffix, ex, wl, **kw):
