@@ -9,7 +9,9 @@ from a fixed seed: 1 to 64 tokens, hidden and inter sizes of whole 16-byte
 code groups that are mostly not multiples of the kernels' tiles, 1 to 8
 groups of 2 to 12 experts, top-k up to what the kept groups hold, 0 to 2
 shared experts, every code width, plain top-k or top-p.  At 8 tokens and
-more the separate calls use the expert-major down.
+more the separate calls use the expert-major down.  A second sample, of
+whole activation blocks, runs the int8-activation call (the integer-dot
+item: Q8_0-style activations) against the oracle's same quantisation.
 """
 import numpy as np
 import pytest
@@ -58,4 +60,38 @@ def test_random_shape_matches_oracle(i, fused):
     lay = synth.layer_device(cfg, 0, DEV)
     x = synth.token_pool(cfg, T)
     g = run_layer(cfg, lay, x, fused=fused, top_p=top_p)
+    check_all(cfg, g, x, synth.router_weight(cfg, 0), synth.router_bias(cfg, 0), synth.expert_loader(cfg, 0))
+
+
+def _act8_shapes(n=12, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        bits = int(rng.choice([2, 4, 8]))
+        blk = 512 // bits                        # one activation block
+        H = int(rng.integers(1, 9)) * blk
+        I = int(rng.integers(1, 7)) * blk
+        G = int(rng.choice([1, 2, 4, 8]))
+        per = int(rng.integers(2, 9))
+        E = G * per
+        TG = int(rng.integers(1, G + 1))
+        K = int(rng.integers(1, min(TG * per, 8) + 1))
+        S = int(rng.integers(0, 3))
+        T = int(rng.choice([1, 2, 3, 6, 16]))
+        top_p = None if rng.random() < 0.7 else float(rng.choice([0.0, 0.6]))
+        out.append((T, H, I, E, G, TG, K, S, bits, top_p))
+    return out
+
+
+ACT8 = _act8_shapes()
+
+
+@pytest.mark.parametrize("i", range(len(ACT8)))
+def test_random_shape_act8_matches_oracle(i):
+    T, H, I, E, G, TG, K, S, bits, top_p = ACT8[i]
+    cfg = synth.MoEConfig(f"act8rand{i}", T, H, I, E, G, TG, K, S, bits, seed=200 + i)
+    say(f"case act8rand{i}: T={T} H={H} I={I} E={E} G={G} TG={TG} K={K} S={S} bits={bits} top_p={top_p}")
+    lay = synth.layer_device(cfg, 0, DEV)
+    x = synth.token_pool(cfg, T)
+    g = run_layer(cfg, lay, x, fused=True, top_p=top_p, act8=True)
     check_all(cfg, g, x, synth.router_weight(cfg, 0), synth.router_bias(cfg, 0), synth.expert_loader(cfg, 0))
