@@ -251,8 +251,20 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(const float* __restric
     if (i >= (long long)T * H) return;
     const int t = (int)(i / H), r = (int)(i - (long long)t * H);
     float acc = 0.f;
-    for (int sl = 0; sl < slots; ++sl)
-        if (sl >= K || topk_idx == nullptr || topk_idx[t * K + sl] >= 0) acc += part[((size_t)t * slots + sl) * H + r];
+    for (int s0 = 0; s0 < slots; s0 += 8) {
+        // the loads of 8 slots at once (valid rows and indices), then the sum in slot order
+        float v[8];
+        int id[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int sl = min(s0 + k, slots - 1);
+            v[k] = part[((size_t)t * slots + sl) * H + r];
+            id[k] = topk_idx != nullptr && sl < K ? topk_idx[t * K + sl] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s0 + k < slots && id[k] >= 0) acc += v[k];
+    }
     y[i] = acc;
 }
 
