@@ -11,10 +11,15 @@ groups of 2 to 12 experts, top-k up to what the kept groups hold, 0 to 2
 shared experts, every code width, plain top-k or top-p.  At 8 tokens and
 more the separate calls use the expert-major down.  A second sample, of
 whole activation blocks, runs the int8-activation call (the integer-dot
-item: Q8_0-style activations) against the oracle's same quantisation.
+item: Q8_0-style activations) against the oracle's same quantisation, and
+a third runs the pre-norm residual form (x_out = x + MoE(rmsnorm(x)), the
+norm inside the launch) against the oracle on the normalised tokens.
 """
 import numpy as np
 import pytest
+import torch
+
+from oracle import moe_oracle as orc
 
 from quantized_moe_decode_route_amd import ops, synth
 
@@ -95,3 +100,38 @@ def test_random_shape_act8_matches_oracle(i):
     x = synth.token_pool(cfg, T)
     g = run_layer(cfg, lay, x, fused=True, top_p=top_p, act8=True)
     check_all(cfg, g, x, synth.router_weight(cfg, 0), synth.router_bias(cfg, 0), synth.expert_loader(cfg, 0))
+
+
+RESID = [s for s in _shapes(n=24, seed=2028) if s[0] <= ops.FUSED_MAX_TOKENS][:10]
+
+
+@pytest.mark.parametrize("i", range(len(RESID)))
+def test_random_shape_residual_form_matches_oracle(i):
+    T, H, I, E, G, TG, K, S, bits, top_p = RESID[i]
+    cfg = synth.MoEConfig(f"residrand{i}", T, H, I, E, G, TG, K, S, bits, seed=300 + i)
+    say(f"case residrand{i}: T={T} H={H} I={I} E={E} G={G} TG={TG} K={K} S={S} bits={bits} top_p={top_p}")
+    lay = synth.layer_device(cfg, 0, DEV)
+    x = synth.token_pool(cfg, T) * np.float32(5.0)           # an un-normalised residual stream
+    xt = torch.from_numpy(x).to(DEV)
+    ex = ops.Experts.from_layer(lay, E, S, bits)
+    buf = ops.LayerBuffers.allocate(T, H, I, E, K, S, DEV)
+    xo = torch.empty_like(xt)
+    try:
+        ops.layer_fused(xt, lay["router_w"], lay["bias"], ex, buf=buf, top_p=top_p, x_out=xo, n_group=G,
+                        topk_group=TG, top_k=K, rsf=cfg.rsf)
+    except ops.MoedecError as err:
+        if err.status == ops.MOEDEC_ERR_UNSUPPORTED:
+            pytest.skip("the activations of this batch do not fit the fused call's LDS plan")
+        raise
+    torch.cuda.synchronize()
+    assert not buf.fused_error()
+    wl = buf.route.worklist
+    n = int(wl.n_active.item())
+    seg = wl.seg[:n + 1].cpu().numpy()
+    g = dict(scores=buf.route.scores.cpu().numpy(), idx=buf.route.topk_idx.cpu().numpy(),
+             w=buf.route.topk_w.cpu().numpy(), n_active=n, expert_id=wl.expert_id[:n].cpu().numpy(), seg=seg,
+             assign=wl.assign[:int(seg[-1])].cpu().numpy(), h=buf.h.cpu().numpy(), y=buf.y.cpu().numpy(),
+             top_p=top_p)
+    np.testing.assert_array_equal(xo.cpu().numpy(), x + g["y"])          # x_out = x + y in fp32
+    xn = orc.rmsnorm(x).astype(np.float32)
+    check_all(cfg, g, xn, synth.router_weight(cfg, 0), synth.router_bias(cfg, 0), synth.expert_loader(cfg, 0))
