@@ -183,7 +183,6 @@ hipError_t launch_route(const float* x, const float* router_w, const float* bias
                         hipStream_t stream);
 
 hipError_t launch_gate_up(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t stream);
-hipError_t launch_gate_up_valu(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t stream);
 hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                             hipStream_t stream);
 

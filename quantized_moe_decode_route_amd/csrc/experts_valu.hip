@@ -1,19 +1,18 @@
-// Expert kernels on the vector ALUs: gate/up + SwiGLU, and down + weighted
-// combine, over row-scaled int8 / packed int4 / packed int2 codes (dequantised
-// on use).  The matrix-core kernels (experts_mfma.hip) are the default; these
-// serve the batches they do not take (more than 16 tokens for down).
+// Down projection + weighted combine on the vector ALUs, over row-scaled int8
+// / packed int4 / packed int2 codes (dequantised on use), for the batches the
+// matrix-core down kernels (experts_mfma.hip) do not take: more than 16
+// tokens.  Gate/up always runs on the matrix cores.
 //
-// Both kernels are persistent: one workgroup of 8 waves per compute unit, each
-// taking an equal contiguous share of the work, so every selected expert's
-// packed rows are streamed exactly once per token batch (the batch union of
-// the worklist) and every CU streams the same number of bytes.  Rows are split
-// into 16-byte groups and the lanes of a lane group take consecutive groups,
-// so one wave-wide load covers a contiguous 1 KB.  Each wave keeps W such loads
-// in flight in a register ring while it decodes earlier ones.  The worklist is
-// copied to LDS first so no weight load waits behind a global lookup.
-// Activations (x for gate/up, h for down) are staged in LDS in a
-// group-transposed layout [token][column-in-group][group], so the lanes of a
-// wave read consecutive LDS words (no bank conflicts).
+// The kernel is persistent: one workgroup of 8 waves per compute unit, each
+// owning a contiguous block of output rows for the whole batch, so every
+// selected expert's packed rows are streamed exactly once per token batch
+// (the batch union of the worklist).  Rows are split into 16-byte groups and
+// the lanes of a lane group take consecutive groups, so one wave-wide load
+// covers a contiguous 1 KB.  Each wave keeps W such loads in flight in a
+// register ring while it decodes earlier ones.  The worklist is copied to LDS
+// first so no weight load waits behind a global lookup.  The activations (h)
+// are staged in LDS in a group-transposed layout [row][column-in-group][group],
+// so the lanes of a wave read consecutive LDS words (no bank conflicts).
 #include "common.h"
 
 namespace moedec {
@@ -21,7 +20,6 @@ namespace moedec {
 constexpr int kPThreads = 512;
 constexpr int kPWaves = kPThreads / kWave;
 constexpr int kMaxActive = MOEDEC_MAX_EXPERTS + 8;
-constexpr int kNcMax = 4;                      // tokens per gate/up segment
 
 // Copy n_active, expert_id[] and seg[] of the worklist to LDS (whole workgroup).
 __device__ __forceinline__ int load_worklist(const ExpertArgs& a, int* eid, int* seg) {
@@ -46,252 +44,6 @@ __device__ __forceinline__ int upper_index(const int* v, int n, int q) {
         else hi = mid - 1;
     }
     return lo;
-}
-
-// cpre[j] = number of token chunks (of up to kNcMax) of experts 0..j-1, for
-// j in [0, n]; each thread scans a contiguous run of entries.
-__device__ void chunk_prefix(const int* seg, int n, int* cpre) {
-    __shared__ int wtot[kPWaves];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int per = (n + 1 + kPThreads - 1) / kPThreads;
-    const int j0 = threadIdx.x * per, j1 = min(j0 + per, n);
-    int local = 0;
-    for (int j = j0; j < j1; ++j) local += (seg[j + 1] - seg[j] + kNcMax - 1) / kNcMax;
-    int inc = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int u = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += u;
-    }
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    int run = inc - local;
-    for (int w = 0; w < wave; ++w) run += wtot[w];
-    for (int j = j0; j < min(j0 + per, n + 1); ++j) {
-        cpre[j] = run;
-        if (j < n) run += (seg[j + 1] - seg[j] + kNcMax - 1) / kNcMax;
-    }
-    __syncthreads();
-}
-
-// Stage n token rows of x into LDS slots: xs[(slot*CW + c)*P + p] and the
-// per-group sums xsum[slot*P + p].
-template <int BITS>
-__device__ __forceinline__ void stage_tokens(const float* __restrict__ x, int H, const int* tok, const int* slot,
-                                             int n, float* xs, float* xsum) {
-    constexpr int CW = 16 * Codec<BITS>::F;
-    const int P = (H * BITS / 8) >> 4;
-    for (int idx = threadIdx.x; idx < n * P; idx += blockDim.x) {
-        const int k = idx / P, p = idx - k * P;
-        const int sl = slot ? slot[k] : k;
-        const int t = tok ? tok[k] : k;
-        const float4* s4 = reinterpret_cast<const float4*>(x + (size_t)t * H + p * CW);
-        float sum = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < CW / 4; ++c4) {
-            const float4 v = s4[c4];
-            xs[(sl * CW + 4 * c4 + 0) * P + p] = v.x;
-            xs[(sl * CW + 4 * c4 + 1) * P + p] = v.y;
-            xs[(sl * CW + 4 * c4 + 2) * P + p] = v.z;
-            xs[(sl * CW + 4 * c4 + 3) * P + p] = v.w;
-            sum += (v.x + v.y) + (v.z + v.w);
-        }
-        xsum[sl * P + p] = sum;
-    }
-}
-
-// ------------------------------------------------------------------ gate / up
-//
-// Work units are (segment, row) with segment = (active expert j, chunk of up
-// to kNcMax of its tokens); segments are enumerated expert-ascending and each
-// workgroup takes an equal contiguous range of the units.  When the batch's
-// tokens fit in LDS they are staged once at kernel start (slot = token index);
-// otherwise each segment stages its own tokens.  h[a][r] = silu(g) * v.
-
-template <int BITS, int NC, int LPR, int W>
-__device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restrict__ h, const float* xs,
-                                             const float* xsum, const int* slot, const int* asg, int e,
-                                             int rlo, int rhi, int lpr) {
-    using C = Codec<BITS>;
-    constexpr int F = C::F;
-    constexpr int CW = 16 * F;
-    const int H = a.H, I = a.I;
-    const int row_bytes = H * BITS / 8;
-    const int P = row_bytes >> 4;
-    const int spl = P / lpr;
-    const int gpw = kWave / lpr;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int grp = lane / lpr, li = lane - grp * lpr;
-    const int rows_per_iter = kPWaves * gpw;
-    const int n_iter = (rhi - rlo + rows_per_iter - 1) / rows_per_iter;
-    const int n_items = n_iter * spl;
-    const uint8_t* gb = a.w_gate + (size_t)e * I * row_bytes;
-    const uint8_t* ub = a.w_up + (size_t)e * I * row_bytes;
-    const float* sg = a.s_gate + (size_t)e * I;
-    const float* su = a.s_up + (size_t)e * I;
-    int sl[NC];
-#pragma unroll
-    for (int k = 0; k < NC; ++k) sl[k] = slot[k];
-
-    auto row_of = [&](int it) { return rlo + it * rows_per_iter + wave * gpw + grp; };
-    uint4 bg[W], bu[W];
-    float bsg[W], bsu[W];
-    auto issue = [&](int i, int w) {
-        const int it = i / spl, s = i - it * spl;
-        const int r = min(row_of(it), rhi - 1);
-        const size_t off = (size_t)r * row_bytes + (li + s * lpr) * 16;
-        bg[w] = ld16(gb + off);
-        bu[w] = ld16(ub + off);
-        bsg[w] = sg[r];
-        bsu[w] = su[r];
-    };
-#pragma unroll
-    for (int w = 0; w < W; ++w)
-        if (w < n_items) issue(w, w);
-
-    // this lane's share of 2^(BITS-1) * sum(x) over its groups
-    float xoff[NC];
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-        float v = 0.f;
-        for (int s = 0; s < spl; ++s) v += xsum[sl[k] * P + li + s * lpr];
-        xoff[k] = C::kOffset * v;
-    }
-
-    float ag[NC][F], au[NC][F];
-#pragma unroll
-    for (int k = 0; k < NC; ++k)
-#pragma unroll
-        for (int f = 0; f < F; ++f) ag[k][f] = au[k][f] = 0.f;
-
-    for (int base = 0; base < n_items; base += W) {
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const int i = base + w;
-            if (i >= n_items) break;
-            const uint4 cg = bg[w], cu = bu[w];
-            const float csg = bsg[w], csu = bsu[w];
-            if (i + W < n_items) issue(i + W, w);
-            const int it = i / spl, s = i - it * spl;
-            const int p = li + s * lpr;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float xv[NC][4 * F];
-#pragma unroll
-                for (int k = 0; k < NC; ++k)
-#pragma unroll
-                    for (int m = 0; m < 4 * F; ++m) xv[k][m] = xs[(sl[k] * CW + 4 * d * F + m) * P + p];
-                const uint32_t wgd = (d == 0 ? cg.x : d == 1 ? cg.y : d == 2 ? cg.z : cg.w) ^ C::kFlip;
-                const uint32_t wud = (d == 0 ? cu.x : d == 1 ? cu.y : d == 2 ? cu.z : cu.w) ^ C::kFlip;
-#pragma unroll
-                for (int f = 0; f < F; ++f) {
-                    const uint32_t mg = wgd & C::mask(f), mu = wud & C::mask(f);
-                    const float g0 = ubyte_f<0>(mg), g1 = ubyte_f<1>(mg), g2 = ubyte_f<2>(mg), g3 = ubyte_f<3>(mg);
-                    const float u0 = ubyte_f<0>(mu), u1 = ubyte_f<1>(mu), u2 = ubyte_f<2>(mu), u3 = ubyte_f<3>(mu);
-#pragma unroll
-                    for (int k = 0; k < NC; ++k) {
-                        ag[k][f] = fmaf(g0, xv[k][0 * F + f], ag[k][f]);
-                        ag[k][f] = fmaf(g1, xv[k][1 * F + f], ag[k][f]);
-                        ag[k][f] = fmaf(g2, xv[k][2 * F + f], ag[k][f]);
-                        ag[k][f] = fmaf(g3, xv[k][3 * F + f], ag[k][f]);
-                        au[k][f] = fmaf(u0, xv[k][0 * F + f], au[k][f]);
-                        au[k][f] = fmaf(u1, xv[k][1 * F + f], au[k][f]);
-                        au[k][f] = fmaf(u2, xv[k][2 * F + f], au[k][f]);
-                        au[k][f] = fmaf(u3, xv[k][3 * F + f], au[k][f]);
-                    }
-                }
-            }
-            if (s == spl - 1) {
-                const int r = row_of(it);
-#pragma unroll
-                for (int k = 0; k < NC; ++k) {
-                    float g = -xoff[k], v = -xoff[k];
-#pragma unroll
-                    for (int f = 0; f < F; ++f) {
-                        g += C::scale(f) * ag[k][f];
-                        v += C::scale(f) * au[k][f];
-                        ag[k][f] = au[k][f] = 0.f;
-                    }
-                    if constexpr (LPR > 0) {
-                        g = group_sum<LPR>(g);
-                        v = group_sum<LPR>(v);
-                    } else {
-                        g = group_sum_rt(g, lpr);
-                        v = group_sum_rt(v, lpr);
-                    }
-                    if (li == 0 && r < rhi) {
-                        g *= csg;
-                        v *= csu;
-                        h[(size_t)asg[k] * I + r] = g / (1.0f + __expf(-g)) * v;
-                    }
-                }
-            }
-        }
-    }
-}
-
-template <int BITS, int LPR, int W>
-__global__ __launch_bounds__(kPThreads) void gate_up_kernel(const float* __restrict__ x, const ExpertArgs a,
-                                                            float* __restrict__ h, int lpr_rt, int ns) {
-    using C = Codec<BITS>;
-    constexpr int CW = 16 * C::F;
-    extern __shared__ float lds[];
-    __shared__ int eid[kMaxActive];
-    __shared__ int seg[kMaxActive + 1];
-    __shared__ int cpre[kMaxActive + 1];
-    __shared__ int tok_s[kNcMax], slot_s[kNcMax], asg_s[kNcMax], staged_s[kNcMax];
-
-    const int H = a.H, I = a.I, T = a.T;
-    const int P = (H * BITS / 8) >> 4;
-    const int lpr = LPR > 0 ? LPR : lpr_rt;
-    float* xs = lds;                            // [ns][CW][P]
-    float* xsum = lds + (size_t)ns * CW * P;    // [ns][P]
-    const bool stage_all = T <= ns;
-
-    if (threadIdx.x < kNcMax) staged_s[threadIdx.x] = -1;
-    if (stage_all) stage_tokens<BITS>(x, H, nullptr, nullptr, T, xs, xsum);   // slot = token
-    const int n_act = load_worklist(a, eid, seg);
-    chunk_prefix(seg, n_act, cpre);
-
-    const int n_seg = cpre[n_act];
-    const long long n_units = (long long)n_seg * I;
-    const long long u0 = n_units * blockIdx.x / gridDim.x;
-    const long long u1 = n_units * (blockIdx.x + 1) / gridDim.x;
-    if (u0 >= u1) return;
-
-    for (int sidx = (int)(u0 / I); (long long)sidx * I < u1; ++sidx) {
-        const int rlo = (int)max(u0 - (long long)sidx * I, 0LL);
-        const int rhi = (int)min(u1 - (long long)sidx * I, (long long)I);
-        const int j = upper_index(cpre, n_act, sidx);
-        const int c = sidx - cpre[j];
-        const int e = eid[j];
-        const int first = seg[j] + c * kNcMax;
-        const int nc = min(kNcMax, seg[j + 1] - first);
-        __syncthreads();   // readers of the previous segment's tokens are done
-        if ((int)threadIdx.x < nc) {
-            const int as = a.assign[first + threadIdx.x];
-            asg_s[threadIdx.x] = as;
-            tok_s[threadIdx.x] = as / a.slots;
-            slot_s[threadIdx.x] = stage_all ? as / a.slots : (int)threadIdx.x;
-        }
-        __syncthreads();
-        if (!stage_all) {
-            bool same = true;
-            for (int k = 0; k < nc; ++k) same = same && staged_s[k] == tok_s[k];
-            if (!same) {
-                stage_tokens<BITS>(x, H, tok_s, slot_s, nc, xs, xsum);
-                __syncthreads();
-                if (threadIdx.x < kNcMax) staged_s[threadIdx.x] = (int)threadIdx.x < nc ? tok_s[threadIdx.x] : -1;
-                __syncthreads();
-            }
-        }
-        switch (nc) {
-            case 1: gate_up_rows<BITS, 1, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
-            case 2: gate_up_rows<BITS, 2, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
-            case 3: gate_up_rows<BITS, 3, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
-            default: gate_up_rows<BITS, 4, LPR, W>(a, h, xs, xsum, slot_s, asg_s, e, rlo, rhi, lpr); break;
-        }
-    }
 }
 
 // ------------------------------------------------------------ down + combine
@@ -456,7 +208,6 @@ __global__ __launch_bounds__(kPThreads) void down_kernel(const float* __restrict
 
 namespace {
 
-constexpr int kGuW = 4;   // gate/up items in flight per wave (2 loads each)
 constexpr int kDnW = 8;   // down items in flight per wave
 constexpr size_t kLdsMax = 160 * 1024;
 // Static LDS of the persistent kernels (worklist copies) plus headroom.
@@ -489,31 +240,6 @@ template <typename Kern>
 hipError_t allow_lds(Kern k, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)bytes);
-}
-
-template <int BITS>
-hipError_t gate_up_bits(const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
-    constexpr int CW = 16 * Codec<BITS>::F;
-    const int P = (a.H * BITS / 8) / 16;
-    const int lpr = lanes_per_row(P);
-    const size_t per_tok = (size_t)(CW * P + P) * sizeof(float);
-    int fit = (int)((kLdsMax - kStaticLds) / per_tok);     // token rows LDS can hold
-    if (fit < kNcMax) return hipErrorInvalidValue;
-    const int ns = a.T <= fit ? a.T : kNcMax;              // all tokens once, else one segment's
-    size_t lds = ns * per_tok;
-    if (lds < kLdsOnePerCu) lds = kLdsOnePerCu;
-    const dim3 grid(cu_count());
-#define MOEDEC_GU(L)                                                              \
-    do {                                                                          \
-        auto k = gate_up_kernel<BITS, L, kGuW>;                                     \
-        hipError_t err = allow_lds(k, lds);                                       \
-        if (err != hipSuccess) return err;                                        \
-        hipLaunchKernelGGL(k, grid, dim3(kPThreads), lds, st, x, a, h, lpr, ns); \
-    } while (0)
-    if (lpr == kWave) MOEDEC_GU(kWave);
-    else MOEDEC_GU(0);
-#undef MOEDEC_GU
-    return hipGetLastError();
 }
 
 template <int BITS>
@@ -552,15 +278,6 @@ hipError_t down_bits(const float* h, const float* topk_w, const ExpertArgs& a, f
 }
 
 }  // namespace
-
-hipError_t launch_gate_up_valu(int bits, const float* x, const ExpertArgs& a, float* h, hipStream_t st) {
-    switch (bits) {
-        case 4: return gate_up_bits<4>(x, a, h, st);
-        case 8: return gate_up_bits<8>(x, a, h, st);
-        case 2: return gate_up_bits<2>(x, a, h, st);
-        default: return hipErrorInvalidValue;
-    }
-}
 
 hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                             hipStream_t st) {

@@ -71,6 +71,7 @@ for _b in ("q4", "q8", "q2"):
                                              _P, _P], _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
+MOEDEC_ERR_DEVICE = 3
 
 # batches from which the separate calls use the expert-major down (each
 # workgroup stages only the h of the experts it streams)
@@ -351,8 +352,17 @@ class LayerBuffers:
                             torch.zeros(FUSED_WORKSPACE_INTS, dtype=torch.int32, device=device), part)
 
     def fused_error(self) -> bool:
-        """True if a fused launch's wait timed out (synchronises)."""
+        """True if a fused launch's wait timed out (synchronises).  While the
+        word is set, the outputs of the launch that set it are invalid."""
         return bool(self.workspace[FUSED_WS_ERROR].item() != 0)
+
+    def check_fused(self, name: str = "moe_layer_fused") -> None:
+        """Raise if a fused launch on this workspace timed out (synchronises);
+        the workspace is zeroed again first, so the next launch starts clean."""
+        if self.fused_error():
+            self.workspace.zero_()
+            raise MoedecError(name, MOEDEC_ERR_DEVICE, "a grid-wide wait of the fused launch timed out (not every "
+                              "workgroup was resident at once: the GPU is shared); its outputs are invalid")
 
 
 def fused_arrivals(workspace: torch.Tensor) -> int:
@@ -368,11 +378,19 @@ def fused_supported(T: int, ex: Experts) -> bool:
 
 def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
                 topk_group: int, top_k: int, rsf: float, buf: LayerBuffers, top_p: float | None = None,
-                x_out: torch.Tensor | None = None, eps: float = 1e-6, act8: bool = False) -> LayerBuffers:
+                x_out: torch.Tensor | None = None, eps: float = 1e-6, act8: bool = False,
+                check: bool | None = None) -> LayerBuffers:
     """moe_layer_fused_q{bits} (moe_layer_fused_topp_q{bits} when top_p is
     given): the whole layer in one launch (outputs in buf).  With x_out:
     moe_layer_fused_resid_q{bits}, x_out = x + MoE(rmsnorm(x)) (x_out may be x).
-    act8: moe_layer_fused_act8_q{bits} (Q8_0-style int8 activations)."""
+    act8: moe_layer_fused_act8_q{bits} (Q8_0-style int8 activations).
+
+    The launch needs every workgroup resident at once; if the GPU is shared
+    and a grid-wide wait times out, the launch ends with invalid outputs and
+    raises the workspace's error word.  check=True synchronises after the
+    launch and raises MoedecError if the word is set (zeroing the workspace);
+    check=None (the default) does so unless the stream is being captured into
+    a graph; check=False leaves it to the caller (buf.check_fused())."""
     T, H = x.shape
     E = ex.n_experts
     if router_w.shape != (E, H) or bias.shape != (E,) or H != ex.hidden:
@@ -403,32 +421,36 @@ def layer_fused(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex:
             _dev(r.topk_w, torch.float32, "topk_w"), ctypes.byref(s_wl), _dev(buf.h, torch.float32, "h"),
             _dev(buf.y, torch.float32, "y"), _dev(buf.workspace, torch.int32, "workspace"), _stream(x))
     _check(name, st)
+    if check or (check is None and not torch.cuda.is_current_stream_capturing()):
+        buf.check_fused(name)
     return buf
 
 
 def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: Experts, *, n_group: int,
               topk_group: int, top_k: int, rsf: float, buf: LayerBuffers | None = None,
-              fused: bool | None = None, top_p: float | None = None, act8: bool = False) -> LayerBuffers:
+              fused: bool | None = None, top_p: float | None = None, act8: bool = False,
+              check: bool | None = None) -> LayerBuffers:
     """One layer on x's stream; returns the buffers (y in .y).  fused=None takes
     the single-launch path where its limits allow, else route_topk ->
-    gate_up_silu -> down_combine; True / False force one of them."""
+    gate_up_silu -> down_combine; True / False force one of them.  check: as
+    for layer_fused (the fused path's timed-out waits)."""
     T = x.shape[0]
     if buf is None:
         buf = LayerBuffers.allocate(T, ex.hidden, ex.inter, ex.n_experts, top_k, ex.n_shared, x.device)
     if act8:                        # only the fused call has int8 activations
         return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
-                           buf=buf, top_p=top_p, act8=True)
+                           buf=buf, top_p=top_p, act8=True, check=check)
     if fused is None:
         if fused_supported(T, ex):
             try:
                 return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k,
-                                   rsf=rsf, buf=buf, top_p=top_p)
+                                   rsf=rsf, buf=buf, top_p=top_p, check=check)
             except MoedecError as err:
                 if err.status != MOEDEC_ERR_UNSUPPORTED:   # the shape does not fit the fused plan
                     raise
     elif fused:
         return layer_fused(x, router_w, bias, ex, n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf,
-                           buf=buf, top_p=top_p)
+                           buf=buf, top_p=top_p, check=check)
     route_topk(x, router_w, bias, n_group=n_group, topk_group=topk_group, top_k=top_k, n_shared=ex.n_shared,
                rsf=rsf, out=buf.route, top_p=top_p)
     gate_up_silu(x, ex, buf.route.worklist, top_k, out=buf.h)
@@ -439,34 +461,53 @@ def moe_layer(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor, ex: E
 
 def stack_forward(x: torch.Tensor, layers: list, bufs: list, *, n_group: int, topk_group: int, top_k: int,
                   rsf: float, eps: float = 1e-6, top_p: float | None = None, fused: bool | None = None,
-                  xn: torch.Tensor | None = None) -> bool:
+                  xn: torch.Tensor | None = None, check: bool | None = None) -> bool:
     """x <- x + MoE_l(rmsnorm(x)) for every layer l, in place on x (the
     pre-norm residual stack).  layers[l] = (router_w, bias, Experts); bufs[l]
     a LayerBuffers.  Fused: one moe_layer_fused_resid launch per layer (the
     norm and the residual inside it); else the separate calls with
     moe_residual_rmsnorm between them (xn: a [T, H] scratch for the normalised
     tokens).  fused=None tries the fused form on the first layer and keeps
-    whichever runs; returns whether the fused form ran."""
+    whichever runs; returns whether the fused form ran.
+
+    A fused layer whose grid-wide wait timed out writes an invalid x for every
+    later layer; check=True (or None outside graph capture) synchronises once
+    after the last layer and raises MoedecError if any layer's workspace
+    reports it (zeroing those workspaces)."""
     T, H = x.shape
     kw = dict(n_group=n_group, topk_group=topk_group, top_k=top_k, rsf=rsf)
+    if check is None:
+        check = not torch.cuda.is_current_stream_capturing()
+
+    def run_fused(items) -> None:
+        for (rw, b, ex), buf in items:
+            layer_fused(x, rw, b, ex, buf=buf, top_p=top_p, x_out=x, eps=eps, check=False, **kw)
+
+    def finish() -> bool:
+        if check:
+            bad = [buf for buf in bufs if buf.fused_error()]
+            for buf in bad:
+                buf.workspace.zero_()
+            if bad:
+                raise MoedecError("moe_layer_fused_resid", MOEDEC_ERR_DEVICE,
+                                  f"{len(bad)} layer(s) timed out in a grid-wide wait; x is invalid")
+        return True
+
     if fused is None:
         fused = fused_supported(T, layers[0][2])
         if fused:
             try:
-                rw, b, ex = layers[0]
-                layer_fused(x, rw, b, ex, buf=bufs[0], top_p=top_p, x_out=x, eps=eps, **kw)
+                run_fused(list(zip(layers, bufs))[:1])
             except MoedecError as err:
                 if err.status != MOEDEC_ERR_UNSUPPORTED:
                     raise
                 fused = False
             else:
-                for (rw, b, ex), buf in zip(layers[1:], bufs[1:]):
-                    layer_fused(x, rw, b, ex, buf=buf, top_p=top_p, x_out=x, eps=eps, **kw)
-                return True
+                run_fused(list(zip(layers, bufs))[1:])
+                return finish()
     if fused:
-        for (rw, b, ex), buf in zip(layers, bufs):
-            layer_fused(x, rw, b, ex, buf=buf, top_p=top_p, x_out=x, eps=eps, **kw)
-        return True
+        run_fused(list(zip(layers, bufs)))
+        return finish()
     if xn is None:
         xn = torch.empty_like(x)
     residual_rmsnorm(x, None, xn, eps)
