@@ -17,7 +17,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoedec.so")
-HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moedec.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "moedec.h")
 
 MAX_TOKENS = 64
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "device error"}
@@ -53,6 +54,7 @@ _SIGS = {
     "moe_route_topk": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P], _I),
     "moe_route_topp": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P], _I),
     "moe_residual_rmsnorm": ([_P, _P, _P, _I, _I, _F, _P], _I),
+    "moe_bench_stream_read": ([_P, _I64, _P, _I, _I, _I, _P], _I),
 }
 for _b in ("q4", "q8", "q2"):
     _SIGS[f"moe_expert_gate_up_silu_{_b}"] = ([_P, _P, _P, _I, _I, _P, _P], _I)
@@ -101,11 +103,14 @@ def lib() -> ctypes.CDLL:
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/moedec.h declares."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:moe|moedec)_\w+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for name in sorted(os.listdir(INCLUDE_DIR)):
+        if name.endswith(".h"):
+            with open(os.path.join(INCLUDE_DIR, name)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names |= set(re.findall(r"\b((?:moe|moedec)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def _check(fn: str, status: int) -> None:
@@ -319,6 +324,20 @@ def quantize_rows(w: torch.Tensor, bits: int, pack: bool = False, out: torch.Ten
             _dev(scales, torch.float32, "scales"), rows, n, _stream(w))
     _check(name, st)
     return out, scales
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, threads: int = 512, unroll: int = 8,
+                nbytes: int | None = None) -> None:
+    """moe_bench_stream_read: a plain streaming read of buf (a measurement
+    aid, not part of the path); sink: uint32 [grid * threads]."""
+    nb = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if not buf.is_cuda or not buf.is_contiguous() or nb > buf.numel() * buf.element_size():
+        raise ValueError("buf must be a contiguous GPU tensor holding nbytes")
+    if sink.numel() < grid * threads:
+        raise ValueError("sink must hold grid * threads words")
+    st = lib().moe_bench_stream_read(buf.data_ptr(), nb, _dev(sink, torch.int32, "sink"), grid, threads, unroll,
+                                     _stream(buf))
+    _check("moe_bench_stream_read", st)
 
 
 def residual_rmsnorm(x: torch.Tensor, y: torch.Tensor | None, xn: torch.Tensor, eps: float = 1e-6) -> None:

@@ -1,5 +1,5 @@
-"""The C-ABI library: it loads, exports every function include/moedec.h
-declares, and rejects bad arguments before anything reaches a device (these
+"""The C-ABI library: it loads, exports every function the headers under
+include/ declare, and rejects bad arguments before anything reaches a device (these
 calls return from host-side validation, so they run without a GPU)."""
 import ctypes
 import os
@@ -19,9 +19,24 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = ops.header_functions()
-    assert len(names) == 38
+    assert len(names) == 39
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_stream_read_validation(lib):
+    """moe_bench_stream_read rejects bad sizes and launch shapes on the host."""
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    sink = ctypes.c_void_p(1 << 21)
+    f = lib.moe_bench_stream_read
+    assert f(None, 1024, sink, 1, 256, 8, None) == 1
+    assert f(fake, 1000, sink, 1, 256, 8, None) == 1           # not a multiple of 16
+    assert f(fake, 0, sink, 1, 256, 8, None) == 1
+    assert f(ctypes.c_void_p((1 << 20) + 4), 1024, sink, 1, 256, 8, None) == 1   # misaligned
+    assert f(fake, 1024, sink, 0, 256, 8, None) == 1
+    assert f(fake, 1024, sink, 1, 384, 8, None) == 1
+    assert f(fake, 1024, sink, 1, 256, 3, None) == 1
+    assert f(fake, 1024, None, 1, 256, 8, None) == 1
 
 
 def test_struct_layouts():
