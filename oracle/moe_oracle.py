@@ -304,17 +304,21 @@ def selection_margin(scores64: np.ndarray, bias: np.ndarray, n_group: int, topk_
     per = E // n_group
     out = np.full(T, np.inf)
     for t in range(T):
-        c = s[t] + b
-        gs = np.array([np.sort(c[g * per:(g + 1) * per])[-2:].sum() for g in range(n_group)])
+        with np.errstate(invalid="ignore"):
+            c = s[t] + b
+            c = np.where(np.isnan(c), -np.inf, c)                # R6: NaN ranks as -inf
+            gs = np.array([np.sort(c[g * per:(g + 1) * per])[-2:].sum() for g in range(n_group)])
+        gs = np.where(np.isnan(gs), -np.inf, gs)                 # R6: +inf + -inf ranks as -inf
         order = np.argsort(-gs, kind="stable")
         m = np.inf
-        if topk_group < n_group:
-            m = gs[order[topk_group - 1]] - gs[order[topk_group]]
-        kept = order[:topk_group]
-        cand = np.sort(np.concatenate([c[g * per:(g + 1) * per] for g in kept]))[::-1]
-        if top_k < len(cand):
-            m = min(m, cand[top_k - 1] - cand[top_k])
-        out[t] = m
+        with np.errstate(invalid="ignore"):
+            if topk_group < n_group:
+                m = gs[order[topk_group - 1]] - gs[order[topk_group]]
+            kept = order[:topk_group]
+            cand = np.sort(np.concatenate([c[g * per:(g + 1) * per] for g in kept]))[::-1]
+            if top_k < len(cand):
+                m = min(m, cand[top_k - 1] - cand[top_k])
+        out[t] = m if not np.isnan(m) else 0.0       # inf - inf: ties between infinities decide by index
     return out
 
 
@@ -322,12 +326,16 @@ def order_margin(scores64: np.ndarray, bias: np.ndarray, idx: np.ndarray) -> np.
     """Per token, the smallest fp64 gap between the corrected scores of
     consecutive chosen slots (infinite for one slot): where it is wide, the
     slot order is the same for any correct fp32 implementation."""
-    c = np.asarray(scores64, np.float64) + np.asarray(bias, np.float64)
+    with np.errstate(invalid="ignore"):
+        c = np.asarray(scores64, np.float64) + np.asarray(bias, np.float64)
+    c = np.where(np.isnan(c), -np.inf, c)                         # R6
     out = np.full(idx.shape[0], np.inf)
     for t in range(idx.shape[0]):
         v = c[t, idx[t][idx[t] >= 0]]
         if len(v) > 1:
-            out[t] = float(np.min(v[:-1] - v[1:]))
+            with np.errstate(invalid="ignore"):
+                d = v[:-1] - v[1:]
+            out[t] = float(np.min(np.where(np.isnan(d), 0.0, d)))   # equal infinities: no margin
     return out
 
 

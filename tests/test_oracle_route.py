@@ -206,3 +206,21 @@ def test_batch_union_invariants():
         for a in seg:
             t, slot = divmod(int(a), K + S)
             assert (idx[t, slot] == e) if slot < K else (e == E)
+
+
+def test_margins_follow_the_nonfinite_reading():
+    """The certificates rank NaN and +inf + -inf group scores as -inf (R6),
+    as the selection itself does: worked rows."""
+    s = np.array([[0.9, 0.8, 0.7, 0.6, 0.5, 0.4, 0.3, 0.2]])
+    b = np.array([np.nan, 0, 0, 0, 0, 0, 0, 0], np.float32)
+    idx, _ = orc.select_experts(s.astype(np.float32), b, 1, 1, 3, 2.5)
+    assert idx.tolist() == [[1, 2, 3]]                          # expert 0 ranks as -inf
+    assert abs(orc.selection_margin(s, b, 1, 1, 3)[0] - 0.1) < 1e-12   # c[3] - c[4]
+    assert abs(orc.order_margin(s, b, idx)[0] - 0.1) < 1e-12
+    # group 0 = experts {0, 1} holds +inf and -inf: its score is NaN and ranks last
+    b2 = np.zeros(8, np.float32)
+    b2[0], b2[1] = np.inf, -np.inf
+    idx2, _ = orc.select_experts(s.astype(np.float32), b2, 4, 2, 2, 2.5)
+    assert idx2.tolist() == [[2, 3]]                            # groups 1 (1.3) and 2 (0.9) kept
+    m = orc.selection_margin(s, b2, 4, 2, 2)[0]
+    assert abs(m - 0.1) < 1e-12                                 # min(gs[2] - gs[3] = 0.4, c[3] - c[4] = 0.1)

@@ -264,8 +264,7 @@ MUTANTS = {
     # the stream is normalised after the residual add
     "norm_after_add": ("x = x + r.y", "x = rmsnorm(x + r.y)", ["stack_zero_down", "stack_closed_form"]),
     # the order margin skips the last gap
-    "order_margin_short": ("out[t] = float(np.min(v[:-1] - v[1:]))",
-                           "out[t] = float(np.min((v[:-1] - v[1:])[:-1])) if len(v) > 2 else np.inf",
+    "order_margin_short": ("d = v[:-1] - v[1:]", "d = (v[:-1] - v[1:])[:-1] if len(v) > 2 else np.array([np.inf])",
                            ["order_margin"]),
     # the top-p margin measured against p of the total without the prefix sums' nearest point
     "topp_margin_first_only": ("m = np.min(np.abs(cum - top_p * total)) / max(total, 1e-300)",
