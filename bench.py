@@ -45,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc")
 # sources each timed kernel is built from (the traffic counters are void once any changes)
-KERNEL_SRCS = {"fused": ["layer_fused.hip", "imma.h", "persist.h", "route.h", "common.h"],
+KERNEL_SRCS = {"fused": ["layer_pipe.hip", "imma.h", "persist.h", "route.h", "common.h"],
                "gate_up": ["experts_mfma.hip", "mfma.h", "common.h"],
                "quantize": ["quant.hip", "common.h"]}
 
@@ -218,12 +218,21 @@ PAGES_CONTEXT = {
 }
 
 
-def step_dtype(bits: int, fused: bool, act8: bool, x24: bool = False) -> str:
+def fused_kernel_name(cfg, top_p, act8: bool, resid: bool) -> str:
+    """The kernel a fused call launches (as the profiler names it)."""
+    tp = "true" if top_p is not None and top_p < 1 else "false"
+    if act8:
+        return f"layer_fused_kernel<{cfg.bits}, {tp}, false, true>"
+    np_ = 1 if 3 * cfg.tokens <= 16 else 3
+    return f"layer_pipe_kernel<{cfg.bits}, {np_}, {tp}, {'true' if resid else 'false'}>"
+
+
+def step_dtype(bits: int, fused: bool, act8: bool) -> str:
     """The arithmetic the timed step computes in."""
     if act8:
         return f"int{bits} codes x int8 activation blocks -> int32, fp32 block scales and sums"
     if fused:
-        return f"int{bits} codes x int{24 if x24 else 16} activations -> exact int32, fp32 scales and sums"
+        return f"int{bits} codes x int24 activations -> exact int32, fp32 scales and sums"
     return f"int{bits} codes -> f16, f16 hi/lo activations, fp32 accumulate"
 
 
@@ -426,8 +435,7 @@ def bench_stack(args, cfg) -> None:
     torch.cuda.synchronize()
     dur = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
-    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, "
-             f"true>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
+    kname = fused_kernel_name(cfg, args.top_p, False, True) if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
     print(f"[bench] {kname} avg {dur.mean() * 1e6:.1f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
     base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
     out = {
@@ -755,8 +763,7 @@ def bench_layer(args, cfg) -> None:
         kdur = np.array(times)
     achieved = float(np.mean(kb) / kdur.mean() / 1e9)
     traffic = traffic_from_profile(kind, cfg.name) if args.top_p is None and not args.act8 else None
-    kname = (f"layer_fused_kernel<{cfg.bits}, {'true' if args.top_p is not None and args.top_p < 1 else 'false'}, "
-             f"false, {'true' if args.act8 else 'false'}>" if fused else f"gate_up_mfma_kernel<{cfg.bits}>")
+    kname = fused_kernel_name(cfg, args.top_p, args.act8, False) if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_us": round(float(kdur.mean() * 1e6), 2),

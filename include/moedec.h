@@ -210,16 +210,25 @@ int moe_expert_down_combine_em_q2(const float* h, const moedec_experts* ex, cons
  * then the gate/up and down calls, fused (same passages as those three calls;
  * Show HN page, "implemented features").  Arguments and outputs are those of
  * the three calls; E = ex->n_experts, H = ex->hidden, S = ex->n_shared.
+ * The experts are streamed one after another (shared experts first), each
+ * expert's down rows a few experts after its gate/up rows, and activations
+ * meet the codes as exact 24-bit integers under one power-of-two scale per
+ * token (and per staged h row), so the products are exact but for that
+ * rounding (2^-23 of the column's largest magnitude).
  *   x, router_w, bias          : as for moe_route_topk
  *   scores, topk_idx, topk_w   : as for moe_route_topk
  *   wl                         : required; filled as moe_route_topk fills it
- *   h                          : fp32 [T*(top_k+S), inter] (the gate/up result)
+ *   h                          : fp32 [T*(top_k+S), inter] (the gate/up result;
+ *                                rows from wl's assignment count on hold
+ *                                unspecified values)
  *   y                          : fp32 [T, H] (the layer output)
  *   workspace : int32 [MOEDEC_FUSED_WORKSPACE_INTS], device memory the caller
  *       zeroes once before the first call and then leaves to the library; it
- *       holds the arrival counters of the launch's two grid-wide exchanges, so
+ *       holds the arrival counters of the launch's grid-wide exchanges, so
  *       launches that may run at the same time need separate workspaces, and
- *       one workspace serves one GPU.  After the call (once the stream has
+ *       one workspace serves one GPU (the plain, top-p and residual calls
+ *       count on words 1024 .. 1279, the int8-activation call on words
+ *       0 .. 511, so the two kinds may share one).  After the call (once the stream has
  *       reached it) workspace[MOEDEC_FUSED_WS_ERROR] != 0 means a wait timed
  *       out: not every workgroup could be resident at once (the GPU was
  *       shared with other work); that call's outputs are invalid and the
@@ -231,7 +240,7 @@ int moe_expert_down_combine_em_q2(const float* h, const moedec_experts* ex, cons
  * n_experts <= MOEDEC_FUSED_MAX_EXPERTS, else MOEDEC_ERR_UNSUPPORTED (use the
  * separate calls).
  */
-#define MOEDEC_FUSED_WORKSPACE_INTS 1024
+#define MOEDEC_FUSED_WORKSPACE_INTS 4096
 #define MOEDEC_FUSED_WS_ERROR 512
 #define MOEDEC_FUSED_WS_SPIN 513
 #define MOEDEC_FUSED_MAX_TOKENS 16

@@ -17,7 +17,7 @@ using namespace moedec;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -141,7 +141,8 @@ int layer_fused(int bits, const float* x, const float* router_w, const float* bi
     f.x_out = x_out;
     f.eps = eps;
     f.act8 = act8;
-    const hipError_t err = launch_layer_fused(bits, f, static_cast<hipStream_t>(stream));
+    const hipError_t err = act8 ? launch_layer_fused(bits, f, static_cast<hipStream_t>(stream))
+                                : launch_layer_pipe(bits, f, static_cast<hipStream_t>(stream));
     if (err == hipErrorInvalidValue) return MOEDEC_ERR_UNSUPPORTED;   // shapes the LDS plan cannot hold
     return device_status(err);
 }

@@ -215,7 +215,8 @@ struct FusedLayerArgs {
     int act8;                  // 1: Q8_0-style int8 activations in blocks
 };
 
-hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);
+hipError_t launch_layer_fused(int bits, const FusedLayerArgs& args, hipStream_t stream);   // int8 activations
+hipError_t launch_layer_pipe(int bits, const FusedLayerArgs& args, hipStream_t stream);    // 24-bit activations
 
 hipError_t launch_pack(int bits, const int8_t* codes, uint8_t* packed, int64_t rows, int64_t row_len,
                        hipStream_t stream);

@@ -1351,13 +1351,13 @@ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 // starts][chunk tables]; the chunk size qc is the largest that fits.
 template <int BITS>
 hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st) {
+    // only the int8-activation form is launched here (the other calls run the
+    // pipelined kernel); it has no residual form
     const bool topp = f.top_p < 1.f, resid = f.x_out != nullptr, q8 = f.act8 != 0;
-    if (q8 && resid) return hipErrorInvalidValue;                   // not instantiated together
-    auto k = q8 ? (topp ? layer_fused_kernel<BITS, true, false, true> : layer_fused_kernel<BITS, false, false, true>)
-        : resid ? (topp ? layer_fused_kernel<BITS, true, true, false> : layer_fused_kernel<BITS, false, true, false>)
-                : (topp ? layer_fused_kernel<BITS, true, false, false> : layer_fused_kernel<BITS, false, false, false>);
-    static size_t static_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};      // each variant's static LDS, read once
-    size_t& static_lds = static_cache[topp][q8 ? 2 : resid ? 1 : 0];
+    if (!q8 || resid) return hipErrorInvalidValue;
+    auto k = topp ? layer_fused_kernel<BITS, true, false, true> : layer_fused_kernel<BITS, false, false, true>;
+    static size_t static_cache[2] = {0, 0};                         // each variant's static LDS, read once
+    size_t& static_lds = static_cache[topp];
     if (static_lds == 0) {
         hipFuncAttributes attr;
         hipError_t err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k));

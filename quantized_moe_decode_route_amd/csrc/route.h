@@ -213,14 +213,18 @@ __device__ __forceinline__ void route_one_token(const float* scores, const float
 // other workgroups of the same launch have just written), else plain loads.
 // kTopP: compile the top-p step in (top_p is read only then; without it the
 // selection is plain top-k and the code stays as small as before).
-template <int TM, int EM, int NW, bool kCoherentScores = false, bool kTopP = false>
+// kLastWaves: token t is routed by wave NW-1-(t % NW) and a one-wave union
+// runs on wave NW-1, so the first waves issue no loads here (their own
+// loads, already in flight, are not waited for).
+template <int TM, int EM, int NW, bool kCoherentScores = false, bool kTopP = false, bool kLastWaves = false>
 __device__ __forceinline__ void route_select_block(const float* scores, const float* __restrict__ bias, int T,
                                                    int E, int n_group, int topk_group, int top_k, int n_shared,
                                                    float rsf, float top_p, RouteLdsT<TM, EM, NW>& r) {
     constexpr int NV = EM / kWave;                    // experts per lane at most
     constexpr int NV4 = NV < 4 ? NV : 4;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
     const int nwaves = blockDim.x / kWave;
+    const int wave = kLastWaves ? nwaves - 1 - (int)(threadIdx.x / kWave) : (int)(threadIdx.x / kWave);
     for (int t = wave; t < T; t += nwaves) {
         if (NV == NV4 || E <= NV4 * kWave)
             route_one_token<NV4, TM, EM, NW, kCoherentScores, kTopP>(scores, bias, t, E, n_group, topk_group, top_k,
@@ -235,7 +239,7 @@ __device__ __forceinline__ void route_select_block(const float* scores, const fl
     const int slots = top_k + n_shared;
     const int A = T * slots;
     if (A <= kWave) {                  // one wave, no workgroup barriers
-        if (wave == 0) {
+        if (wave == 0) {                // (the last wave with kLastWaves)
             int k = INT_MAX;                   // a dropped slot keeps INT_MAX: sorted last, not written
             if (lane < A) {
                 const int tt = lane / slots, s = lane - tt * slots;

@@ -82,9 +82,13 @@ DOWN_EM_MIN_TOKENS = 8
 # limits of the fused layer call (include/moedec.h)
 FUSED_MAX_TOKENS = 16
 FUSED_MAX_EXPERTS = 512
-FUSED_WORKSPACE_INTS = 1024
+FUSED_WORKSPACE_INTS = 4096
 FUSED_WS_ERROR = 512            # workspace word: a wait timed out
 FUSED_WS_GATES, FUSED_WS_GATE_STRIDE = 8, 64   # arrival counters (int64) every 64 int32 words
+# the plain / top-p / residual fused calls: the scores exchange's counters
+# (int64) at words PIPE_WS_BASE + i * PIPE_WS_STRIDE, i < FUSED_WS_GATES
+PIPE_WS_BASE = 1024
+PIPE_WS_STRIDE = 32            # words between a gate's counters
 
 
 def lib() -> ctypes.CDLL:
@@ -385,10 +389,18 @@ class LayerBuffers:
 
 
 def fused_arrivals(workspace: torch.Tensor) -> int:
-    """Arrivals counted in a fused-call workspace so far: the sum of its
-    counters (synchronises).  Each launch adds two per workgroup."""
+    """Arrivals the int8-activation fused call counted in a workspace so far:
+    the sum of its counters (synchronises).  Each launch adds two per workgroup."""
     c = workspace[:FUSED_WS_GATES * FUSED_WS_GATE_STRIDE].view(torch.int64)[::FUSED_WS_GATE_STRIDE // 2]
     return int(c.sum().item())
+
+
+def pipe_arrivals(workspace: torch.Tensor) -> int:
+    """Arrivals the plain / top-p / residual fused calls counted on a
+    workspace's scores exchange so far, one per workgroup per launch
+    (synchronises)."""
+    c = workspace[PIPE_WS_BASE:PIPE_WS_BASE + FUSED_WS_GATES * PIPE_WS_STRIDE].view(torch.int64)
+    return int(c[::PIPE_WS_STRIDE // 2].sum().item())
 
 
 def fused_supported(T: int, ex: Experts) -> bool:

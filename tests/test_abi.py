@@ -49,7 +49,7 @@ def test_status_strings(lib):
     assert lib.moedec_status_string(0) == b"ok"
     assert lib.moedec_status_string(1) == b"invalid argument"
     assert lib.moedec_status_string(99) == b"unknown status"
-    assert lib.moedec_abi_version() == 1
+    assert lib.moedec_abi_version() == 2
 
 
 FAKE = 1 << 20       # an aligned, never-dereferenced address
@@ -231,3 +231,5 @@ def test_binding_constants_match_the_header():
     assert defs["MOEDEC_FUSED_MAX_TOKENS"] == ops.FUSED_MAX_TOKENS
     assert defs["MOEDEC_FUSED_MAX_EXPERTS"] == ops.FUSED_MAX_EXPERTS
     assert ops.FUSED_WS_GATES * ops.FUSED_WS_GATE_STRIDE <= ops.FUSED_WS_ERROR
+    end = ops.PIPE_WS_BASE + ops.FUSED_WS_GATES * ops.PIPE_WS_STRIDE
+    assert ops.FUSED_WS_ERROR < ops.PIPE_WS_BASE and end <= ops.FUSED_WORKSPACE_INTS

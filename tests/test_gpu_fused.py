@@ -1,8 +1,9 @@
 """The single-launch layer call beyond plain parity: every launch adds exactly
-two arrivals per workgroup (the scores exchange and the h exchange) to the
-workspace counters, and launches back to back on one workspace and HIP-graph
-replays give the eager results bit for bit (every reduction in the kernel has
-a fixed order, so equal inputs give equal bits)."""
+one arrival per workgroup to the scores exchange's counters of the
+workspace, and launches back to back on one workspace and HIP-graph replays
+give the eager results bit for bit (every reduction in the kernel has a fixed
+order, so equal inputs give equal bits; rows of h no token is assigned to
+hold a marker, compared as bits too)."""
 import numpy as np
 import pytest
 import torch
@@ -38,6 +39,10 @@ def _tokens(pool, i):
     return pool[b * T:(b + 1) * T]
 
 
+def _bits(a):
+    return a.view(torch.int32) if a.dtype == torch.float32 else a
+
+
 def _eager(layers, experts, pool, i):
     l = i % len(layers)
     buf = ops.moe_layer(_tokens(pool, i), layers[l]["router_w"], layers[l]["bias"], experts[l], fused=True, **KW)
@@ -58,15 +63,15 @@ def test_back_to_back_launches_share_a_workspace():
                       fused=True, **KW)
     torch.cuda.synchronize()
     nwg = torch.cuda.get_device_properties(DEV).multi_processor_count
-    count = ops.fused_arrivals(ws)
+    count = ops.pipe_arrivals(ws)
     err = int(ws[ops.FUSED_WS_ERROR].item())
-    say(f"  workspace after {n} launches: arrivals {count} (2 x {nwg} workgroups each), error {err}")
-    assert count == 2 * n * nwg and err == 0
+    say(f"  workspace after {n} launches: arrivals {count} ({nwg} workgroups), error {err}")
+    assert count == n * nwg and err == 0
     for i in range(n):
         for a, b in ((bufs[i].y, ref[i].y), (bufs[i].h, ref[i].h), (bufs[i].route.scores, ref[i].route.scores),
                      (bufs[i].route.topk_idx, ref[i].route.topk_idx), (bufs[i].route.topk_w, ref[i].route.topk_w),
                      (bufs[i].route.worklist.assign, ref[i].route.worklist.assign)):
-            assert torch.equal(a, b), f"launch {i} differs from its eager run"
+            assert torch.equal(_bits(a), _bits(b)), f"launch {i} differs from its eager run"
 
 
 def test_graph_replays_match_eager():
@@ -92,8 +97,8 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert not buf.fused_error()
         for a, b in ((buf.y, ref[i].y), (buf.h, ref[i].h), (buf.route.topk_idx, ref[i].route.topk_idx)):
-            assert torch.equal(a, b), f"replay {i} differs from the eager run"
+            assert torch.equal(_bits(a), _bits(b)), f"replay {i} differs from the eager run"
     nwg = torch.cuda.get_device_properties(DEV).multi_processor_count
     # the warm-up launch and n replays (capture runs nothing)
-    assert ops.fused_arrivals(buf.workspace) == 2 * (n + 1) * nwg
+    assert ops.pipe_arrivals(buf.workspace) == (n + 1) * nwg
 

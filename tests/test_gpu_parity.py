@@ -92,11 +92,11 @@ def test_one_hot_expert_closed_form(fused):
     one-hot token: the output is the closed form of that single expert.
 
     The split calls carry activations as an f16 hi/lo pair (about 22 bits):
-    within 1e-5 of the largest output.  The fused call carries them as 16-bit
+    within 1e-5 of the largest output.  The fused call carries them as 24-bit
     integers with a power-of-two scale per column, and its integer products
     are exact, so its error is what rounding the weighted h (2.5 h) to that
-    grid allows: at most half a step, max|2.5 h| / 32512, per element, times
-    the row's sum of |code| * scale, plus fp32 rounding of the rest."""
+    grid allows: at most half a step, max|2.5 h| / 8323072, per element,
+    times the row's sum of |code| * scale, plus fp32 rounding of the rest."""
     cfg = synth.MoEConfig("onehot", 1, 256, 128, 16, 1, 1, 1, 1, 4, seed=3)
     lay = synth.layer_device(cfg, 0, DEV)
     lay["bias"].zero_()
@@ -121,7 +121,7 @@ def test_one_hot_expert_closed_form(fused):
         assert err <= 1e-5
         return
     m = 2.5 * np.abs(hv).max()
-    bound = sd * (np.abs(qd) @ np.ones_like(hv)) * m * (1.0 / 32512 + 2e-6)
+    bound = sd * (np.abs(qd) @ np.ones_like(hv)) * m * (1.0 / 8323072 + 2e-6)
     worst = (np.abs(g["y"][0] - want) / bound).max()
     say(f"  fused: largest error / bound {worst:.3f}")
     assert worst <= 1.0
