@@ -206,6 +206,25 @@ int moe_expert_down_combine_em_q2(const float* h, const moedec_experts* ex, cons
                                   float* y, void* stream);
 
 /*
+ * moe_expert_down_combine_em_q4 without the part argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The partial outputs go to a
+ * static array of MOEDEC_NOALLOC_PART_FLOATS floats (4 MiB) that the library
+ * holds on each GPU it runs on until the process ends; the call allocates
+ * nothing.  Every call on one GPU shares that GPU's array, so calls that may
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  Results are those of
+ * moe_expert_down_combine_em_q4 bit for bit.  T*(top_k+S)*hidden >
+ * MOEDEC_NOALLOC_PART_FLOATS: MOEDEC_ERR_UNSUPPORTED (use the _em call with
+ * a caller buffer).  Other arguments, layouts and errors as for
+ * moe_expert_down_combine_em_q4.
+ */
+#define MOEDEC_NOALLOC_PART_FLOATS (1 << 20)
+int moe_expert_down_combine_em_noalloc_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
+                                          const float* topk_w, const int32_t* topk_idx, int T, int top_k, float* y,
+                                          void* stream);
+
+/*
  * The whole layer step in one launch: moe_route_topk (with the worklist),
  * then the gate/up and down calls, fused (same passages as those three calls;
  * Show HN page, "implemented features").  Arguments and outputs are those of

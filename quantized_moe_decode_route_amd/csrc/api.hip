@@ -238,6 +238,18 @@ MOEDEC_API int moe_expert_down_combine_em_q4(const float* h, const moedec_expert
                                              float* part, float* y, void* stream) {
     return down_em(4, h, ex, wl, topk_w, topk_idx, T, top_k, part, y, stream);
 }
+MOEDEC_API int moe_expert_down_combine_em_noalloc_q4(const float* h, const moedec_experts* ex,
+                                                     const moedec_worklist* wl, const float* topk_w,
+                                                     const int32_t* topk_idx, int T, int top_k, float* y,
+                                                     void* stream) {
+    if (!h || !topk_w || !y) return MOEDEC_ERR_INVALID_ARG;
+    ExpertArgs a;
+    const int st = check_experts(ex, wl, 4, T, top_k, a);
+    if (st != MOEDEC_OK) return st;
+    if (!aligned16(h)) return MOEDEC_ERR_INVALID_ARG;
+    if ((long long)a.T * a.slots * a.H > MOEDEC_NOALLOC_PART_FLOATS) return MOEDEC_ERR_UNSUPPORTED;
+    return device_status(launch_down_em_noalloc(4, h, topk_w, topk_idx, a, y, static_cast<hipStream_t>(stream)));
+}
 MOEDEC_API int moe_expert_down_combine_q4(const float* h, const moedec_experts* ex, const moedec_worklist* wl,
                                           const float* topk_w, int T, int top_k, float* y, void* stream) {
     return down(4, h, ex, wl, topk_w, T, top_k, y, stream);

@@ -188,6 +188,10 @@ hipError_t launch_down_valu(int bits, const float* h, const float* topk_w, const
 
 hipError_t launch_down_em(int bits, const float* h, const float* topk_w, const int32_t* topk_idx, const ExpertArgs& a,
                           float* part, float* y, hipStream_t stream);
+// launch_down_em with its partial outputs in the library's per-device static
+// array (hipErrorInvalidValue when T * slots * H exceeds it)
+hipError_t launch_down_em_noalloc(int bits, const float* h, const float* topk_w, const int32_t* topk_idx,
+                                  const ExpertArgs& a, float* y, hipStream_t stream);
 hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,
                        hipStream_t stream);
 

@@ -6,6 +6,8 @@
 // The codes of each selected expert are streamed from HBM exactly once per
 // token batch (the batch union of the worklist): one persistent 8-wave
 // workgroup per compute unit, each owning a contiguous share of the rows.
+#include <mutex>
+
 #include "mfma.h"
 
 namespace moedec {
@@ -347,6 +349,48 @@ hipError_t launch_down_em(int bits, const float* h, const float* topk_w, const i
         case 2: return down_em_bits<2>(h, topk_w, topk_idx, a, part, y, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ------------------------------------------------ the no-allocation down call
+//
+// The expert-major down call with its partial outputs in a file-scope device
+// array instead of a caller buffer, for callers that cannot allocate.  Each
+// GPU holds its own copy of the array until the process ends; the host finds
+// its address once per device with hipGetSymbolAddress (the array's name in
+// host code is not a device address).  Every call on a GPU reuses that GPU's
+// array, so calls that overlap on one GPU race; every row a call reads back
+// was written earlier in the same call, so nothing needs clearing.
+static __device__ __align__(256) float scratch[MOEDEC_NOALLOC_PART_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_part(float** out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float*>(g_scratch_ptr[dev]);
+    return hipSuccess;
+}
+
+hipError_t launch_down_em_noalloc(int bits, const float* h, const float* topk_w, const int32_t* topk_idx,
+                                  const ExpertArgs& a, float* y, hipStream_t st) {
+    if ((long long)a.T * a.slots * a.H > MOEDEC_NOALLOC_PART_FLOATS) return hipErrorInvalidValue;
+    float* part = nullptr;
+    const hipError_t err = noalloc_part(&part);
+    if (err != hipSuccess) return err;
+    return launch_down_em(bits, h, topk_w, topk_idx, a, part, y, st);
 }
 
 hipError_t launch_down(int bits, const float* h, const float* topk_w, const ExpertArgs& a, float* y,

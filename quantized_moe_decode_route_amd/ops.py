@@ -71,6 +71,7 @@ for _b in ("q4", "q8", "q2"):
                                            _I)
     _SIGS[f"moe_layer_fused_resid_{_b}"] = ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P], _I)
+_SIGS["moe_expert_down_combine_em_noalloc_q4"] = ([_P, _P, _P, _P, _P, _I, _I, _P, _P], _I)
 
 MOEDEC_ERR_UNSUPPORTED = 2
 MOEDEC_ERR_DEVICE = 3
@@ -285,6 +286,30 @@ def down_combine(h: torch.Tensor, ex: Experts, wl: Worklist, topk_w: torch.Tenso
     st = fn(_dev(h, torch.float32, "h"), ctypes.byref(s_ex), ctypes.byref(s_wl),
             _dev(topk_w, torch.float32, "topk_w"), T, top_k, _dev(out, torch.float32, "y"), _stream(h))
     _check(fn.__name__, st)
+    return out
+
+
+NOALLOC_PART_FLOATS = 1 << 20   # the static partial-output array of the no-allocation down call
+
+
+def down_combine_noalloc(h: torch.Tensor, ex: Experts, wl: Worklist, topk_w: torch.Tensor, top_k: int,
+                         out: torch.Tensor, topk_idx: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_expert_down_combine_em_noalloc_q4: the expert-major down call with
+    its partial outputs in the library's static per-GPU array (int4 experts;
+    T*(top_k+S)*hidden <= NOALLOC_PART_FLOATS; calls on one GPU must not
+    overlap).  Allocates nothing: out must be given."""
+    T = topk_w.shape[0]
+    if ex.bits != 4:
+        raise ValueError("the no-allocation down call takes int4 experts")
+    if out.shape != (T, ex.hidden) or h.shape != (T * (top_k + ex.n_shared), ex.inter):
+        raise ValueError("shape mismatch between h, topk_w and y")
+    s_ex, s_wl = ex.struct(), wl.struct()
+    idx = _dev(topk_idx, torch.int32, "topk_idx") if topk_idx is not None else None
+    name = "moe_expert_down_combine_em_noalloc_q4"
+    st = getattr(lib(), name)(_dev(h, torch.float32, "h"), ctypes.byref(s_ex), ctypes.byref(s_wl),
+                              _dev(topk_w, torch.float32, "topk_w"), idx, T, top_k, _dev(out, torch.float32, "y"),
+                              _stream(h))
+    _check(name, st)
     return out
 
 
