@@ -75,9 +75,6 @@ using namespace imma;
 #ifndef MOEDEC_PIPE_RING
 #define MOEDEC_PIPE_RING 4
 #endif
-#ifndef MOEDEC_PIPE_PF
-#define MOEDEC_PIPE_PF 1
-#endif
 #ifndef MOEDEC_PIPE_WAVES
 #define MOEDEC_PIPE_WAVES 8
 #endif
@@ -1186,22 +1183,21 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
                 PIPE_MARK(tr, 45 + j);
             }
         };
-        // Rows of one piece stream through three register buffers: rows r + 1
-        // and r + 2 are in flight while row r is staged, which keeps the long
-        // round trips of loads behind the weight stream off the critical path.
+        // Rows of one piece alternate between two register buffers: row r + 1
+        // is in flight while row r is staged, which keeps most of the long
+        // round trip of a load behind the weight stream off the critical path.
         // A row is loaded once this workgroup's own finalizer has stored its
         // slot (every workgroup finalizes a slot at about the same time), so a
         // load seldom returns a sentinel and costs a second trip.  (Past the
-        // end the last row is loaded again, so every buffer always has its
-        // loads in the same order and the waits are static counts.)
+        // end the last row is loaded again, so both buffers always have their
+        // loads in the same order.)
         auto prefetch = [&](int r, u32x4* P) {
             const uint2 e = row_at(min(r, nrows - 1));
             lds_wait_ge(&sy.fin_done, (int)(e.y & 1023) + 1, f.ws, lds_cap);
             load_row((int)e.x, 0, P);
         };
         if (one && nrows > 0) {
-            u32x4 pa[kStageH4], pb[kStageH4], pc[kStageH4];
-#if MOEDEC_PIPE_PF == 1
+            u32x4 pa[kStageH4], pb[kStageH4];
             prefetch(0, pa);
             for (int r = 0; r < nrows; r += 2) {
                 prefetch(r + 1, pb);
@@ -1209,30 +1205,6 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
                 prefetch(r + 2, pa);
                 if (r + 1 < nrows) stage_row(r + 1, pb);
             }
-#elif MOEDEC_PIPE_PF == 2
-            prefetch(0, pa);
-            prefetch(1, pb);
-            for (int r = 0; r < nrows; r += 3) {
-                prefetch(r + 2, pc);
-                stage_row(r, pa);
-                prefetch(r + 3, pa);
-                if (r + 1 < nrows) stage_row(r + 1, pb);
-                prefetch(r + 4, pb);
-                if (r + 2 < nrows) stage_row(r + 2, pc);
-            }
-#else
-            prefetch(0, pa);
-            prefetch(1, pb);
-            prefetch(2, pc);
-            for (int r = 0; r < nrows; r += 3) {
-                stage_row(r, pa);
-                prefetch(r + 3, pa);
-                if (r + 1 < nrows) stage_row(r + 1, pb);
-                prefetch(r + 4, pb);
-                if (r + 2 < nrows) stage_row(r + 2, pc);
-                prefetch(r + 5, pc);
-            }
-#endif
         } else if (!one) {
             u32x4 v[kStageH4];
             for (int r = 0; r < nrows; ++r) {
