@@ -23,16 +23,24 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns and
- *     frees all memory.  The library allocates nothing, keeps no mutable global
- *     state, and never synchronises: work is enqueued on `stream` (a
- *     hipStream_t; NULL = the null stream) and the call returns at once.
+ *     frees all memory.  The library allocates nothing and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     null stream) and the call returns at once.  Its only mutable global
+ *     state is the static array of moe_expert_down_combine_em_noalloc_q4.
  *   - Struct arguments (moedec_experts, moedec_worklist) are HOST memory read
  *     during the call; their pointer fields are device pointers.
  *   - Arguments are validated before anything is enqueued.  Return values:
  *     MOEDEC_OK, MOEDEC_ERR_INVALID_ARG (null pointer, inconsistent sizes),
  *     MOEDEC_ERR_UNSUPPORTED (valid but outside the kernels' limits below),
  *     MOEDEC_ERR_DEVICE (the HIP runtime reported a launch error).
- *   - Non-finite inputs give unspecified (but memory-safe) results.
+ *   - Non-finite values: the router ranks a NaN corrected score (s + bias),
+ *     and a NaN group score (+inf and -inf in one group), as -inf, ties going
+ *     to the lower index, so every slot still gets a distinct valid expert
+ *     (Show HN page, implemented features, router item: the plain reading of
+ *     a top-k over such scores).  The routing of every other token, and its
+ *     outputs, are unaffected.  A token whose x holds a non-finite value
+ *     routes by that rule (its scores are NaN); its h and y rows are
+ *     unspecified.  Every call stays memory-safe.
  *   - Limits: 1 <= T <= MOEDEC_MAX_TOKENS; n_experts <= MOEDEC_MAX_EXPERTS;
  *     n_group <= 64; top_k <= 32; n_shared <= 8; hidden and inter must be
  *     multiples of 128/bits (one 16-byte group of codes) and at most 16384.

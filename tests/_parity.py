@@ -86,9 +86,34 @@ def oracle_layer(cfg, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray, exp
                          top_p=1.0 if top_p is None else top_p, act8=act8)
 
 
+def oracle_layer_c(cfg, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray, expert_fn) -> orc.LayerResult:
+    """The same LayerResult from the plain-C oracle (oracle/moe_ref.c, on
+    every host thread; a second implementation, cross-checked against the
+    NumPy one on the CPU), for the full-size sweeps the NumPy oracle is too
+    slow for.  The selection certificates come from the NumPy oracle's margin
+    functions on the C oracle's fp64 scores; the routing of the two must
+    agree.  Plain top-k, fp32 activations only."""
+    from oracle import moe_ref
+    x = np.asarray(x, np.float32)
+    E, S, K = router_w.shape[0], cfg.n_shared, cfg.top_k
+    s64 = orc.router_scores(x, router_w)
+    idx, w = orc.select_experts(s64.astype(np.float32), bias, cfg.n_group, cfg.topk_group, K, cfg.rsf)
+    wl = orc.batch_union(idx, E, S)
+    experts = {int(e): expert_fn(int(e)) for e in wl.expert_id}
+    c = moe_ref.layer(x, router_w, bias, experts, n_group=cfg.n_group, topk_group=cfg.topk_group, top_k=K,
+                      n_shared=S, rsf=cfg.rsf, bits=cfg.bits, threads=moe_ref.max_threads())
+    np.testing.assert_array_equal(c.idx, idx)                  # the two oracles route alike
+    assert np.abs(c.scores64 - s64).max() <= 1e-12
+    margin = orc.selection_margin(s64, bias, cfg.n_group, cfg.topk_group, K)
+    return orc.LayerResult(s64, idx, c.w, wl, c.h, c.y, margin, orc.order_margin(s64, bias, idx),
+                           np.full(x.shape[0], np.inf))
+
+
 def check_routing(cfg, g: dict, r: orc.LayerResult, bias: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Returns (set_certified, order_certified) per token after checking."""
-    err = np.abs(g["scores"].astype(np.float64) - r.scores64).max()
+    d = np.abs(g["scores"].astype(np.float64) - r.scores64)
+    both_nan = np.isnan(g["scores"]) & np.isnan(r.scores64)     # a token whose x holds a NaN
+    err = float(np.where(both_nan, 0.0, np.where(np.isnan(d), np.inf, d)).max())
     assert err <= SCORE_ATOL, f"scores off by {err}"
     set_ok = (r.margin >= MARGIN) & (r.topp >= MARGIN)       # top-p: the kept prefix is certified too
     order_ok = set_ok & (r.order >= MARGIN)
@@ -131,8 +156,12 @@ def check_layer(cfg, g: dict, r: orc.LayerResult, set_ok: np.ndarray, order_ok: 
     return eh, ey
 
 
-def check_all(cfg, g: dict, x, router_w, bias, expert_fn) -> orc.LayerResult:
-    r = oracle_layer(cfg, x, router_w, bias, expert_fn, g.get("top_p"), g.get("act8", False))
+def check_all(cfg, g: dict, x, router_w, bias, expert_fn, c_oracle: bool = False) -> orc.LayerResult:
+    if c_oracle:
+        assert g.get("top_p") is None and not g.get("act8", False)
+        r = oracle_layer_c(cfg, x, router_w, bias, expert_fn)
+    else:
+        r = oracle_layer(cfg, x, router_w, bias, expert_fn, g.get("top_p"), g.get("act8", False))
     set_ok, order_ok = check_routing(cfg, g, r, bias)
     check_layer(cfg, g, r, set_ok, order_ok)
     return r

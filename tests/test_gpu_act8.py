@@ -15,9 +15,10 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import moe_oracle as orc
 from quantized_moe_decode_route_amd import ops, synth
 
-from _parity import check_all, run_layer, say
+from _parity import MARGIN, check_all, rel_err, run_layer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +39,41 @@ def _cfg(name, seed=31):
     return synth.MoEConfig(name, T, H, I, E, G, TG, K, S, b, seed=seed)
 
 
+TIGHT = 1e-5
+
+
+def check_tight(cfg, g, r):
+    """Beyond the 1e-3 bar: x is quantised identically on both sides, so h
+    rows match to fp32 accumulation (<= 1e-5); the down input's codes come
+    from each side's own h, so y is held to 1e-5 on every token whose codes
+    (and block scales) come out equal on both sides -- the tokens where no
+    value sits on a rounding boundary."""
+    K, S = cfg.top_k, cfg.n_shared
+    slots = K + S
+    blk = orc.act8_block(cfg.bits)
+    ok = (r.margin >= MARGIN) & (r.topp >= MARGIN) & (r.order >= MARGIN)
+    rows = [t * slots + s for t in range(cfg.tokens) if ok[t] for s in range(slots) if s >= K or r.idx[t, s] >= 0]
+    eh = rel_err(g["h"][rows], r.h[rows]) if rows else 0.0
+    tight = []
+    for t in np.flatnonzero(ok):
+        same = True
+        for sl in range(slots):
+            if sl < K and r.idx[t, sl] < 0:
+                continue
+            a = t * slots + sl
+            coef = np.float32(r.w[t, sl]) if sl < K else np.float32(1.0)
+            qg, dg = orc.quantize_rows((g["h"][a].astype(np.float32) * coef).reshape(-1, blk), 8)
+            qo, do = orc.quantize_rows((r.h[a].astype(np.float32) * coef).reshape(-1, blk), 8)
+            same &= np.array_equal(qg, qo) and np.array_equal(dg, do)
+        if same:
+            tight.append(t)
+    ey = rel_err(g["y"][tight], r.y[tight]) if tight else 0.0
+    say(f"  tight: h err {eh:.2e} ({len(rows)} rows), y err {ey:.2e} on {len(tight)}/{int(ok.sum())} tokens "
+        f"without a code flip")
+    assert eh <= TIGHT and ey <= TIGHT
+    return len(tight)
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("top_p", [None, 0.75])
 def test_act8_layer_matches_oracle(name, top_p):
@@ -47,7 +83,8 @@ def test_act8_layer_matches_oracle(name, top_p):
     x = synth.token_pool(cfg, cfg.tokens)
     g = run_layer(cfg, lay, x, fused=True, top_p=top_p, act8=True)
     rw, b = synth.router_weight(cfg, 0), synth.router_bias(cfg, 0)
-    check_all(cfg, g, x, rw, b, synth.expert_loader(cfg, 0))
+    r = check_all(cfg, g, x, rw, b, synth.expert_loader(cfg, 0))
+    check_tight(cfg, g, r)
 
 
 def test_act8_blocks_of_very_different_scale():
