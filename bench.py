@@ -85,10 +85,10 @@ def traffic_from_profile(kind: str, workload: str):
     counters, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            d = json.load(f).get(kind, {})
-    except (OSError, ValueError):
+            d = json.load(f).get(kind, {}).get(workload, {})
+    except (OSError, ValueError, AttributeError):
         return None
-    if d.get("kernel_sha") != kernel_hash(kind) or d.get("workload") != workload:
+    if d.get("kernel_sha") != kernel_hash(kind):
         return None
     return d.get("bytes_per_launch")
 
@@ -437,6 +437,7 @@ def bench_stack(args, cfg) -> None:
     achieved = float(np.mean(kb) / dur.mean() / 1e9)
     kname = fused_kernel_name(cfg, args.top_p, False, True) if fused else f"gate_up_mfma_kernel<{cfg.bits}>"
     print(f"[bench] {kname} avg {dur.mean() * 1e6:.1f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    traffic = traffic_from_profile("fused" if fused else "gate_up", cfg.name) if args.top_p is None else None
     base = cpu_baseline(cfg, args.cpu_budget, args.top_p) if args.cpu_budget > 0 else None
     out = {
         "metric": METRIC + " (16-layer stack)", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -452,7 +453,7 @@ def bench_stack(args, cfg) -> None:
                    "separate calls + residual/RMSNorm kernel per layer",
                    "unique_experts_per_layer": float(active[idx].mean()), "top_p": args.top_p},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_us": round(float(dur.mean() * 1e6), 2), "bytes_per_launch": int(np.mean(kb))},
         "cpu_baseline": base,
     }
