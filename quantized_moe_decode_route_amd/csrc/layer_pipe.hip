@@ -69,9 +69,6 @@ namespace {
 using namespace mfma;
 using namespace imma;
 
-#ifndef MOEDEC_PIPE_STAGERS
-#define MOEDEC_PIPE_STAGERS 1
-#endif
 #ifndef MOEDEC_PIPE_RING
 #define MOEDEC_PIPE_RING 4
 #endif
@@ -80,12 +77,12 @@ using namespace imma;
 #endif
 constexpr int kPW = MOEDEC_PIPE_WAVES;                  // waves of a workgroup (one per compute unit)
 constexpr int kPT = kPW * kWave;                        // its threads
-constexpr int kNStg = MOEDEC_PIPE_STAGERS;              // stager waves (slot j: stager j % kNStg)
+constexpr int kNStg = 1;                                // stager waves
 constexpr int kSW = kPW - 1 - kNStg;                    // streaming waves
 constexpr int kFin = kSW, kStg = kSW + 1;               // control waves: the finalizer, the stagers
 constexpr int kRing = MOEDEC_PIPE_RING;                 // items in flight per streaming wave
 constexpr int kLag = 5;                                 // DN(j) follows GU(j + kLag)
-constexpr int kNHB = 2;                                 // staged-h buffers
+constexpr int kNHBMax = 4;                              // staged-h buffers at most (2 where LDS is short)
 constexpr int kNPB = 3;                                 // gate/up partial-sum buffers
 constexpr int kPieces = 3;                              // bytes of a 24-bit activation
 constexpr int kPipeExperts = 512;                       // routed experts at most
@@ -131,20 +128,21 @@ struct PipeArgs {
     int off_gsc, off_dsc;          // row-scale tables: [slot][tile][16] gate/up, [slot][32] down
     int off_items, max_items;      // the streaming waves' item lists: [kSW][max_items] uint2
     int off_rows, max_rows;        // the stagers' row lists: [kNStg][max_rows] uint2
+    int nhb;                       // staged-h buffers (2 .. kNHBMax)
 };
 
 // LDS words shared by the waves of a workgroup.
 struct PipeSync {
     int gu_cnt[kNPB];              // partial-sum tiles written to each buffer (cumulative)
     int gu_free[kNPB];             // 1 + the last gate/up unit finalized from each buffer
-    int hb_ready[kNHB];            // 1 + the down unit staged in each buffer
-    int hb_done[kNHB];             // streaming waves done with each buffer (cumulative)
+    int hb_ready[kNHBMax];         // 1 + the down unit staged in each buffer
+    int hb_done[kNHBMax];          // streaming waves done with each buffer (cumulative)
     int fin_cum[kNPB];             // finalizer: partial-sum tiles expected from each buffer so far
     int fin_done;                  // 1 + the last slot whose h this workgroup's finalizer has stored
     float xu[kCols];               // 2^-(e_t + shift): undoes token t's exponent and the code factor
     float xinv[kCols];             // residual form: 1 / rms of token t
     unsigned cmax[kCols];          // largest |x| of token t (bits)
-    float dsl[kNHB][kCols];        // per staged buffer: token t's unscale times its piece, 0 = not routed
+    float dsl[kNHBMax][kCols];     // per staged buffer: token t's unscale times its piece, 0 = not routed
     float gemv_red[kCols][kPW];
     float gemv_ssq[kCols][kPW];
     int n_slots;                   // experts of the batch (shared first)
@@ -680,6 +678,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     const int lane = lane_id(), wave = wave_id();
     const int ln = lane & 15, lq = lane >> 4;
     const int nc = f.nc;
+    const int nhb = f.nhb;
     const int rbg = H * BITS / 8, Pg = rbg >> 4, NCHg = (Pg + 3) >> 2;
     const int rbd = I * BITS / 8, Pd = rbd >> 4, NCHd = (Pd + 3) >> 2;
     const int nwg = gridDim.x, b = blockIdx.x;
@@ -706,7 +705,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
         sy.fin_cum[threadIdx.x] = 0;
     }
     if (threadIdx.x == 0) sy.fin_done = 0;
-    if (threadIdx.x < kNHB) {
+    if (threadIdx.x < kNHBMax) {
         sy.hb_ready[threadIdx.x] = 0;
         sy.hb_done[threadIdx.x] = 0;
     }
@@ -802,7 +801,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     }
     __syncthreads();
     // HB's padding groups are zero in every staged buffer (staging writes only valid groups)
-    zero_pad<BITS, NP>(Pd, NCHd, nc, HB, kNHB, hb_bytes, threadIdx.x, kPT);
+    zero_pad<BITS, NP>(Pd, NCHd, nc, HB, nhb, hb_bytes, threadIdx.x, kPT);
     __syncthreads();
     g.n = n_act;
     if (wave == 0) PIPE_MARK(tr, 3);
@@ -905,7 +904,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
                     lds_signal_add(&sy.gu_cnt[pb], 1);
                 }
             } else {
-                const int hb = j % kNHB;
+                const int hb = j % nhb;
                 if (hb_cur != j) {
                     lds_wait_ge(&sy.hb_ready[hb], j + 1, f.ws, lds_cap);
                     hb_cur = j;
@@ -1043,7 +1042,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
         __syncthreads();                                 // (B)
     } else {
         // ================================================ stagers (waves kStg ..: slots j % kNStg)
-        static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1 && kNHB == 2, "wave roles");
+        static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1 && kNStg == 1, "wave roles");
         const int sg = wave - kStg;                      // this stager's slots: j % kNStg == sg
         const int I4 = I >> 2;
         const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1136,7 +1135,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
             const uint2 e = row_at(r);
             const int as = (int)e.x, j = e.y & 1023, t = (e.y >> 10) & 1023;
             const bool first = (e.y >> 20) & 1, last = (e.y >> 21) & 1;
-            const int hb = j % kNHB;
+            const int hb = j % nhb;
             uint8_t* B = HB + hb * hb_bytes;
             if (first) PIPE_MARK(tr, 35 + j);
             const int sl = as - (as / slots) * slots;
@@ -1147,7 +1146,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
                 settle(as, c40, v);
                 if (first && c40 == 0) {
                     PIPE_MARK(tr, 66 + j);
-                    lds_wait_ge(&sy.hb_done[hb], (j / kNHB) * nc_dn, f.ws, lds_cap);   // its previous slot is consumed
+                    lds_wait_ge(&sy.hb_done[hb], (j / nhb) * nc_dn, f.ws, lds_cap);    // its previous slot is consumed
                     if (lane < T) sy.dsl[hb][lane] = 0.f;            // tokens not routed here (routed ones below)
                     PIPE_MARK(tr, 75 + j);
                 }
@@ -1284,14 +1283,13 @@ hipError_t pipe_bits(PipeArgs f, const FusedLayerArgs& l, hipStream_t st) {
     const size_t xb = align16((size_t)NCHg * chunk);
     const size_t red = align16((size_t)kSW * 2 * NP * 16 * 16 * sizeof(float));
     const size_t r0 = xb > red ? xb : red;
-    const size_t hb = align16((size_t)kNHB * NCHd * chunk);
+    const size_t hb1 = (size_t)NCHd * chunk;             // one staged expert's h
     const int NT = I / 8;
     const int ntile_max = (NT + nwg - 1) / nwg;
     // the item fields' widths: slots < 1024, chunks < 256, tiles < 1024
     if (l.ex.max_active >= 1024 || NCHg > 256 || NCHd > 256 || ntile_max > 1024) return hipErrorInvalidValue;
     const size_t part = align16((size_t)kNPB * ntile_max * kSW * NP * 16 * nc * sizeof(int));
     const size_t route = align16(sizeof(PipeRoute));
-    const size_t r1 = hb + part > route ? hb + part : route;
     const int K = l.ex.top_k, A = T * l.ex.slots;
     const size_t pers = align16(((size_t)2 * T * K + 2 * l.ex.max_active + 1 + A) * sizeof(int));
     const size_t gsc = align16((size_t)l.ex.max_active * ntile_max * 16 * sizeof(float));
@@ -1299,9 +1297,18 @@ hipError_t pipe_bits(PipeArgs f, const FusedLayerArgs& l, hipStream_t st) {
     const int max_items = max_items_of(l.ex.max_active, ntile_max, NCHg, NCHd);
     const size_t items = align16((size_t)kSW * max_items * sizeof(uint2));
     const size_t rows = align16((size_t)kNStg * A * sizeof(uint2));
-    size_t lds = r0 + r1 + pers + gsc + dsc + items + rows;
+    // as many staged-h buffers as fit (more let the stager run further ahead)
+    int nhb = kNHBMax;
+    size_t hb = 0, r1 = 0, lds = 0;
+    for (;; nhb -= 2) {
+        hb = align16((size_t)nhb * hb1);
+        r1 = hb + part > route ? hb + part : route;
+        lds = r0 + r1 + pers + gsc + dsc + items + rows;
+        if (static_lds + lds <= kLdsMax || nhb == 2) break;
+    }
     if (static_lds + lds > kLdsMax) return hipErrorInvalidValue;
     f.nc = nc;
+    f.nhb = nhb;
     f.ntile_max = ntile_max;
     f.off_hb = (int)r0;
     f.off_part = (int)(r0 + hb);
