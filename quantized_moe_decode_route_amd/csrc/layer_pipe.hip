@@ -13,11 +13,13 @@
 // layout that exchanges all experts' h at once leaves HBM idle for the whole
 // exchange.  Here every workgroup takes an equal share of EVERY expert (a
 // tile of 8 gate/up row pairs, and a fixed block of down output rows) and
-// the experts are streamed one after another in the order
-//     GU(0) GU(1) GU(2) DN(0) GU(3) DN(1) ... GU(n-1) DN(n-3) DN(n-2) DN(n-1)
-// (slot 0.. the shared experts first, they need no routing, then the routed
-// ones): expert j's h is exchanged while GU(j+1) and GU(j+2) stream, so the
-// exchange costs no bandwidth but at the very end.
+// the experts are streamed one after another (slot 0.. the shared experts
+// first, they need no routing, then the routed ones).  When the staged-h
+// buffers in LDS hold every expert of the batch, the order is all GU(j),
+// then all DN(j): each expert's h is exchanged and staged while the later
+// experts' gate/up rows stream.  Otherwise DN(j) follows GU(j + 5):
+//     GU(0) .. GU(4) GU(5) DN(0) GU(6) DN(1) ... GU(n-1) DN(n-6) DN(n-5) .. DN(n-1)
+// so a staged buffer is freed while later experts still stream.
 //
 // Waves of a workgroup (one workgroup per compute unit, 8 waves by default):
 //   streaming (0-5): a ring of kRing items per wave in flight, int8
@@ -77,12 +79,15 @@ using namespace imma;
 #endif
 constexpr int kPW = MOEDEC_PIPE_WAVES;                  // waves of a workgroup (one per compute unit)
 constexpr int kPT = kPW * kWave;                        // its threads
-constexpr int kNStg = 1;                                // stager waves
+#ifndef MOEDEC_PIPE_STAGERS
+#define MOEDEC_PIPE_STAGERS 1
+#endif
+constexpr int kNStg = MOEDEC_PIPE_STAGERS;              // stager waves (slot j: stager j % kNStg)
 constexpr int kSW = kPW - 1 - kNStg;                    // streaming waves
 constexpr int kFin = kSW, kStg = kSW + 1;               // control waves: the finalizer, the stagers
 constexpr int kRing = MOEDEC_PIPE_RING;                 // items in flight per streaming wave
-constexpr int kLag = 5;                                 // DN(j) follows GU(j + kLag)
-constexpr int kNHBMax = 4;                              // staged-h buffers at most (2 where LDS is short)
+constexpr int kLag = 5;                                 // DN(j) follows GU(j + kLag) when not every slot fits a buffer
+constexpr int kNHBMax = 16;                             // staged-h buffers at most (2 where LDS is short)
 constexpr int kNPB = 3;                                 // gate/up partial-sum buffers
 constexpr int kPieces = 3;                              // bytes of a 24-bit activation
 constexpr int kPipeExperts = 512;                       // routed experts at most
@@ -531,28 +536,29 @@ __device__ __forceinline__ void stage_x(const PipeArgs& f, PipeSync& sy, uint8_t
 
 struct Geo {
     int n;                         // slots
+    int lag;                       // DN(j) follows GU(j + lag)
     int NT;                        // gate/up tiles per expert (I / 8)
     int NCHg, NCHd;                // K-chunks of a gate/up row and of a down row
     int rd;                        // down rows of this workgroup
     int nwg, b;
 };
 
-__device__ __forceinline__ void unit_of(int u, int n, int& kind, int& j) {
-    if (n <= kLag) {
+__device__ __forceinline__ void unit_of(int u, int n, int lag, int& kind, int& j) {
+    if (n <= lag) {
         kind = u < n ? 0 : 1;
         j = u < n ? u : u - n;
         return;
     }
-    if (u < kLag) {
+    if (u < lag) {
         kind = 0;
         j = u;
-    } else if (u < kLag + 2 * (n - kLag)) {
-        const int k = u - kLag;
+    } else if (u < lag + 2 * (n - lag)) {
+        const int k = u - lag;
         kind = k & 1;
-        j = kind == 0 ? kLag + (k >> 1) : (k >> 1);
+        j = kind == 0 ? lag + (k >> 1) : (k >> 1);
     } else {
         kind = 1;
-        j = n - kLag + (u - kLag - 2 * (n - kLag));
+        j = n - lag + (u - lag - 2 * (n - lag));
     }
 }
 
@@ -615,7 +621,7 @@ __device__ __forceinline__ int build_items(const Geo& g, int w, int nu, uint2* L
         const int u = u0 + lane;
         int kind = 0, j = 0, c0 = 0, cnt = 0, i0 = 0, ntile = 0, nit = 0, n_items = 0;
         if (u < nu) {
-            unit_of(u, g.n, kind, j);
+            unit_of(u, g.n, g.lag, kind, j);
             if (kind == 0) {
                 ntile = tiles_of(g, j, i0);
                 cnt = chunks_of(g.NCHg, rot_of(j), w, c0);
@@ -734,6 +740,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
 
     Geo g;
     g.n = S;                       // before routing only the shared slots are known
+    g.lag = kLag;
     g.NT = I / 8;
     g.NCHg = NCHg;
     g.NCHd = NCHd;
@@ -804,6 +811,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     zero_pad<BITS, NP>(Pd, NCHd, nc, HB, nhb, hb_bytes, threadIdx.x, kPT);
     __syncthreads();
     g.n = n_act;
+    g.lag = nhb >= n_act ? n_act : kLag;             // every slot has a buffer: all gate/up first
     if (wave == 0) PIPE_MARK(tr, 3);
 
     // assignment of (token t, slot j), or -1
@@ -1042,7 +1050,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
         __syncthreads();                                 // (B)
     } else {
         // ================================================ stagers (waves kStg ..: slots j % kNStg)
-        static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1 && kNStg == 1, "wave roles");
+        static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1 && kNHBMax % kNStg == 0, "wave roles");
         const int sg = wave - kStg;                      // this stager's slots: j % kNStg == sg
         const int I4 = I >> 2;
         const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
