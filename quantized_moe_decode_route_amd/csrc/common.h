@@ -53,6 +53,31 @@ __device__ __forceinline__ int dpp_i(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
+// Sum over the wave, complete in lane 63 only: DPP sums each row of 16 lanes,
+// then row 1 (3) adds lane 15 (47) of the row before it and rows 2 and 3 add
+// lane 31 (row broadcasts; rows outside the mask add 0).
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    v += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return v;
+}
+
+// Inclusive prefix sum over the wave's lanes: within each row, the sums of
+// the three lanes before (shifted in with zeros), then of the four and the
+// eight before; then the row broadcasts carry each row's total onward.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+    int s = v + dpp_i<0x111>(v) + dpp_i<0x112>(v) + dpp_i<0x113>(v);   // row_shr:1, 2, 3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, false);    // row_shr:4 into lanes 4-15
+    s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, false);    // row_shr:8 into lanes 8-15
+    s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);    // row_bcast:15 into rows 1, 3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);    // row_bcast:31 into rows 2, 3
+    return s;
+}
+
 __device__ __forceinline__ int wave_min(int v) {
     v = min(v, dpp_i<0xB1>(v));
     v = min(v, dpp_i<0x4E>(v));

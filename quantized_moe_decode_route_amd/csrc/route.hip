@@ -7,89 +7,154 @@
 // group-score rule (top-2 sum), the use of the corrected score for selection
 // only and the tie-breaking (lower index) are this library's reading.
 //
-// Kernel 1 (router_gemv): one workgroup per expert row; every thread issues all
-// of its 16-byte loads of the row before using them, then the row is dotted
-// with the tokens, four at a time with their loads issued together, and
-// s = sigmoid(W_r[e] . x_t) is written.
-// Kernel 2 (route_select): one workgroup running route_select_block (see
-// route.h): each wave routes its tokens with wave-wide arg-max rounds, then
-// the expert-ascending worklist comes from a rank sort in LDS.
+// Kernel 1 (router_gemv): a 16-wave workgroup per tile of EB expert rows and
+// TB tokens, so each workgroup reads EB + TB rows of H floats (a one-row
+// workgroup would read the row and every token's x); s = sigmoid(W_r[e] . x_t).
+// A split over the hidden dimension would read every row once, but needs
+// scratch space the call does not have.
+// Kernel 2 (route_tokens): one one-wave workgroup per token routes it with
+// wave-wide arg-max rounds (route_one_token, see route.h); the last
+// workgroup to finish builds the expert-ascending worklist by a counting sort
+// in LDS (route_union_counting).
 #include "route.h"
 
 namespace moedec {
 
 namespace {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvMaxF4 = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 per thread at most
-constexpr int kGemvTB = 4;                                        // tokens whose x loads go out together
-constexpr int kSelThreads = 512;                                   // 8 waves (1024 would spill)
+constexpr int kGemvThreads = 1024;
+constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kGemvMaxSweeps = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 columns per thread at most
 
-// NF float4 of the row per thread; tokens in batches of kGemvTB whose x loads
-// all go out before any is used (the row's loads went out first of all).
-template <int NF>
+// Block b -> (expert tile, token tile).  The token tiles of one expert tile
+// get blocks with the same b % 8: blocks are dealt round-robin to the eight
+// XCDs, so they share an L2 and the tile's rows come from HBM once.
+// Per sweep s every thread loads column 1024*s + tid (a float4) of its EB
+// rows and TB tokens, the next sweep's loads going out before this sweep is
+// dotted; columns past the row's end are clamped for the load and their
+// products masked to zero.  Each wave's partial sums go to LDS and one
+// thread per (expert, token) adds the 16 waves' sums in wave order.
+template <int EB, int TB, int NS>
 __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* __restrict__ x,
                                                                    const float* __restrict__ W, int T, int H,
-                                                                   int E, float* __restrict__ scores) {
-    __shared__ float red[MOEDEC_MAX_TOKENS][kGemvThreads / kWave];
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const float4* w4 = reinterpret_cast<const float4*>(W + (size_t)e * H);
+                                                                   int E, float* __restrict__ scores,
+                                                                   int32_t* __restrict__ arrivals) {
+    if (arrivals != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *arrivals = 0;   // route_tokens counts here
+    const int nEt = (E + EB - 1) / EB, nTt = (T + TB - 1) / TB;
+    const int q = blockIdx.x >> 3;
+    const int tt = q % nTt, et = (q / nTt) * 8 + (blockIdx.x & 7);
+    if (et >= nEt) return;                               // the grid's last row of eight may be short
+    const int e0 = et * EB, t0 = tt * TB;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int n4 = H >> 2;
-    float4 wr[NF];
+    const float4* rows[EB + TB];
 #pragma unroll
-    for (int k = 0; k < NF; ++k) wr[k] = w4[min((int)threadIdx.x + k * kGemvThreads, n4 - 1)];
+    for (int i = 0; i < EB; ++i) rows[i] = reinterpret_cast<const float4*>(W + (size_t)min(e0 + i, E - 1) * H);
 #pragma unroll
-    for (int k = 0; k < NF; ++k)          // columns past the row's end count as zero
-        if ((int)threadIdx.x + k * kGemvThreads >= n4) wr[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t0 = 0; t0 < T; t0 += kGemvTB) {
-        float4 xv[kGemvTB][NF];
+    for (int j = 0; j < TB; ++j) rows[EB + j] = reinterpret_cast<const float4*>(x + (size_t)min(t0 + j, T - 1) * H);
+    float4 buf[2][EB + TB];
+    auto load = [&](float4 (&r)[EB + TB], int s) {
+        const int c = min(tid + s * kGemvThreads, n4 - 1);
 #pragma unroll
-        for (int b = 0; b < kGemvTB; ++b) {
-            const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)min(t0 + b, T - 1) * H);
+        for (int i = 0; i < EB + TB; ++i) r[i] = rows[i][c];
+    };
+    float acc[EB][TB];
 #pragma unroll
-            for (int k = 0; k < NF; ++k) xv[b][k] = x4[min((int)threadIdx.x + k * kGemvThreads, n4 - 1)];
-        }
+    for (int i = 0; i < EB; ++i)
 #pragma unroll
-        for (int b = 0; b < kGemvTB; ++b) {
-            float acc = 0.f;
+        for (int j = 0; j < TB; ++j) acc[i][j] = 0.f;
+    load(buf[0], 0);
 #pragma unroll
-            for (int k = 0; k < NF; ++k)
-                acc += (wr[k].x * xv[b][k].x + wr[k].y * xv[b][k].y) + (wr[k].z * xv[b][k].z + wr[k].w * xv[b][k].w);
-            acc = group_sum<kWave>(acc);
-            if (lane == 0 && t0 + b < T) red[t0 + b][wave] = acc;
-        }
+    for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) load(buf[(s + 1) & 1], s + 1);
+        const unsigned keep = tid + s * kGemvThreads < n4 ? ~0u : 0u;
+        const float4* r = buf[s & 1];
+#pragma unroll
+        for (int i = 0; i < EB; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const float4 w = r[i], v = r[EB + j];
+                const float d = (w.x * v.x + w.y * v.y) + (w.z * v.z + w.w * v.w);
+                acc[i][j] += __uint_as_float(__float_as_uint(d) & keep);
+            }
+    }
+    __shared__ float red[EB * TB][kGemvWaves];
+#pragma unroll
+    for (int i = 0; i < EB; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = wave_sum_last(acc[i][j]);
+    if (lane == kWave - 1) {
+#pragma unroll
+        for (int i = 0; i < EB; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j) red[i * TB + j][wave] = acc[i][j];
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += kGemvThreads) {
-        const float z = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
-        scores[(size_t)t * E + e] = 1.0f / (1.0f + expf(-z));
+    if (tid < EB * TB) {
+        const int i = tid / TB, j = tid - (tid / TB) * TB;
+        if (e0 + i < E && t0 + j < T) {
+            float z = 0.f;
+#pragma unroll
+            for (int w = 0; w < kGemvWaves; ++w) z += red[tid][w];
+            scores[(size_t)(t0 + j) * E + e0 + i] = 1.0f / (1.0f + expf(-z));
+        }
     }
 }
 
-template <bool kTopP>
-__global__ __launch_bounds__(kSelThreads) void route_select_kernel(
+template <int EB, int TB, int MaxNS = kGemvMaxSweeps>
+hipError_t launch_gemv(const float* x, const float* W, int T, int H, int E, float* scores, int32_t* arrivals,
+                       hipStream_t st) {
+    const int sweeps = (H / 4 + kGemvThreads - 1) / kGemvThreads;
+    const int nEt = (E + EB - 1) / EB, nTt = (T + TB - 1) / TB;
+    const dim3 grid(((nEt + 7) / 8) * 8 * nTt);
+    auto k = router_gemv_kernel<EB, TB, MaxNS>;
+    if (sweeps <= 1) k = router_gemv_kernel<EB, TB, 1>;
+    else if (sweeps <= 2) k = router_gemv_kernel<EB, TB, 2>;
+    hipLaunchKernelGGL(k, grid, dim3(kGemvThreads), 0, st, x, W, T, H, E, scores, arrivals);
+    return hipGetLastError();
+}
+
+// One one-wave workgroup per token (tokens on separate SIMDs: one wave's
+// routing is a chain of dependent wave-wide steps, and waves sharing a SIMD
+// would take turns).  Each writes its slots with device-scope stores, counts
+// itself on the worklist's n_active word (zeroed by router_gemv), and the
+// last to arrive reads every token's slots back and builds the worklist.
+template <bool kTopP, int NV, int EMT>
+__global__ __launch_bounds__(kWave) void route_tokens_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, int T, int E, int n_group, int topk_group,
     int top_k, int n_shared, float rsf, float top_p, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ wl_n_active, int32_t* __restrict__ wl_expert_id, int32_t* __restrict__ wl_seg,
     int32_t* __restrict__ wl_assign) {
-    __shared__ RouteLdsT<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS, kSelThreads / kWave> r;
-    route_select_block<MOEDEC_MAX_TOKENS, MOEDEC_MAX_EXPERTS, kSelThreads / kWave, false, kTopP>(
-        scores, bias, T, E, n_group, topk_group, top_k, n_shared, rsf, top_p, r);
-    // outputs
-    for (int i = threadIdx.x; i < T * top_k; i += blockDim.x) {
-        topk_idx[i] = r.sel[i];
-        topk_w[i] = r.selw[i];
+    static_assert(NV * kWave == EMT, "lane l holds experts l*NV .. l*NV+NV-1");
+    __shared__ RouteLdsT<MOEDEC_MAX_TOKENS, EMT, 1> r;
+    const int t = blockIdx.x, lane = threadIdx.x;
+    route_one_token<NV, MOEDEC_MAX_TOKENS, EMT, 1, false, kTopP>(scores, bias, t, E, n_group, topk_group, top_k, rsf,
+                                                                top_p, r);
+    wave_lds_sync();
+    if (lane < top_k) {                // device-scope stores: the last workgroup reads them back
+        __hip_atomic_store(topk_idx + t * top_k + lane, r.sel[t * top_k + lane], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        topk_w[t * top_k + lane] = r.selw[t * top_k + lane];
     }
     if (wl_n_active == nullptr) return;
-    const int n = r.n_active;
-    const int A = r.n_assign;                          // = seg[n]
-    if (threadIdx.x == 0) *wl_n_active = n;
-    for (int j = threadIdx.x; j <= n; j += blockDim.x) {
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's slot stores have completed: arrive
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(wl_n_active, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, kWave);
+    if (old != T - 1) return;
+    // the last to arrive: every token's slots (device-scope loads), then the union
+    for (int i = lane; i < T * top_k; i += kWave)
+        r.sel[i] = __hip_atomic_load(topk_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wave_lds_sync();
+    route_union_counting<MOEDEC_MAX_TOKENS, EMT, 1, kTopP>(T, E, top_k, n_shared, r);
+    const int n = min(r.n_active, E + n_shared);      // (bounds for the writes below)
+    const int A = min(r.n_assign, T * (top_k + n_shared));   // = seg[n]
+    for (int j = lane; j <= n; j += kWave) {
         if (j < n) wl_expert_id[j] = r.eid[j];
         wl_seg[j] = r.seg[j];
     }
-    for (int a = threadIdx.x; a < A; a += blockDim.x) wl_assign[a] = r.assign[a];
+    for (int a = lane; a < A; a += kWave) wl_assign[a] = r.assign[a];
+    if (lane == 0) *wl_n_active = n;
 }
 
 }  // namespace
@@ -98,24 +163,24 @@ hipError_t launch_route(const float* x, const float* router_w, const float* bias
                         int n_group, int topk_group, int top_k, int n_shared, float rsf, float top_p,
                         float* scores, int32_t* topk_idx, float* topk_w, const moedec_worklist* wl,
                         hipStream_t st) {
-    const int per = (H / 4 + kGemvThreads - 1) / kGemvThreads;
-    if (per <= 2)
-        hipLaunchKernelGGL(router_gemv_kernel<2>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
-    else if (per <= 4)
-        hipLaunchKernelGGL(router_gemv_kernel<4>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
-    else if (per <= 6)
-        hipLaunchKernelGGL(router_gemv_kernel<6>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
-    else if (per <= 8)
-        hipLaunchKernelGGL(router_gemv_kernel<8>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E, scores);
-    else
-        hipLaunchKernelGGL(router_gemv_kernel<kGemvMaxF4>, dim3(E), dim3(kGemvThreads), 0, st, x, router_w, T, H, E,
-                           scores);
-    hipError_t err = hipGetLastError();
+    // tiles: about 256 workgroups for E = 256 at every T, at most 8 rows each
+    int32_t* arrivals = wl ? wl->n_active : nullptr;
+    hipError_t err;
+    if (T == 1) err = launch_gemv<1, 1>(x, router_w, T, H, E, scores, arrivals, st);
+    else if (T == 2) err = launch_gemv<1, 2>(x, router_w, T, H, E, scores, arrivals, st);
+    else if (T <= 4) err = launch_gemv<1, 4>(x, router_w, T, H, E, scores, arrivals, st);
+    else if (T <= 8) err = launch_gemv<2, 4>(x, router_w, T, H, E, scores, arrivals, st);
+    else if (H <= 2 * 4 * kGemvThreads) err = launch_gemv<4, 4, 2>(x, router_w, T, H, E, scores, arrivals, st);
+    else err = launch_gemv<2, 4>(x, router_w, T, H, E, scores, arrivals, st);      // (4, 4) would spill at 4 sweeps
     if (err != hipSuccess) return err;
-    auto k = top_p < 1.f ? route_select_kernel<true> : route_select_kernel<false>;
-    hipLaunchKernelGGL(k, dim3(1), dim3(kSelThreads), 0, st, scores, bias, T, E, n_group,
-                       topk_group, top_k, n_shared, rsf, top_p, topk_idx, topk_w, wl ? wl->n_active : nullptr,
-                       wl ? wl->expert_id : nullptr, wl ? wl->seg : nullptr, wl ? wl->assign : nullptr);
+    // E <= 256: 4 experts per lane; more: 16
+    const bool topp = top_p < 1.f, wide = E > 4 * kWave;
+    auto k = topp ? route_tokens_kernel<true, 4, 4 * kWave> : route_tokens_kernel<false, 4, 4 * kWave>;
+    if (wide)
+        k = topp ? route_tokens_kernel<true, 16, MOEDEC_MAX_EXPERTS> : route_tokens_kernel<false, 16, MOEDEC_MAX_EXPERTS>;
+    hipLaunchKernelGGL(k, dim3(T), dim3(kWave), 0, st, scores, bias, T, E, n_group, topk_group, top_k, n_shared, rsf,
+                       top_p, topk_idx, topk_w, arrivals, wl ? wl->expert_id : nullptr, wl ? wl->seg : nullptr,
+                       wl ? wl->assign : nullptr);
     return hipGetLastError();
 }
 
