@@ -348,14 +348,27 @@ __device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restr
             du[b] = ld16(ub + off);
         }
     };
-    // With an even chunk count per wave the next group's first two chunks go
-    // out as soon as this group's buffers are free, ahead of its reduction
-    // (the last group re-reads its own first chunks instead).
+    // With an even chunk count per wave, chunks go in pairs t, t + 1: the two
+    // 64-byte halves of each row's 128-byte line, issued back to back so the
+    // second half meets the first one's fill (issued apart, under load about
+    // a third of the lines were fetched twice).  Gate and up pairs alternate:
+    // one matrix's pair streams while the other's is multiplied, and the next
+    // group's first pairs go out ahead of this group's reduction.
     const bool ahead = nk > 0 && (nk & 1) == 0;
     uint4 g0b[kNB], u0b[kNB], g1b[kNB], u1b[kNB];
+    auto issue_m = [&](int gs, int ch, uint4* d, const uint8_t* mb) {
+        const int grp = min(ch * 4 + lq, P - 1);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            const int r = min(gs + b * 16 + ln, rhi - 1);
+            d[b] = ld16(mb + (size_t)r * row_bytes + grp * 16);
+        }
+    };
     if (ahead) {
-        issue_at(rlo, cw0, g0b, u0b);
-        issue_at(rlo, cw0 + 1, g1b, u1b);
+        issue_m(rlo, cw0, g0b, gb);
+        issue_m(rlo, cw0 + 1, g1b, gb);
+        issue_m(rlo, cw0, u0b, ub);
+        issue_m(rlo, cw0 + 1, u1b, ub);
     }
     for (int g0 = rlo; g0 < rhi; g0 += G) {
         const int gn = min(rhi - g0, G);                 // rows in this group
@@ -399,12 +412,46 @@ __device__ __forceinline__ void gate_up_rows(const ExpertArgs& a, float* __restr
         };
         if (ahead) {
             const int gnx = g0 + G < rhi ? g0 + G : g0;
-            for (int t = 0; t < nk; t += 2) {          // chunks t, t+1 are in buffers 0, 1
-                compute(cw0 + t, g0b, u0b);
-                const bool in0 = t + 2 < nk;
-                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 2 : cw0, g0b, u0b);
-                compute(cw0 + t + 1, g1b, u1b);
-                issue_at(in0 ? g0 : gnx, in0 ? cw0 + t + 3 : cw0 + 1, g1b, u1b);
+            auto compute_m = [&](int ch, const uint4* d, floatx4* acc) {
+                half8 bh[NCALL], bl[NCALL];
+#pragma unroll
+                for (int c = 0; c < NCALL; ++c) {
+                    if (bslot >= 0) {
+                        const int src = ((ch * 4 + lq) * ns + bslot) * NCALL + c;
+                        bh[c] = xhi[src];
+                        bl[c] = xlo[src];
+                    } else {
+#pragma unroll
+                        for (int e2 = 0; e2 < 8; ++e2) bh[c][e2] = bl[c][e2] = (_Float16)0.f;
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) {
+                    if (b < nb) {
+#pragma unroll
+                        for (int c = 0; c < NCALL; ++c) {
+                            const half8 av = a_operand<BITS>(d[b], c);
+                            acc[b] = mfma(av, bh[c], acc[b]);
+                            acc[b] = mfma(av, bl[c], acc[b]);
+                        }
+                    }
+                }
+            };
+            for (int t = 0; t < nk; t += 2) {          // gate chunks t, t+1 in g0b, g1b; up in u0b, u1b
+                compute_m(cw0 + t, g0b, accg);
+                compute_m(cw0 + t + 1, g1b, accg);
+                const bool in0 = t + 2 < nk, more = in0 || g0 + G < rhi;
+                const int ng = in0 ? g0 : gnx, nc0 = in0 ? cw0 + t + 2 : cw0;
+                if (more) {
+                    issue_m(ng, nc0, g0b, gb);
+                    issue_m(ng, nc0 + 1, g1b, gb);
+                }
+                compute_m(cw0 + t, u0b, accu);
+                compute_m(cw0 + t + 1, u1b, accu);
+                if (more) {
+                    issue_m(ng, nc0, u0b, ub);
+                    issue_m(ng, nc0 + 1, u1b, ub);
+                }
             }
         } else if (nk > 0) {
             issue(cw0, g0b, u0b);
