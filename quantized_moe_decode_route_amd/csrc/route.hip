@@ -7,7 +7,7 @@
 // group-score rule (top-2 sum), the use of the corrected score for selection
 // only and the tie-breaking (lower index) are this library's reading.
 //
-// Kernel 1 (router_gemv): a 16-wave workgroup per tile of EB expert rows and
+// Kernel 1 (router_gemv): an 8-wave workgroup per tile of EB expert rows and
 // TB tokens, so each workgroup reads EB + TB rows of H floats (a one-row
 // workgroup would read the row and every token's x); s = sigmoid(W_r[e] . x_t).
 // A split over the hidden dimension would read every row once, but needs
@@ -22,18 +22,18 @@ namespace moedec {
 
 namespace {
 
-constexpr int kGemvThreads = 1024;
+constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kGemvMaxSweeps = MOEDEC_MAX_DIM / 4 / kGemvThreads;   // float4 columns per thread at most
 
 // Block b -> (expert tile, token tile).  The token tiles of one expert tile
 // get blocks with the same b % 8: blocks are dealt round-robin to the eight
 // XCDs, so they share an L2 and the tile's rows come from HBM once.
-// Per sweep s every thread loads column 1024*s + tid (a float4) of its EB
+// Per sweep s every thread loads column 512*s + tid (a float4) of its EB
 // rows and TB tokens, the next sweep's loads going out before this sweep is
 // dotted; columns past the row's end are clamped for the load and their
 // products masked to zero.  Each wave's partial sums go to LDS and one
-// thread per (expert, token) adds the 16 waves' sums in wave order.
+// thread per (expert, token) adds the 8 waves' sums in wave order.
 template <int EB, int TB, int NS>
 __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(const float* __restrict__ x,
                                                                    const float* __restrict__ W, int T, int H,
@@ -110,6 +110,8 @@ hipError_t launch_gemv(const float* x, const float* W, int T, int H, int E, floa
     auto k = router_gemv_kernel<EB, TB, MaxNS>;
     if (sweeps <= 1) k = router_gemv_kernel<EB, TB, 1>;
     else if (sweeps <= 2) k = router_gemv_kernel<EB, TB, 2>;
+    else if (sweeps <= 3) k = router_gemv_kernel<EB, TB, 3>;
+    else if (sweeps <= 4) k = router_gemv_kernel<EB, TB, 4>;
     hipLaunchKernelGGL(k, grid, dim3(kGemvThreads), 0, st, x, W, T, H, E, scores, arrivals);
     return hipGetLastError();
 }
@@ -170,8 +172,8 @@ hipError_t launch_route(const float* x, const float* router_w, const float* bias
     else if (T == 2) err = launch_gemv<1, 2>(x, router_w, T, H, E, scores, arrivals, st);
     else if (T <= 4) err = launch_gemv<1, 4>(x, router_w, T, H, E, scores, arrivals, st);
     else if (T <= 8) err = launch_gemv<2, 4>(x, router_w, T, H, E, scores, arrivals, st);
-    else if (H <= 2 * 4 * kGemvThreads) err = launch_gemv<4, 4, 2>(x, router_w, T, H, E, scores, arrivals, st);
-    else err = launch_gemv<2, 4>(x, router_w, T, H, E, scores, arrivals, st);      // (4, 4) would spill at 4 sweeps
+    else if (H <= 4 * 4 * kGemvThreads) err = launch_gemv<4, 4, 4>(x, router_w, T, H, E, scores, arrivals, st);
+    else err = launch_gemv<2, 4>(x, router_w, T, H, E, scores, arrivals, st);      // (4, 4) would spill at 8 sweeps
     if (err != hipSuccess) return err;
     // E <= 256: 4 experts per lane; more: 16
     const bool topp = top_p < 1.f, wide = E > 4 * kWave;

@@ -2,8 +2,8 @@
 
 The router GEMV runs in tiles of expert rows x tokens (1x1, 1x2, 1x4, 2x4,
 4x4, and 2x4 for rows longer than 8192 at more than 8 tokens), each thread
-taking one float4 column per sweep of 1024 (1, 2 or 4 sweeps, the last one
-ragged); expert counts of 72 leave the last tile of eight short and 1024
+taking one float4 column per sweep of 512 (1, 2, 3, 4 or 8 sweeps, the last
+one ragged); expert counts of 72 leave the last tile of eight short and 1024
 puts 16 experts on a lane.  Selection runs one workgroup per token, and the
 workgroup that arrives last builds the batch union.  Scores, selections and
 the worklist are checked as in every layer test (tests/_parity.py): scores
@@ -29,15 +29,16 @@ DEV = "cuda:0"
 
 # (T, H, E, n_group, topk_group, top_k, n_shared)
 CASES = [
-    (1, 6144, 256, 8, 4, 8, 1),      # 1x1 tile, 2 sweeps (the second half empty)
-    (2, 4096, 256, 8, 4, 8, 1),      # 1x2, 1 sweep exactly
-    (3, 4100, 72, 8, 2, 6, 2),       # 1x4 with a clamped token, ragged second sweep, short last tile
+    (1, 6144, 256, 8, 4, 8, 1),      # 1x1 tile, 3 full sweeps
+    (2, 4096, 256, 8, 4, 8, 1),      # 1x2, 2 full sweeps
+    (3, 4100, 72, 8, 2, 6, 2),       # 1x4 with a clamped token, a 1-column third sweep, short last tile
     (4, 12, 64, 4, 2, 4, 0),         # 1x4, a tiny row
-    (6, 8192, 256, 8, 4, 8, 1),      # 2x4, 2 full sweeps
-    (8, 16384, 256, 8, 4, 8, 1),     # 2x4, 4 sweeps
-    (9, 8196, 256, 8, 4, 8, 1),      # 2x4 at 3 sweeps (rows past 8192), ragged tokens
-    (16, 6144, 256, 8, 4, 8, 1),     # 4x4, the stack's shape
-    (16, 16384, 1024, 8, 4, 8, 2),   # 2x4 at 4 sweeps, 16 experts per lane
+    (6, 8192, 256, 8, 4, 8, 1),      # 2x4, 4 full sweeps
+    (8, 16384, 256, 8, 4, 8, 1),     # 2x4, 8 sweeps
+    (9, 8196, 256, 8, 4, 8, 1),      # 2x4 at 8 sweeps for 5 (rows past 8192), ragged tokens
+    (12, 7168, 256, 8, 4, 8, 1),     # 4x4 at 4 sweeps, the last one half full
+    (16, 6144, 256, 8, 4, 8, 1),     # 4x4, 3 sweeps: the stack's shape
+    (16, 16384, 1024, 8, 4, 8, 2),   # 2x4 at 8 sweeps, 16 experts per lane
     (33, 2048, 72, 4, 2, 5, 1),      # 4x4 with ragged token and expert tiles
     (64, 6144, 256, 8, 4, 8, 1),     # the most tokens: 16 token tiles, 64 selection workgroups
 ]
