@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc")
 # sources each timed kernel is built from (the traffic counters are void once any changes)
 KERNEL_SRCS = {"fused": ["layer_pipe.hip", "imma.h", "persist.h", "route.h", "common.h"],
-               "gate_up": ["experts_mfma.hip", "mfma.h", "common.h"],
+               "gate_up": ["experts_mfma.hip", "mfma.h", "persist.h", "common.h"],
                "quantize": ["quant.hip", "common.h"]}
 
 
