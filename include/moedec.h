@@ -101,7 +101,9 @@ typedef struct moedec_experts {
  *                                       routed slots of token t, K..K+S-1 its shared slots
  * Only the first n_active (+1 for seg) entries are defined after the call,
  * and the first seg[n_active] of assign (T*(K+S) unless top-p dropped slots,
- * which get no assignment).
+ * which get no assignment).  While moe_route_topk / moe_route_topp run, the
+ * n_active word also counts their per-token selection workgroups (it is
+ * zeroed by the call itself and holds the expert count once the call ends).
  */
 typedef struct moedec_worklist {
     int32_t* n_active;
