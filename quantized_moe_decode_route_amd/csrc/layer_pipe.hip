@@ -29,7 +29,8 @@
 //        the stream does no schedule arithmetic;
 //   finalizer (6): per expert, the gate/up partial sums of all streaming
 //        waves -> h = silu(g) * u for the workgroup's 8 pairs, stored with
-//        device-scope stores;
+//        device-scope stores; once every expert is finalized it stages the
+//        experts the stager has not claimed yet;
 //   stager (7): per expert, loads every workgroup's h once it is there and
 //        stages it (times the routing weight) as matrix-core operands in LDS;
 //        the next row's loads are in flight while a row is staged.
@@ -82,7 +83,7 @@ constexpr int kPT = kPW * kWave;                        // its threads
 #ifndef MOEDEC_PIPE_STAGERS
 #define MOEDEC_PIPE_STAGERS 1
 #endif
-constexpr int kNStg = MOEDEC_PIPE_STAGERS;              // stager waves (slot j: stager j % kNStg)
+constexpr int kNStg = MOEDEC_PIPE_STAGERS;              // stager waves (slots claimed in order, see staging)
 constexpr int kSW = kPW - 1 - kNStg;                    // streaming waves
 constexpr int kFin = kSW, kStg = kSW + 1;               // control waves: the finalizer, the stagers
 constexpr int kRing = MOEDEC_PIPE_RING;                 // items in flight per streaming wave
@@ -132,7 +133,7 @@ struct PipeArgs {
     int off_hb, off_part, off_pers, off_route;   // dynamic LDS layout (bytes); x operands at 0
     int off_gsc, off_dsc;          // row-scale tables: [slot][tile][16] gate/up, [slot][32] down
     int off_items, max_items;      // the streaming waves' item lists: [kSW][max_items] uint2
-    int off_rows, max_rows;        // the stagers' row lists: [kNStg][max_rows] uint2
+    int off_rows, max_rows;        // the staging row list: [max_rows] uint2, then [max_active + 1] slot offsets
     int nhb;                       // staged-h buffers (2 .. kNHBMax)
 };
 
@@ -144,6 +145,8 @@ struct PipeSync {
     int hb_done[kNHBMax];          // streaming waves done with each buffer (cumulative)
     int fin_cum[kNPB];             // finalizer: partial-sum tiles expected from each buffer so far
     int fin_done;                  // 1 + the last slot whose h this workgroup's finalizer has stored
+    int next_slot;                 // staging: the next slot to claim (stagers, then the finalizer too)
+    int rows_listed;               // staging: 1 once the row list and slot offsets are in LDS
     float xu[kCols];               // 2^-(e_t + shift): undoes token t's exponent and the code factor
     float xinv[kCols];             // residual form: 1 / rms of token t
     unsigned cmax[kCols];          // largest |x| of token t (bits)
@@ -710,7 +713,11 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
         sy.gu_free[threadIdx.x] = 0;
         sy.fin_cum[threadIdx.x] = 0;
     }
-    if (threadIdx.x == 0) sy.fin_done = 0;
+    if (threadIdx.x == 0) {
+        sy.fin_done = 0;
+        sy.next_slot = 0;
+        sy.rows_listed = 0;
+    }
     if (threadIdx.x < kNHBMax) {
         sy.hb_ready[threadIdx.x] = 0;
         sy.hb_done[threadIdx.x] = 0;
@@ -827,6 +834,208 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     const int nc_gu = NCHg < kSW ? NCHg : kSW;          // streaming waves with chunks of a gate/up tile
     const int nc_dn = rd > 0 ? (NCHd < kSW ? NCHd : kSW) : 0;   // ... of a down unit (none without rows)
     const int ncolT = kPieces * T;                       // B columns in use
+
+    auto staging = [&](bool builder) {
+    // ================================================ staging
+    // Slots are claimed one at a time from an LDS counter by every staging
+    // wave: the stagers, and the finalizer once it has finalized every slot
+    // (at one token it is done well before the last slots are staged).  The
+    // first stager ("builder") loads the down row scales and lists the rows.
+    static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1, "wave roles");
+    const int I4 = I >> 2;
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        f.h, (short)0, (int)((size_t)T * slots * I * sizeof(float)), kBufWord3);
+    if (builder) {
+        // the down row scales of this workgroup's rows for every slot, to LDS once
+        // (the streaming waves read a slot's after its release)
+        for (int base = 0; base < n_act * 32; base += 8 * kWave) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {                // every load first, then the stores
+                const int idx = min(base + k * kWave + lane, max(n_act * 32 - 1, 0));
+                const int j = idx >> 5, r = idx & 31;
+                v[k] = a.s_down[(size_t)eid_of(min(j, n_act - 1)) * H + dr0 + min(r, max(rd - 1, 0))];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int idx = base + k * kWave + lane;
+                if (idx < n_act * 32) DSC[idx] = (idx & 31) < rd ? v[k] : 0.f;
+            }
+        }
+    }
+    const bool one = I4 <= kStageH4 * kWave;            // a row is read once, else twice
+    // float4 k of a lane in a piece of the row: int4 codes take 16 consecutive
+    // values per lane (4 float4), so each staged operand gets 8-byte writes
+    auto c4_of = [&](int c40, int k) {
+        return BITS == 4 ? c40 + 4 * ((k >> 2) * kWave + lane) + (k & 3) : c40 + k * kWave + lane;
+    };
+    auto load_row = [&](int as, int c40, u32x4* v) {
+#pragma unroll
+        for (int k = 0; k < kStageH4; ++k) {
+            const int c4 = c4_of(c40, k);
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(hrs, (as * I4 + min(c4, I4 - 1)) * 16, 0, kCoherent);
+        }
+    };
+    auto any_stale = [&](const u32x4* v) {
+        bool st = false;
+#pragma unroll
+        for (int k = 0; k < kStageH4; ++k)
+            st = st || v[k].x == kSentinel || v[k].y == kSentinel || v[k].z == kSentinel || v[k].w == kSentinel;
+        return __ballot(st) != 0;
+    };
+    // loads of a row piece until no sentinel is left (bounded)
+    auto settle = [&](int as, int c40, u32x4* v) {
+        for (int tries = 0; any_stale(v); ++tries) {
+            if (tries >= gates.spin_max) {
+                raise_error(f.ws);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            load_row(as, c40, v);
+        }
+    };
+    auto piece_max = [&](const u32x4* v, int c40, float w) {
+        float mx = 0.f;
+#pragma unroll
+        for (int k = 0; k < kStageH4; ++k) {
+            if (c4_of(c40, k) < I4) {
+                const float m4 = fmaxf(fmaxf(fabsf(__uint_as_float(v[k].x) * w), fabsf(__uint_as_float(v[k].y) * w)),
+                                       fmaxf(fabsf(__uint_as_float(v[k].z) * w), fabsf(__uint_as_float(v[k].w) * w)));
+                mx = fmaxf(mx, m4);
+            }
+        }
+        return mx;
+    };
+    // The rows (slot j, token t, assignment as) in slot order, listed once by
+    // the builder: x = as, y = j | t << 10 | first << 20 | last << 21
+    // (first / last: the slot's first / last row; every slot has one), and
+    // slot j's rows are r0[j] .. r0[j + 1] - 1.
+    uint2* rl = reinterpret_cast<uint2*>(dyn + f.off_rows);
+    int* r0 = reinterpret_cast<int*>(rl + f.max_rows);
+    if (builder) {
+        int n = 0;
+        for (int j = 0; j < n_act; ++j) {
+            const int m = lane < T ? assign_of(j, lane) : -1;
+            const unsigned long long bal = __ballot(m >= 0);
+            const int pos = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+            const int cnt = __builtin_popcountll(bal);
+            if (m >= 0)
+                rl[n + pos] = make_uint2((uint32_t)m, (uint32_t)j | (uint32_t)lane << 10 |
+                                                          (pos == 0 ? 1u << 20 : 0u) |
+                                                          (pos == cnt - 1 ? 1u << 21 : 0u));
+            if (lane == 0) r0[j] = n;
+            n += cnt;
+        }
+        if (lane == 0) r0[n_act] = n;
+        lds_signal_set(&sy.rows_listed, 1);          // (publishes the lanes' list writes)
+    } else {
+        lds_wait_ge(&sy.rows_listed, 1, f.ws, lds_cap);
+    }
+    const int nrows = __builtin_amdgcn_readfirstlane(r0[n_act]);
+    auto row_at = [&](int r) {                       // (wave-uniform fields)
+        const uint2 e = rl[r];
+        return make_uint2((uint32_t)__builtin_amdgcn_readfirstlane((int)e.x),
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)e.y));
+    };
+    // Stage row r, whose first (or only) piece is in v: the slot's buffer is
+    // taken on its first row and released on its last.
+    auto stage_row = [&](int r, u32x4* v) {
+        const uint2 e = row_at(r);
+        const int as = (int)e.x, j = e.y & 1023, t = (e.y >> 10) & 1023;
+        const bool first = (e.y >> 20) & 1, last = (e.y >> 21) & 1;
+        const int hb = j % nhb;
+        uint8_t* B = HB + hb * hb_bytes;
+        if (first) PIPE_MARK(tr, 35 + j);
+        const int sl = as - (as / slots) * slots;
+        const float w = sl < K ? p_selw[t * K + sl] : 1.0f;
+        float mx = 0.f;
+        for (int c40 = 0; c40 < I4; c40 += kStageH4 * kWave) {
+            if (c40 > 0) load_row(as, c40, v);
+            settle(as, c40, v);
+            if (first && c40 == 0) {
+                PIPE_MARK(tr, 66 + j);
+                lds_wait_ge(&sy.hb_done[hb], (j / nhb) * nc_dn, f.ws, lds_cap);    // its previous slot is consumed
+                if (lane < T) sy.dsl[hb][lane] = 0.f;            // tokens not routed here (routed ones below)
+                PIPE_MARK(tr, 75 + j);
+            }
+            mx = fmaxf(mx, piece_max(v, c40, w));
+        }
+        mx = wave_max(mx);
+        const int ex = q24_exponent(mx);
+        const float ws = w * ldexpf(1.0f, ex);
+        for (int c40 = 0; c40 < I4; c40 += kStageH4 * kWave) {
+            if (!one) load_row(as, c40, v);
+            if constexpr (BITS == 4) {
+                static_assert(kStageH4 % 4 == 0, "whole quads");
+#pragma unroll
+                for (int k = 0; k < kStageH4; k += 4) {
+                    const int c4 = c4_of(c40, k);            // a quad lies wholly inside the row (I % 32 == 0)
+                    if (c4 < I4) scatter24_quad4<NP>(v + k, ws, c4 * 4, t, nc, B);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kStageH4; ++k) {
+                    const int c4 = c4_of(c40, k);
+                    if (c4 < I4) {
+                        const float4 hv = make_float4(__uint_as_float(v[k].x) * ws, __uint_as_float(v[k].y) * ws,
+                                                      __uint_as_float(v[k].z) * ws, __uint_as_float(v[k].w) * ws);
+                        scatter24<BITS, NP>(hv, c4 * 4, t, nc, B);
+                    }
+                }
+            }
+        }
+        if (lane == 0) sy.dsl[hb][t] = ldexpf(1.0f, -ex - C::kShift);
+        if (last) {
+            lds_signal_set(&sy.hb_ready[hb], j + 1);
+            PIPE_MARK(tr, 45 + j);
+        }
+    };
+    // Rows of one piece alternate between two register buffers: row r + 1
+    // is in flight while row r is staged, which keeps most of the long
+    // round trip of a load behind the weight stream off the critical path.
+    // A row is loaded once this workgroup's own finalizer has stored its
+    // slot (every workgroup finalizes a slot at about the same time), so a
+    // load seldom returns a sentinel and costs a second trip.  (Past the
+    // end the last row is loaded again, so both buffers always have their
+    // loads in the same order.)
+    auto prefetch = [&](int r, u32x4* P) {
+        const uint2 e = row_at(min(r, nrows - 1));
+        lds_wait_ge(&sy.fin_done, (int)(e.y & 1023) + 1, f.ws, lds_cap);
+        load_row((int)e.x, 0, P);
+    };
+    // The rows this wave stages, in order: the rest of its current slot,
+    // then the first row of the next slot it claims (nrows: no slot left).
+    int slot_end = 0;
+    auto next_row = [&](int r) {
+        if (r + 1 < slot_end) return r + 1;
+        int j = 0;
+        if (lane == 0) j = __hip_atomic_fetch_add(&sy.next_slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        j = __builtin_amdgcn_readfirstlane(j);
+        if (j >= n_act) return nrows;
+        slot_end = r0[j + 1];
+        return r0[j];
+    };
+    if (nrows > 0 && one) {
+        u32x4 pa[kStageH4], pb[kStageH4];
+        int ra = next_row(-1);
+        prefetch(ra, pa);
+        while (ra < nrows) {
+            const int rb = next_row(ra);
+            prefetch(rb, pb);
+            stage_row(ra, pa);
+            if (rb >= nrows) break;
+            ra = next_row(rb);
+            prefetch(ra, pa);
+            stage_row(rb, pb);
+        }
+    } else if (nrows > 0) {
+        u32x4 v[kStageH4];
+        for (int r = next_row(-1); r < nrows; r = next_row(r)) {
+            load_row((int)row_at(r).x, 0, v);
+            stage_row(r, v);
+        }
+    }
+    };
 
     if (streaming) {
         // ================================================ streaming waves
@@ -1046,179 +1255,11 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
             lds_signal_set(&sy.fin_done, j + 1);
             PIPE_MARK(tr, 25 + j);
         }
+        staging(false);                                  // then it stages the slots still unclaimed
         __syncthreads();                                 // (A)
         __syncthreads();                                 // (B)
     } else {
-        // ================================================ stagers (waves kStg ..: slots j % kNStg)
-        static_assert(kStg + kNStg == kPW && kFin == kSW && kStg == kFin + 1 && kNHBMax % kNStg == 0, "wave roles");
-        const int sg = wave - kStg;                      // this stager's slots: j % kNStg == sg
-        const int I4 = I >> 2;
-        const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
-            f.h, (short)0, (int)((size_t)T * slots * I * sizeof(float)), kBufWord3);
-        // the down row scales of this workgroup's rows for this stager's slots, to LDS
-        // once (the streaming waves read them after the stager's release of each slot)
-        const int nmine = (n_act - sg + kNStg - 1) / kNStg;
-        for (int base = 0; base < nmine * 32; base += 8 * kWave) {
-            float v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {                    // every load first, then the stores
-                const int idx = min(base + k * kWave + lane, max(nmine * 32 - 1, 0));
-                const int j = kNStg * (idx >> 5) + sg, r = idx & 31;
-                v[k] = a.s_down[(size_t)eid_of(min(j, n_act - 1)) * H + dr0 + min(r, max(rd - 1, 0))];
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int idx = base + k * kWave + lane;
-                if (idx < nmine * 32) DSC[(kNStg * (idx >> 5) + sg) * 32 + (idx & 31)] = (idx & 31) < rd ? v[k] : 0.f;
-            }
-        }
-        const bool one = I4 <= kStageH4 * kWave;            // a row is read once, else twice
-        // float4 k of a lane in a piece of the row: int4 codes take 16 consecutive
-        // values per lane (4 float4), so each staged operand gets 8-byte writes
-        auto c4_of = [&](int c40, int k) {
-            return BITS == 4 ? c40 + 4 * ((k >> 2) * kWave + lane) + (k & 3) : c40 + k * kWave + lane;
-        };
-        auto load_row = [&](int as, int c40, u32x4* v) {
-#pragma unroll
-            for (int k = 0; k < kStageH4; ++k) {
-                const int c4 = c4_of(c40, k);
-                v[k] = __builtin_amdgcn_raw_buffer_load_b128(hrs, (as * I4 + min(c4, I4 - 1)) * 16, 0, kCoherent);
-            }
-        };
-        auto any_stale = [&](const u32x4* v) {
-            bool st = false;
-#pragma unroll
-            for (int k = 0; k < kStageH4; ++k)
-                st = st || v[k].x == kSentinel || v[k].y == kSentinel || v[k].z == kSentinel || v[k].w == kSentinel;
-            return __ballot(st) != 0;
-        };
-        // loads of a row piece until no sentinel is left (bounded)
-        auto settle = [&](int as, int c40, u32x4* v) {
-            for (int tries = 0; any_stale(v); ++tries) {
-                if (tries >= gates.spin_max) {
-                    raise_error(f.ws);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                load_row(as, c40, v);
-            }
-        };
-        auto piece_max = [&](const u32x4* v, int c40, float w) {
-            float mx = 0.f;
-#pragma unroll
-            for (int k = 0; k < kStageH4; ++k) {
-                if (c4_of(c40, k) < I4) {
-                    const float m4 = fmaxf(fmaxf(fabsf(__uint_as_float(v[k].x) * w), fabsf(__uint_as_float(v[k].y) * w)),
-                                           fmaxf(fabsf(__uint_as_float(v[k].z) * w), fabsf(__uint_as_float(v[k].w) * w)));
-                    mx = fmaxf(mx, m4);
-                }
-            }
-            return mx;
-        };
-        // This stager's rows (slot j, token t, assignment as) in staging order,
-        // listed once: x = as, y = j | t << 10 | first << 20 | last << 21
-        // (first / last: the slot's first / last row; every slot has one).
-        uint2* rl = reinterpret_cast<uint2*>(dyn + f.off_rows) + (size_t)sg * f.max_rows;
-        int nrows = 0;
-        for (int j = sg; j < n_act; j += kNStg) {
-            const int m = lane < T ? assign_of(j, lane) : -1;
-            const unsigned long long bal = __ballot(m >= 0);
-            const int pos = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-            const int cnt = __builtin_popcountll(bal);
-            if (m >= 0)
-                rl[nrows + pos] = make_uint2((uint32_t)m, (uint32_t)j | (uint32_t)lane << 10 |
-                                                              (pos == 0 ? 1u << 20 : 0u) |
-                                                              (pos == cnt - 1 ? 1u << 21 : 0u));
-            nrows += cnt;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");   // the lanes' list writes
-        auto row_at = [&](int r) {                       // (wave-uniform fields)
-            const uint2 e = rl[r];
-            return make_uint2((uint32_t)__builtin_amdgcn_readfirstlane((int)e.x),
-                              (uint32_t)__builtin_amdgcn_readfirstlane((int)e.y));
-        };
-        // Stage row r, whose first (or only) piece is in v: the slot's buffer is
-        // taken on its first row and released on its last.
-        auto stage_row = [&](int r, u32x4* v) {
-            const uint2 e = row_at(r);
-            const int as = (int)e.x, j = e.y & 1023, t = (e.y >> 10) & 1023;
-            const bool first = (e.y >> 20) & 1, last = (e.y >> 21) & 1;
-            const int hb = j % nhb;
-            uint8_t* B = HB + hb * hb_bytes;
-            if (first) PIPE_MARK(tr, 35 + j);
-            const int sl = as - (as / slots) * slots;
-            const float w = sl < K ? p_selw[t * K + sl] : 1.0f;
-            float mx = 0.f;
-            for (int c40 = 0; c40 < I4; c40 += kStageH4 * kWave) {
-                if (c40 > 0) load_row(as, c40, v);
-                settle(as, c40, v);
-                if (first && c40 == 0) {
-                    PIPE_MARK(tr, 66 + j);
-                    lds_wait_ge(&sy.hb_done[hb], (j / nhb) * nc_dn, f.ws, lds_cap);    // its previous slot is consumed
-                    if (lane < T) sy.dsl[hb][lane] = 0.f;            // tokens not routed here (routed ones below)
-                    PIPE_MARK(tr, 75 + j);
-                }
-                mx = fmaxf(mx, piece_max(v, c40, w));
-            }
-            mx = wave_max(mx);
-            const int ex = q24_exponent(mx);
-            const float ws = w * ldexpf(1.0f, ex);
-            for (int c40 = 0; c40 < I4; c40 += kStageH4 * kWave) {
-                if (!one) load_row(as, c40, v);
-                if constexpr (BITS == 4) {
-                    static_assert(kStageH4 % 4 == 0, "whole quads");
-#pragma unroll
-                    for (int k = 0; k < kStageH4; k += 4) {
-                        const int c4 = c4_of(c40, k);            // a quad lies wholly inside the row (I % 32 == 0)
-                        if (c4 < I4) scatter24_quad4<NP>(v + k, ws, c4 * 4, t, nc, B);
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < kStageH4; ++k) {
-                        const int c4 = c4_of(c40, k);
-                        if (c4 < I4) {
-                            const float4 hv = make_float4(__uint_as_float(v[k].x) * ws, __uint_as_float(v[k].y) * ws,
-                                                          __uint_as_float(v[k].z) * ws, __uint_as_float(v[k].w) * ws);
-                            scatter24<BITS, NP>(hv, c4 * 4, t, nc, B);
-                        }
-                    }
-                }
-            }
-            if (lane == 0) sy.dsl[hb][t] = ldexpf(1.0f, -ex - C::kShift);
-            if (last) {
-                lds_signal_set(&sy.hb_ready[hb], j + 1);
-                PIPE_MARK(tr, 45 + j);
-            }
-        };
-        // Rows of one piece alternate between two register buffers: row r + 1
-        // is in flight while row r is staged, which keeps most of the long
-        // round trip of a load behind the weight stream off the critical path.
-        // A row is loaded once this workgroup's own finalizer has stored its
-        // slot (every workgroup finalizes a slot at about the same time), so a
-        // load seldom returns a sentinel and costs a second trip.  (Past the
-        // end the last row is loaded again, so both buffers always have their
-        // loads in the same order.)
-        auto prefetch = [&](int r, u32x4* P) {
-            const uint2 e = row_at(min(r, nrows - 1));
-            lds_wait_ge(&sy.fin_done, (int)(e.y & 1023) + 1, f.ws, lds_cap);
-            load_row((int)e.x, 0, P);
-        };
-        if (one && nrows > 0) {
-            u32x4 pa[kStageH4], pb[kStageH4];
-            prefetch(0, pa);
-            for (int r = 0; r < nrows; r += 2) {
-                prefetch(r + 1, pb);
-                stage_row(r, pa);
-                prefetch(r + 2, pa);
-                if (r + 1 < nrows) stage_row(r + 1, pb);
-            }
-        } else if (!one) {
-            u32x4 v[kStageH4];
-            for (int r = 0; r < nrows; ++r) {
-                load_row((int)row_at(r).x, 0, v);
-                stage_row(r, v);
-            }
-        }
+        staging(wave == kStg);
         __syncthreads();                                 // (A)
         __syncthreads();                                 // (B)
     }
@@ -1304,7 +1345,7 @@ hipError_t pipe_bits(PipeArgs f, const FusedLayerArgs& l, hipStream_t st) {
     const size_t dsc = align16((size_t)l.ex.max_active * 32 * sizeof(float));
     const int max_items = max_items_of(l.ex.max_active, ntile_max, NCHg, NCHd);
     const size_t items = align16((size_t)kSW * max_items * sizeof(uint2));
-    const size_t rows = align16((size_t)kNStg * A * sizeof(uint2));
+    const size_t rows = align16((size_t)A * sizeof(uint2) + ((size_t)l.ex.max_active + 1) * sizeof(int));
     // as many staged-h buffers as fit (more let the stager run further ahead)
     int nhb = kNHBMax;
     size_t hb = 0, r1 = 0, lds = 0;
