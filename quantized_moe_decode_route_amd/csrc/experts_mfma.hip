@@ -27,14 +27,15 @@ using namespace mfma;
 // order afterwards.  No atomics: deterministic.
 
 // Rows [rlo, rhi) of expert e's down matrix for the nc staged columns.
-// red: LDS [kMW][NB][16][ns]; sd_s: LDS [NB*16].
+// red: LDS [kMW][NBE][16][ns]; sd_s: LDS [NBE*16].
 template <int BITS>
 __device__ __forceinline__ void down_em_rows(const ExpertArgs& a, float* __restrict__ part, int e, int rlo, int rhi,
                                              int nc, const int* asg, const half8* hhi, const half8* hlo, int ns,
                                              float unscale, float* red, float* sd_s) {
     using M = MfmaCodec<BITS>;
     constexpr int NCALL = M::NCALL;
-    constexpr int kNB = M::NB;
+    constexpr int kNB = M::NBE;
+    static_assert(kNB <= kNBMax, "the row-scale array holds kNBMax blocks");
     const int H = a.H, I = a.I;
     const int row_bytes = I * BITS / 8;
     const int P = row_bytes >> 4;
@@ -144,7 +145,7 @@ struct DownEmLds {
     int asg[kCols];
     float mul[kCols];
     float scratch[kMW];
-    float sd[MfmaCodec<2>::NB * 16 > MfmaCodec<8>::NB * 16 ? MfmaCodec<2>::NB * 16 : MfmaCodec<8>::NB * 16];
+    float sd[kNBMax * 16];
     int kexp;
 };
 
@@ -186,7 +187,7 @@ __device__ __forceinline__ void down_em_units(const ExpertArgs& a, const float* 
 // LDS per staged assignment of down_em_units: hi + lo B operands and the reduction.
 template <int BITS>
 __host__ __device__ constexpr size_t down_em_lds_per_col(int I) {
-    return staged_row_bytes<BITS>(I) + (size_t)kMW * MfmaCodec<BITS>::NB * 16 * sizeof(float);
+    return staged_row_bytes<BITS>(I) + (size_t)kMW * MfmaCodec<BITS>::NBE * 16 * sizeof(float);
 }
 
 // Gate/up: all tokens staged once when they fit (T <= ns), then this

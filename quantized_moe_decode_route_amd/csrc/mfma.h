@@ -40,6 +40,7 @@ template <>
 struct MfmaCodec<4> {
     static constexpr int NCALL = 4;
     static constexpr int NB = 3;          // 16-row blocks per gate/up group (5 ran 3-4 % slower)
+    static constexpr int NBE = 5;         // ... per expert-major down group (3 ran 5 % slower)
     static constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64086408u, kBias = 0x64086408u;   // 1032
     __device__ static int col(int c, int e) { return 8 * c + (e >> 1) + 4 * (e & 1); }
     __device__ static void place(int p, int& c, int& e) {      // col(c, e) == p
@@ -51,6 +52,7 @@ template <>
 struct MfmaCodec<8> {
     static constexpr int NCALL = 2;
     static constexpr int NB = 5;
+    static constexpr int NBE = 5;
     static constexpr uint32_t kMask = 0x00FF00FFu, kMagic = 0x64806480u, kBias = 0x64806480u;   // 1152
     __device__ static int col(int c, int e) { return 8 * c + 4 * (e >> 2) + ((e >> 1) & 1) + 2 * (e & 1); }
     __device__ static void place(int p, int& c, int& e) {      // col(c, e) == p
@@ -62,6 +64,7 @@ template <>
 struct MfmaCodec<2> {
     static constexpr int NCALL = 8;
     static constexpr int NB = 3;          // wider B operands: fewer blocks fit in registers
+    static constexpr int NBE = 3;
     static constexpr uint32_t kMask = 0x00030003u, kMagic = 0x64026402u, kBias = 0x64026402u;   // 1026
     // call c = 2*dword + half; element e = 2*s + t is field 4*half + s + 8*t of the dword
     __device__ static int col(int c, int e) { return 16 * (c >> 1) + 4 * (c & 1) + (e >> 1) + 8 * (e & 1); }
