@@ -54,11 +54,10 @@ Readings (the pages are silent on these):
      problem shows in every output computed from it.
  R23 Q8_0-style int8 activations (the integer-dot item): the activations that
      meet the weights -- each token's x, and each assignment's h times its
-     routing weight (fp32) -- are quantised in blocks of 512/bits consecutive
-     input columns (64 / 128 / 256 for int8 / int4 / int2 weights: one
-     K-chunk of the matrix-core tile; Q8_0 itself uses 32) by R20's rule
-     with qmax 127 (d = absmax / 127, q = rint(v / d) half to even); the dot
-     products are then exact integer sums scaled by d.
+     routing weight (fp32) -- are quantised in blocks of 32 consecutive
+     input columns, Q8_0's block (whatever the weights' code width), by
+     R20's rule with qmax 127 (d = absmax / 127, q = rint(v / d) half to
+     even); the dot products are then exact integer sums scaled by d.
  R22 adaptive expert top-p (the run options' --topp): after the top-k
      selection, order the K chosen experts by unbiased score s descending
      (a NaN s last, ties to the lower index), add their s in that order in
@@ -138,8 +137,9 @@ def unpack_rows(packed: np.ndarray, bits: int) -> np.ndarray:
 
 
 def act8_block(bits: int) -> int:
-    """Input columns per activation block for weights of `bits` (R23)."""
-    return 512 // bits
+    """Input columns per activation block for weights of `bits` (R23: Q8_0's
+    block of 32, the same for every code width)."""
+    return 32
 
 
 def dequantize(packed: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:

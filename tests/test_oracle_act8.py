@@ -4,7 +4,7 @@ dot products are integer sums).
 
 Show HN page "धीमे कंप्यूटर पर GLM 5.2 चलाना", section "implemented features":
 the integer-dot kernel item (Q8_0-style int8 activations).  The block length
-and the rounding rule are readings (one K-chunk of the matrix-core tile;
+and the rounding rule are readings (Q8_0's block of 32 consecutive values;
 the row quantiser's absmax / 127 rule): these tests pin the oracle to them
 with lossless inputs, the per-block error bound, block independence, and
 the layer's reduction to the exact layer when x is representable.
@@ -15,12 +15,12 @@ import pytest
 from oracle import moe_oracle as orc
 
 
-@pytest.mark.parametrize("bits,block", [(8, 64), (4, 128), (2, 256)])
-def test_block_lengths(bits, block):
-    assert orc.act8_block(bits) == block
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_block_lengths(bits):
+    assert orc.act8_block(bits) == 32
 
 
-@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("block", [32, 64, 128])
 def test_representable_values_are_kept(block):
     """Values q * 2^-5 with a block's largest |q| = 127 quantise losslessly."""
     rng = np.random.default_rng(block)
@@ -31,7 +31,7 @@ def test_representable_values_are_kept(block):
     np.testing.assert_array_equal(orc.quantize_act8(v, block), v.astype(np.float64))
 
 
-@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("block", [32, 64, 128])
 def test_error_bound_and_block_independence(block):
     """Every element within half a step of its block's scale (absmax / 127),
     each block on its own scale: a block of tiny values next to a block of
