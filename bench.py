@@ -222,7 +222,9 @@ def fused_kernel_name(cfg, top_p, act8: bool, resid: bool) -> str:
     """The kernel a fused call launches (as the profiler names it)."""
     tp = "true" if top_p is not None and top_p < 1 else "false"
     if act8:
-        return f"layer_fused_kernel<{cfg.bits}, {tp}, false, true>"
+        ncb = 2 if cfg.bits == 8 else 4               # MFMA columns of a token (one per column block)
+        passes = 1 if cfg.tokens * ncb <= 16 else ncb
+        return f"layer_fused_kernel<{cfg.bits}, {tp}, false, true, {passes}>"
     np_ = 1 if 3 * cfg.tokens <= 16 else 3
     return f"layer_pipe_kernel<{cfg.bits}, {np_}, {tp}, {'true' if resid else 'false'}>"
 

@@ -310,15 +310,14 @@ int moe_layer_fused_topp_q2(const float* x, const float* router_w, const float* 
  * "implemented features": the integer-dot kernel uses Q8_0-style int8
  * activations).  The activations that meet the weights -- each token's x,
  * and each assignment's h times its routing weight -- are quantised in
- * blocks of 512/bits consecutive input columns (64, 128, 256 for q8, q4,
- * q2 weights: one K-chunk of the matrix-core tile; Q8_0 itself uses 32):
- * d = absmax / 127, q = rint(v / d) with ties to even, both in IEEE fp32
+ * Q8_0's blocks of 32 consecutive input columns, whatever the weights'
+ * width: d = absmax / 127, q = rint(v / d) with ties to even, both in IEEE fp32
  * (a zero block: d = 0; a block with a NaN or an infinity: d = NaN, q = 0).
  * Each block's integer dot products are exact and scaled by d.  The result
  * is the layer with those quantised activations (an approximation of the
  * other calls' result, to the blocks' resolution of 1/254 of their largest
  * value).  Arguments, outputs and limits as for moe_layer_fused_topp_q*;
- * also hidden and inter must be multiples of 512/bits, else
+ * also hidden and inter must be multiples of 32, else
  * MOEDEC_ERR_UNSUPPORTED.
  */
 int moe_layer_fused_act8_q4(const float* x, const float* router_w, const float* bias, const moedec_experts* ex,

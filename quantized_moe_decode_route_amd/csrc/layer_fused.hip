@@ -102,6 +102,24 @@ struct FusedArgs {
     int deferred;                  // 1: every block has its own slot and is finalised after the segment
     int off_gured, off_gsc, off_dsc, off_pairs, off_chunk, off_hprod;   // dynamic LDS layout (bytes)
     int off_shpart;                                                     // shp: the shared tile's partial sums
+    int off_qdx;                                                        // kQ8: block scales of the staged x
+};
+
+// kQ8: column blocks of a K-chunk (the MFMA columns of one token), blocks
+// per column block, whether lane group lq belongs to column block cb, and
+// half hf of a lane's B operand (int2: the slots of block 2 cb + hf only).
+template <int BITS>
+struct Q8Cols {
+    static constexpr int NCB = BITS == 8 ? 2 : 4;
+    static constexpr int HALVES = BITS == 2 ? 2 : 1;
+    __device__ static bool in(int lq, int cb) { return BITS == 8 ? (lq >> 1) == cb : lq == cb; }
+    __device__ static i32x4 half(i32x4 v, int hf) {
+        if constexpr (BITS == 2) {
+            if (hf) v.x = v.y = 0;
+            else v.z = v.w = 0;
+        }
+        return v;
+    }
 };
 
 // Workgroup barrier for LDS only: loads in flight to registers stay in flight.
@@ -359,11 +377,18 @@ __device__ __forceinline__ void zero_pad(int P, int NCH, int n, int ldn, i32x4* 
     }
 }
 
-// ---- int8 activations in blocks (Q8_0 style): a block is one K-chunk of
-// the B layout, 4 groups of CW columns = 512/BITS columns, so one wave item
-// covers exactly one block of every column and the block's scale applies to
-// the item's integer MFMA sums.  d = absmax / 127 and q = rint(v / d) in IEEE
-// fp32 (d = 0: all zero; a NaN or an infinity in the block: d = NaN, q = 0).
+// ---- int8 activations in blocks of 32 consecutive columns (Q8_0): d =
+// absmax / 127 and q = rint(v / d) in IEEE fp32 (d = 0: all zero; a NaN or
+// an infinity in the block: d = NaN, q = 0).  A K-chunk of the B layout (4
+// lane groups of CW columns, 512/BITS columns) holds 16/BITS blocks.  Each
+// MFMA column stands for one (token, column block) pair, a column block
+// being the lane groups of one block (int8: two lane groups) or one lane
+// group (int4: one block; int2: two blocks, the lane's dwords 0-1 and 2-3,
+// multiplied in two MFMAs, each half with the other zeroed): its B operand
+// is the token's codes there and zero elsewhere, so the column's sum is the
+// block's exact integer dot product, scaled by the block's d.  The columns
+// of a token are added at the end of a tile.  One MFMA per code operand (and
+// half) covers 8 tokens with int8 codes, 4 with int4 and int2.
 
 // Largest |value| (and non-finite flag) over the GL lanes of this lane's group.
 template <int GL>
@@ -383,7 +408,8 @@ __device__ __forceinline__ float q8_scale(const float4& v, bool valid, int gl_lo
     float m = valid ? fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))) : 0.f;
     bool bad = valid && !(m <= 3.402823466e38f) ;
     bad = bad || (valid && (v.x != v.x || v.y != v.y || v.z != v.z || v.w != v.w));
-    if (gl_log2 == 4) m = group_absmax<16>(m, bad);
+    if (gl_log2 == 3) m = group_absmax<8>(m, bad);
+    else if (gl_log2 == 4) m = group_absmax<16>(m, bad);
     else if (gl_log2 == 5) m = group_absmax<32>(m, bad);
     else m = group_absmax<64>(m, bad);
     const float d = bad ? __uint_as_float(0x7FC00000u) : m / 127.0f;
@@ -424,8 +450,7 @@ template <int BITS>
 __device__ __forceinline__ void stage_q8(float4 v, bool valid, int row, int c4, int ldn, uint8_t* hi, float* qd,
                                          int qld) {
     using C = I8Codec<BITS>;
-    constexpr int GL = 128 / BITS;                 // float4 per block: 512 / BITS columns
-    constexpr int GLOG = BITS == 8 ? 4 : BITS == 4 ? 5 : 6;
+    constexpr int GL = 8, GLOG = 3;                // float4 per block: 32 columns
     bool ok;
     const float d = q8_scale(v, valid, GLOG, ok);
     if (!valid) return;
@@ -441,7 +466,8 @@ __device__ __forceinline__ void stage_q8(float4 v, bool valid, int row, int c4, 
 }
 
 // Stage the T token rows of x (row-major [T][H]) as int8 hi/lo B operands,
-// unit ((g*T + t)*NM + m); column t = token t has its own exponent, and
+// unit ((g*T + t)*NM + m) (kQ8: the codes, and the block scales in
+// qdx[blk * T + t]); column t = token t has its own exponent, and
 // xu[t] = 2^-(e_t + kShift) undoes it and the code factor.  cmax[0..T) must
 // be zero on entry.  When all of x fits the registers (kStageX4 float4 per
 // thread) it is read once, else twice (a max pass and a convert pass).
@@ -474,7 +500,7 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int H, int 
                     const float r = xinv[t];
                     vv = make_float4(vv.x * r, vv.y * r, vv.z * r, vv.w * r);
                 }
-                stage_q8<BITS>(vv, ok, t, i4 - t * H4, T, h8, qdx, kCols);
+                stage_q8<BITS>(vv, ok, t, i4 - t * H4, T, h8, qdx, T);
             }
         }
         if ((int)threadIdx.x < T) xu[threadIdx.x] = 1.0f;      // the block scales carry the unscale
@@ -656,7 +682,9 @@ __device__ __forceinline__ void shared_prefetch(const FusedArgs& f, SharedTile& 
     }
 }
 
-template <int BITS, bool kResid, bool kQ8>
+// kPass (kQ8): passes of MFMA token columns compiled in (1: up to 16 / NCB
+// tokens; more: up to kCols, at the cost of a larger loop body).
+template <int BITS, bool kResid, bool kQ8, int kPass>
 __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, unsigned char* dyn, const float* xu,
                                        const float* qdx, GridGate& gate, const SharedTile& shtile) {
     using C = I8Codec<BITS>;
@@ -711,7 +739,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     float* dsl = reinterpret_cast<float*>(qmax + qc);             // [qc]
     int* amap = reinterpret_cast<int*>(dsl + qc);                 // [qc][16]
     int* ctab = amap + qc * kCols;                                 // [chunks + 1][3]
-    // kQ8: block scales of the staged h rows, [NCHd][qc], after the chunk tables
+    // kQ8: block scales of the staged h rows, [I / 32][qc], after the chunk tables
 
     // Positions: the gate/up items, then each down chunk's items, every segment
     // padded to a multiple of W, so a segment starts at ring slot 0 and its
@@ -809,13 +837,51 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     const floatx4 zerof4 = {0.f, 0.f, 0.f, 0.f};
     i32x4 gh = zero4, gl = zero4, uh = zero4, ul = zero4;     // gate / up, hi / lo parts
     i32x4 ah[kNBD], al[kNBD];
-    floatx4 tot[kNBD];
-    floatx4 gf = zerof4, uf = zerof4, af[kNBD];              // kQ8: block-scaled sums
+    // kQ8: block-scaled sums per pass of TPP tokens (MFMA column ln = token
+    // p * TPP + ln / NCB of pass p, column block ln % NCB of the K-chunk)
+    using QC = Q8Cols<BITS>;
+    constexpr int NCB = kQ8 ? QC::NCB : 1;                    // column blocks of a K-chunk
+    constexpr int NHF = QC::HALVES;                           // blocks of a column block
+    constexpr int NBC = NCB * NHF;                            // blocks of a K-chunk
+    constexpr int TPP = 16 / NCB;                             // tokens of a pass
+    constexpr int NPS = kQ8 ? kPass : 1;                      // passes at most
+    static_assert(!kQ8 || kPass == 1 || kPass * TPP >= kCols, "passes for every token");
+    const int bc = ln % NCB, tp = ln / NCB;
+    const bool bq_on = QC::in(lq, bc);                        // this lane's K slots are column block bc's
+    const int npass = (T + TPP - 1) / TPP;
+    // tot[p]: the layer output of pass p's tokens (kQ8: in lanes bc = 0 of
+    // each token's columns; else pass 0 only, column = token)
+    floatx4 gf[NPS], uf[NPS], af[NPS][kNBD], tot[NPS][kNBD];
 #pragma unroll
-    for (int bb = 0; bb < kNBD; ++bb) {
-        ah[bb] = al[bb] = zero4;
-        tot[bb] = af[bb] = zerof4;
+    for (int p = 0; p < NPS; ++p) {
+        gf[p] = uf[p] = zerof4;
+#pragma unroll
+        for (int bb = 0; bb < kNBD; ++bb) af[p][bb] = tot[p][bb] = zerof4;
     }
+#pragma unroll
+    for (int bb = 0; bb < kNBD; ++bb) ah[bb] = al[bb] = zero4;
+    int cbqp[NPS];                  // kQ8: per pass, the staged slot of this lane's B token, or -1
+    // kQ8: a pass's sums of this lane's column added over the token's NCB
+    // columns (lanes tp * NCB .. + NCB - 1 of a quad: DPP); every lane gets it
+    auto q8_token_sum = [&](float v) { return group_sum<NCB>(v); };
+    // kQ8: leave a finished gate/up tile's sums in LDS (token t's column)
+    auto q8_part_out = [&](float* part) {
+#pragma unroll
+        for (int p = 0; p < NPS; ++p) {
+            if (p < npass) {
+                const int tt = p * TPP + tp;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float g = q8_token_sum(gf[p][ii]), u = q8_token_sum(uf[p][ii]);
+                    if (bc == 0 && tt < T) {
+                        part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + tt] = g;
+                        part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + tt] = u;
+                    }
+                }
+            }
+            gf[p] = uf[p] = zerof4;
+        }
+    };
     int chunk_first = 0;            // first expert of the staged chunk
     // per-expert state of the computing cursor: this lane's staged column and its unscale
     int cj = -1, cbq = -1;
@@ -827,20 +893,33 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     auto gu_item = [&](const Cursor& c, const uint4* cur) {
         const int ch = wave * nkg + c.k;
         if (kQ8 && ch < NCHg) {
-            i32x4 bq[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) bq[m] = xhi[((ch * 4 + lq) * T + tcol) * NM + m];
-            i32x4 g8 = zero4, u8 = zero4;
+            for (int p = 0; p < NPS; ++p) {
+                if (p < npass) {
+                    const int tt = p * TPP + tp;
+                    const bool on = tt < T;
+                    i32x4 bx[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                g8 = mma(operand<BITS>(cur[0], m), bq[m], g8);
-                u8 = mma(operand<BITS>(cur[1], m), bq[m], u8);
-            }
-            const float dq = qdx[ch * kCols + tcol];          // the block's scale for this lane's token
+                    for (int m = 0; m < NM; ++m) bx[m] = on && bq_on ? xhi[((ch * 4 + lq) * T + tt) * NM + m] : zero4;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                gf[ii] = fmaf(dq, (float)g8[ii], gf[ii]);
-                uf[ii] = fmaf(dq, (float)u8[ii], uf[ii]);
+                    for (int hf = 0; hf < NHF; ++hf) {
+                        i32x4 g8 = zero4, u8 = zero4;
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) {
+                            const i32x4 bq = QC::half(bx[m], hf);
+                            g8 = mma(operand<BITS>(cur[0], m), bq, g8);
+                            u8 = mma(operand<BITS>(cur[1], m), bq, u8);
+                        }
+                        const int blk = ch * NBC + bc * NHF + hf;     // this column's block of the row
+                        const float dq = on && blk < H / 32 ? qdx[blk * T + tt] : 0.f;   // padding groups: none
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            gf[p][ii] = fmaf(dq, (float)g8[ii], gf[p][ii]);
+                            uf[p][ii] = fmaf(dq, (float)u8[ii], uf[p][ii]);
+                        }
+                    }
+                }
+                if constexpr (BITS == 2) __builtin_amdgcn_sched_barrier(0);   // one pass's operands live at a time
             }
         } else if (!kQ8 && ch < NCHg) {
             i32x4 bh[NM], bl[NM];
@@ -864,15 +943,16 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             // every block has a slot of its own: leave the partial sums there;
             // all blocks are finalised together after the gate/up segment
             float* part = gred + (size_t)c.blk * kMW * 2 * 16 * T;
-            if (ln < T) {
+            if constexpr (kQ8) {
+                q8_part_out(part);
+            } else if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? gf[ii] : combine(gh[ii], gl[ii]);
-                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? uf[ii] : combine(uh[ii], ul[ii]);
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
                 }
             }
             gh = gl = uh = ul = zero4;
-            gf = uf = zerof4;
         } else if (c.k == nkg - 1) {
             // This wave's part of the block is done.  No workgroup barrier here
             // (every one would wait for the slowest wave's loads): the wave leaves
@@ -894,15 +974,16 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
-            if (ln < T) {
+            if constexpr (kQ8) {
+                q8_part_out(part);
+            } else if (ln < T) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? gf[ii] : combine(gh[ii], gl[ii]);
-                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = kQ8 ? uf[ii] : combine(uh[ii], ul[ii]);
+                    part[((wave * 2 + 0) * 16 + 4 * lq + ii) * T + ln] = combine(gh[ii], gl[ii]);
+                    part[((wave * 2 + 1) * 16 + 4 * lq + ii) * T + ln] = combine(uh[ii], ul[ii]);
                 }
             }
             gh = gl = uh = ul = zero4;
-            gf = uf = zerof4;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             int arrived = 0;
             if (lane == 0)
@@ -943,21 +1024,37 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             cj = c.j;
             cbq = amap[(cj - chunk_first) * kCols + ln];      // staged slot of this lane's token, or -1
             du = cbq >= 0 ? dsl[cbq] : 0.f;
+            if constexpr (kQ8) {
+#pragma unroll
+                for (int p = 0; p < NPS; ++p)                 // (tokens < kCols: the map holds -1 past T)
+                    cbqp[p] = amap[(cj - chunk_first) * kCols + min(p * TPP + tp, kCols - 1)];
+            }
         }
         const int ch = wave * nkd + c.k;
         if (kQ8 && ch < NCHd) {
-            const int slot = max(cbq, 0);
-            i32x4 bq[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) bq[m] = hhi[((ch * 4 + lq) * qc + slot) * NM + m];
-            const float dq = qdh[ch * qc + slot];
+            for (int p = 0; p < NPS; ++p) {
+                if (p < npass) {
+                    const int slot = cbqp[p];
+                    i32x4 bx[NM];
 #pragma unroll
-            for (int bb = 0; bb < kNBD; ++bb) {
-                i32x4 a8 = zero4;
+                    for (int m = 0; m < NM; ++m)
+                        bx[m] = slot >= 0 && bq_on ? hhi[((ch * 4 + lq) * qc + slot) * NM + m] : zero4;
 #pragma unroll
-                for (int m = 0; m < NM; ++m) a8 = mma(operand<BITS>(cur[bb], m), bq[m], a8);
+                    for (int hf = 0; hf < NHF; ++hf) {
+                        const int blk = ch * NBC + bc * NHF + hf;
+                        const float dq = slot >= 0 && blk < I / 32 ? qdh[blk * qc + slot] : 0.f;
 #pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) af[bb][i2] = fmaf(dq, (float)a8[i2], af[bb][i2]);
+                        for (int bb = 0; bb < kNBD; ++bb) {
+                            i32x4 a8 = zero4;
+#pragma unroll
+                            for (int m = 0; m < NM; ++m) a8 = mma(operand<BITS>(cur[bb], m), QC::half(bx[m], hf), a8);
+#pragma unroll
+                            for (int i2 = 0; i2 < 4; ++i2) af[p][bb][i2] = fmaf(dq, (float)a8[i2], af[p][bb][i2]);
+                        }
+                    }
+                }
+                if constexpr (BITS == 2) __builtin_amdgcn_sched_barrier(0);   // one pass's operands live at a time
             }
         } else if (!kQ8 && ch < NCHd) {
             const int slot = max(cbq, 0);
@@ -979,24 +1076,36 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
             }
         }
         if (c.k == nkd - 1) {         // this pair is complete: scale rows, add (tokens routed here only)
-            if (cbq >= 0) {
+            if constexpr (kQ8) {
+                // token p * TPP + tp: its sum over its columns, added where it is routed here
+#pragma unroll
+                for (int p = 0; p < NPS; ++p) {
+                    if (p < npass) {
+#pragma unroll
+                        for (int bb = 0; bb < kNBD; ++bb) {
+#pragma unroll
+                            for (int i2 = 0; i2 < 4; ++i2) {
+                                const float v = q8_token_sum(af[p][bb][i2]);
+                                const int rr = min(bb * 16 + 4 * lq + i2, rd - 1);
+                                if (cbqp[p] >= 0) tot[p][bb][i2] += dsc[cj * rd + rr] * v;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int bb = 0; bb < kNBD; ++bb) af[p][bb] = zerof4;
+                }
+            } else if (cbq >= 0) {
 #pragma unroll
                 for (int bb = 0; bb < kNBD; ++bb) {
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) {
                         const int rr = min(bb * 16 + 4 * lq + i2, rd - 1);
-                        if (kQ8)
-                            tot[bb][i2] += dsc[cj * rd + rr] * af[bb][i2];
-                        else
-                            tot[bb][i2] += (dsc[cj * rd + rr] * du) * combine(ah[bb][i2], al[bb][i2]);
+                        tot[0][bb][i2] += (dsc[cj * rd + rr] * du) * combine(ah[bb][i2], al[bb][i2]);
                     }
                 }
             }
 #pragma unroll
-            for (int bb = 0; bb < kNBD; ++bb) {
-                ah[bb] = al[bb] = zero4;
-                af[bb] = zerof4;
-            }
+            for (int bb = 0; bb < kNBD; ++bb) ah[bb] = al[bb] = zero4;
         }
     };
 
@@ -1270,11 +1379,23 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     // the waves' partial sums -> LDS -> y, summed in wave order
     if (nchunk == 0) return;
     lds_barrier();
-    if (ln < T) {
+    if constexpr (kQ8) {
+#pragma unroll
+        for (int p = 0; p < NPS; ++p) {
+            const int tt = p * TPP + tp;
+            if (p < npass && bc == 0 && tt < T) {
+#pragma unroll
+                for (int bb = 0; bb < kNBD; ++bb)
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2)
+                        dred[((wave * kNBD + bb) * 16 + 4 * lq + i2) * 16 + tt] = tot[p][bb][i2];
+            }
+        }
+    } else if (ln < T) {
 #pragma unroll
         for (int bb = 0; bb < kNBD; ++bb)
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) dred[((wave * kNBD + bb) * 16 + 4 * lq + i2) * 16 + ln] = tot[bb][i2];
+            for (int i2 = 0; i2 < 4; ++i2) dred[((wave * kNBD + bb) * 16 + 4 * lq + i2) * 16 + ln] = tot[0][bb][i2];
     }
     lds_barrier();
     for (int idx = threadIdx.x; idx < rd * T; idx += kMT) {
@@ -1288,7 +1409,7 @@ __device__ __forceinline__ void stream(const FusedArgs& f, const FusedRoute& r, 
     }
 }
 
-template <int BITS, bool kTopP, bool kResid, bool kQ8>
+template <int BITS, bool kTopP, bool kResid, bool kQ8, int kPass>
 __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     constexpr int NM = I8Codec<BITS>::NM;
     extern __shared__ __align__(16) unsigned char dyn[];
@@ -1298,14 +1419,13 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
     __shared__ unsigned xmax[kCols];
     __shared__ float xu[kCols];
     __shared__ float xinv[kCols];                     // kResid: 1 / rms of each token's x
-    // kQ8: the block scales of the staged x, [chunk][token]
-    __shared__ float qdx[kQ8 ? MOEDEC_MAX_DIM * BITS / 512 * kCols : 1];
 
     const ExpertArgs& a = f.a;
     const int T = a.T, H = a.H, K = a.top_k, S = f.n_shared, E = f.E;
     const int NCHg = ((H * BITS / 8) / 16 + 3) / 4;
     i32x4* xhi = reinterpret_cast<i32x4*>(dyn);
     i32x4* xlo = xhi + (size_t)NCHg * 4 * T * NM;
+    float* qdx = reinterpret_cast<float*>(dyn + f.off_qdx);   // kQ8: block scales of the staged x, [H / 32][T]
     if (threadIdx.x < kCols) xmax[threadIdx.x] = 0u;
     GridGate gate{f.ws, f.ws[kWsSpin] > 0 ? f.ws[kWsSpin] : kSpinDefault, 0ull};
     gate.init();
@@ -1324,7 +1444,7 @@ __global__ __launch_bounds__(kMT) void layer_fused_kernel(const FusedArgs f) {
                                                              f.rsf, f.top_p, r);
 
     // ---- phase 3: the stream
-    stream<BITS, kResid, kQ8>(f, r, dyn, xu, qdx, gate, shtile);
+    stream<BITS, kResid, kQ8, kPass>(f, r, dyn, xu, qdx, gate, shtile);
 
     // Workgroup 0 writes the routing outputs last, from LDS: stores issued
     // earlier would make the compiler wait for the stream's first loads
@@ -1355,9 +1475,14 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     // pipelined kernel); it has no residual form
     const bool topp = f.top_p < 1.f, resid = f.x_out != nullptr, q8 = f.act8 != 0;
     if (!q8 || resid) return hipErrorInvalidValue;
-    auto k = topp ? layer_fused_kernel<BITS, true, false, true> : layer_fused_kernel<BITS, false, false, true>;
-    static size_t static_cache[2] = {0, 0};                         // each variant's static LDS, read once
-    size_t& static_lds = static_cache[topp];
+    // one pass of token columns where the batch fits it, else all passes
+    constexpr int kNCB = Q8Cols<BITS>::NCB, kFull = (kCols * kNCB + 15) / 16;
+    const bool one = l.T * kNCB <= 16;
+    auto k = one ? (topp ? layer_fused_kernel<BITS, true, false, true, 1> : layer_fused_kernel<BITS, false, false, true, 1>)
+                 : (topp ? layer_fused_kernel<BITS, true, false, true, kFull>
+                         : layer_fused_kernel<BITS, false, false, true, kFull>);
+    static size_t static_cache[2][2] = {{0, 0}, {0, 0}};            // each variant's static LDS, read once
+    size_t& static_lds = static_cache[one][topp];
     if (static_lds == 0) {
         hipFuncAttributes attr;
         hipError_t err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k));
@@ -1368,8 +1493,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const int H = l.ex.H, I = l.ex.I, T = l.T;
     const int rd = (H + nwg - 1) / nwg;
     if (rd > kNBD * 16) return hipErrorInvalidValue;             // more output rows than a pass holds
-    if (q8 && (H % (512 / BITS) || I % (512 / BITS))) return hipErrorInvalidValue;   // whole activation blocks
-    const int NCHd = ((I * BITS / 8) / 16 + 3) / 4;
+    if (q8 && (H % 32 || I % 32)) return hipErrorInvalidValue;   // whole activation blocks
     const int A = T * l.ex.slots;
     const int max_active = l.ex.max_active;
     if (static_lds + kLdsOnePerCu > kLdsMax) return hipErrorInvalidValue;
@@ -1393,7 +1517,8 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     const bool shp = !q8 && l.n_shared >= 1 && T <= kMW - 2 && (long long)l.n_shared * I <= 8LL * nwg &&
                      (kMW - 1 - T) * kShPref >= NCHg;
     const size_t shpart = shp ? align16(((size_t)kMW * 16 * T + 16) * sizeof(float)) : 0;
-    const size_t fixed = gured + gsc + dsc + pairs + hprod + shpart;
+    const size_t qdx = q8 ? align16((size_t)(H / 32) * T * sizeof(float)) : 0;   // block scales of the staged x
+    const size_t fixed = gured + gsc + dsc + pairs + hprod + shpart + qdx;
     auto staging = [&](int q) {
         size_t s = align16(staged_row_bytes_i8<BITS>(I) * q);
         if (s < x_bytes) s = x_bytes;
@@ -1402,7 +1527,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     };
     auto total = [&](int q) {
         const size_t chunks = (size_t)(A + q - 1) / q;
-        const size_t q8_scales = q8 ? (size_t)q * NCHd : 0;       // the staged h rows' block scales
+        const size_t q8_scales = q8 ? (size_t)q * (I / 32) : 0;   // the staged h rows' block scales
         const size_t all_chunks = (size_t)(T * l.ex.slots + q - 1) / q;
         return staging(q) + fixed +
                align16(((size_t)q * (4 + kCols) + 3 * ((q8 ? all_chunks : chunks) + 1) + q8_scales) * sizeof(int));
@@ -1421,6 +1546,7 @@ hipError_t layer_fused_bits(FusedArgs f, const FusedLayerArgs& l, hipStream_t st
     f.off_pairs = (int)(stg + gured + gsc + dsc);
     f.off_hprod = (int)(stg + gured + gsc + dsc + pairs);
     f.off_shpart = (int)(stg + gured + gsc + dsc + pairs + hprod);
+    f.off_qdx = (int)(stg + gured + gsc + dsc + pairs + hprod + shpart);
     f.shp = shp ? 1 : 0;
     f.off_chunk = (int)(stg + fixed);
     size_t lds = total(qc);

@@ -24,13 +24,20 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
-# name: (T, H, I, E, G, TG, K, S, bits); hidden and inter multiples of 512 / bits
+# name: (T, H, I, E, G, TG, K, S, bits); hidden and inter whole 32-column
+# blocks and whole 16-byte code groups.  The "ragged" shapes end inside a
+# K-chunk of the matrix-core tile (4 groups of 16 bytes of codes) and take
+# two passes of the MFMA's token columns (4 tokens a pass for int4 and int2,
+# 8 for int8).
 SHAPES = {
     "tiny_q4": (1, 256, 128, 16, 4, 2, 4, 1, 4),
     "t3_q4_s2": (3, 2048, 512, 64, 8, 3, 6, 2, 4),
     "t5_q8_noshared": (5, 1536, 320, 16, 2, 1, 2, 0, 8),
     "t2_q2": (2, 512, 256, 32, 4, 2, 4, 1, 2),
     "t16_q4": (16, 1024, 256, 64, 8, 4, 8, 1, 4),
+    "t5_q4_ragged": (5, 1056, 352, 32, 4, 2, 4, 1, 4),
+    "t9_q8_ragged": (9, 800, 224, 24, 4, 2, 3, 1, 8),
+    "t6_q2_ragged": (6, 576, 192, 16, 2, 1, 4, 1, 2),
 }
 
 
@@ -93,7 +100,7 @@ def test_act8_blocks_of_very_different_scale():
     cfg = _cfg("t3_q4_s2", seed=37)
     lay = synth.layer_device(cfg, 0, DEV)
     x = synth.token_pool(cfg, cfg.tokens)
-    blk = 512 // cfg.bits
+    blk = orc.act8_block(cfg.bits)
     x[0, :blk] *= np.float32(1e-6)
     x[0, blk:2 * blk] *= np.float32(1e6)
     x[1, 3 * blk:4 * blk] = 0.0
@@ -102,7 +109,7 @@ def test_act8_blocks_of_very_different_scale():
 
 
 def test_act8_needs_whole_blocks():
-    cfg = synth.MoEConfig("odd", 1, 256, 96, 16, 4, 2, 4, 1, 4, seed=3)     # inter 96: not whole 128-blocks
+    cfg = synth.MoEConfig("odd", 1, 256, 48, 16, 4, 2, 4, 1, 8, seed=3)     # int8, inter 48: not whole 32-blocks
     lay = synth.layer_device(cfg, 0, DEV)
     xt = torch.from_numpy(synth.token_pool(cfg, 1)).to(DEV)
     ex = ops.Experts.from_layer(lay, cfg.n_experts, cfg.n_shared, cfg.bits)

@@ -73,9 +73,9 @@ def _act8_shapes(n=12, seed=2027):
     out = []
     while len(out) < n:
         bits = int(rng.choice([2, 4, 8]))
-        blk = 512 // bits                        # one activation block
-        H = int(rng.integers(1, 9)) * blk
-        I = int(rng.integers(1, 7)) * blk
+        unit = max(32, 128 // bits)              # whole activation blocks and code groups
+        H = int(rng.integers(1, 33)) * unit
+        I = int(rng.integers(1, 25)) * unit
         G = int(rng.choice([1, 2, 4, 8]))
         per = int(rng.integers(2, 9))
         E = G * per
