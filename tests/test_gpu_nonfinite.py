@@ -1,5 +1,5 @@
-"""Non-finite routing inputs through the fused and the separate calls,
-against the oracle (reading R6: a NaN corrected score, or a NaN group score
+"""Non-finite routing inputs through the fused, the separate and the
+int8-activation calls, against the oracle (reading R6: a NaN corrected score, or a NaN group score
 from +inf and -inf in one group, ranks as -inf with ties to the lower index).
 
 Show HN page "धीमे कंप्यूटर पर GLM 5.2 चलाना", section "implemented
@@ -38,17 +38,20 @@ def _bias(case):
     return b
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "split"])
+@pytest.mark.parametrize("mode", ["fused", "split", "act8"])
 @pytest.mark.parametrize("case", ["nan_bias", "inf_groups", "nan_x"])
-def test_nonfinite_routing(case, fused):
-    say(f"case {case} {'fused' if fused else 'split'}")
+def test_nonfinite_routing(case, mode):
+    """(act8: the int8-activation call, whose NaN-x token has a NaN block
+    scale -- reading R21 applied to activation blocks -- so its h and y are
+    NaN; the other tokens as usual.)"""
+    say(f"case {case} {mode}")
     lay = synth.layer_device(CFG, 0, DEV)
     b = _bias(case)
     lay["bias"] = torch.from_numpy(b).to(DEV)
     x = synth.batch_tokens(CFG, 0).copy()
     if case == "nan_x":
         x[1, 7] = np.nan
-    g = run_layer(CFG, lay, x, fused=fused)
+    g = run_layer(CFG, lay, x, fused=mode != "split", act8=mode == "act8")
     r = check_all(CFG, g, x, synth.router_weight(CFG, 0), b, synth.expert_loader(CFG, 0))
     if case == "nan_bias":
         assert not np.isin(g["idx"], [3, 17, 40]).any()
@@ -61,3 +64,5 @@ def test_nonfinite_routing(case, fused):
         np.testing.assert_array_equal(r.idx[1], np.arange(CFG.top_k))
         others = [t for t in range(CFG.tokens) if t != 1]
         assert np.isfinite(g["y"][others]).all()
+        if mode == "act8":
+            assert np.isnan(g["y"][1]).all() and np.isnan(r.y[1]).all()
