@@ -80,10 +80,12 @@ all-tied case; the weights-sum invariant; the one-hot-input and all-equal
 closed forms of the FFN; the RMSNorm closed form; the ~19 MB expert size of
 [HN-S]; for the row quantiser, hand-worked rows, the exact round trip of code
 rows that reach +-qmax, the nearest-code brute force over the whole code
-alphabet, and the sign and power-of-two scaling symmetries.  Parity unpinned
-by the pages: the group-score rule R1, the code layouts R8-R10 and the
-quantiser rule R20-R21 are readings; the tests pin the oracle to those
-readings, not the readings to the pages.
+alphabet, and the sign and power-of-two scaling symmetries.  The pages
+print no worked example, so the group-score rule R1, the code layouts
+R8-R10, the quantiser rule R20-R21, the top-p rule R22 and the activation
+blocks R23 are readings: the tests pin each function to its reading's own
+mathematics (brute force, closed forms, exhaustive tables), and the
+readings themselves are choices, listed with their reasons.
 """
 from __future__ import annotations
 
