@@ -17,9 +17,10 @@
 // first, they need no routing, then the routed ones).  When the staged-h
 // buffers in LDS hold every expert of the batch, the order is all GU(j),
 // then all DN(j): each expert's h is exchanged and staged while the later
-// experts' gate/up rows stream.  Otherwise DN(j) follows GU(j + 5):
-//     GU(0) .. GU(4) GU(5) DN(0) GU(6) DN(1) ... GU(n-1) DN(n-6) DN(n-5) .. DN(n-1)
-// so a staged buffer is freed while later experts still stream.
+// experts' gate/up rows stream.  Otherwise DN(j) follows GU(j + L), L = 10:
+//     GU(0) .. GU(9) GU(10) DN(0) GU(11) DN(1) ... GU(n-1) DN(n-11) DN(n-10) .. DN(n-1)
+// so a staged buffer is freed while later experts still stream, and each
+// expert's h has the time of L gate/up units to be exchanged and staged.
 //
 // Waves of a workgroup (one workgroup per compute unit, 8 waves by default):
 //   streaming (0-5): a ring of kRing items per wave in flight, int8
@@ -87,7 +88,7 @@ constexpr int kNStg = MOEDEC_PIPE_STAGERS;              // stager waves (slots c
 constexpr int kSW = kPW - 1 - kNStg;                    // streaming waves
 constexpr int kFin = kSW, kStg = kSW + 1;               // control waves: the finalizer, the stagers
 constexpr int kRing = MOEDEC_PIPE_RING;                 // items in flight per streaming wave
-constexpr int kLag = 5;                                 // DN(j) follows GU(j + kLag) when not every slot fits a buffer
+constexpr int kLag = 10;                                // DN(j) follows GU(j + kLag) when not every slot fits a buffer
 constexpr int kNHBMax = 16;                             // staged-h buffers at most (2 where LDS is short)
 constexpr int kNPB = 3;                                 // gate/up partial-sum buffers
 constexpr int kPieces = 3;                              // bytes of a 24-bit activation
