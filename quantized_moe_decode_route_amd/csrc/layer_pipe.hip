@@ -796,25 +796,64 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
 
     // ---- phase 2: routing (the last waves route, the union on the last wave)
     if (routes) gates.wait(0, gates.launch + 1ull);
-    route_select_block<kCols, kPipeExperts, kPW, true, kTopP, true>(f.scores, f.bias, T, E, f.n_group, f.topk_group,
-                                                                   K, S, f.rsf, f.top_p, route);
-    // the routing outputs the rest of the launch reads, out of the region HB / PART reuse
-    const int n_act = route.n_active;
-    const int A = route.n_assign;
-    for (int i = threadIdx.x; i < T * K; i += kPT) {
-        p_sel[i] = route.sel[i];
-        p_selw[i] = route.selw[i];
-    }
-    for (int i = threadIdx.x; i <= n_act; i += kPT) {
-        if (i < n_act) p_eid[i] = route.eid[i];
-        p_seg[i] = route.seg[i];
-    }
-    for (int i = threadIdx.x; i < A; i += kPT) p_asn[i] = route.assign[i];
-    if (threadIdx.x == 0) {
-        sy.n_slots = n_act;
-        sy.n_assign = A;
+    if (!kTopP && T == 1) {
+        // One token under top-k: its K experts are distinct, so the batch
+        // union is them in ascending order, one assignment each (slot k is
+        // assignment k), then the shared experts; the routing wave writes it
+        // straight to the arrays the launch reads.
+        if (wave == kPW - 1) {
+            constexpr int NV = kPipeExperts / kWave, NV4 = NV < 4 ? NV : 4;
+            if (NV == NV4 || E <= NV4 * kWave)
+                route_one_token<NV4, kCols, kPipeExperts, kPW, true, false>(f.scores, f.bias, 0, E, f.n_group,
+                                                                        f.topk_group, K, f.rsf, 1.f, route);
+            else
+                route_one_token<NV, kCols, kPipeExperts, kPW, true, false>(f.scores, f.bias, 0, E, f.n_group,
+                                                                       f.topk_group, K, f.rsf, 1.f, route);
+            wave_lds_sync();                             // this wave's selection writes
+            const int e = lane < K ? route.sel[lane] : INT_MAX;
+            const float w = lane < K ? route.selw[lane] : 0.f;
+            int rank = 0;
+            for (int k = 0; k < K; ++k) rank += __builtin_amdgcn_readlane(e, k) < e;
+            if (lane < K) {
+                p_sel[lane] = e;
+                p_selw[lane] = w;
+                p_eid[rank] = e;
+                p_seg[rank] = rank;
+                p_asn[rank] = lane;
+            } else if (lane < K + S) {
+                p_eid[lane] = E + (lane - K);
+                p_seg[lane] = lane;
+                p_asn[lane] = lane;
+            }
+            if (lane == 0) {
+                p_seg[K + S] = K + S;
+                sy.n_slots = K + S;
+                sy.n_assign = K + S;
+            }
+        }
+    } else {
+        route_select_block<kCols, kPipeExperts, kPW, true, kTopP, true>(f.scores, f.bias, T, E, f.n_group,
+                                                                       f.topk_group, K, S, f.rsf, f.top_p, route);
+        // the routing outputs the rest of the launch reads, out of the region HB / PART reuse
+        const int n_act0 = route.n_active;
+        const int A0 = route.n_assign;
+        for (int i = threadIdx.x; i < T * K; i += kPT) {
+            p_sel[i] = route.sel[i];
+            p_selw[i] = route.selw[i];
+        }
+        for (int i = threadIdx.x; i <= n_act0; i += kPT) {
+            if (i < n_act0) p_eid[i] = route.eid[i];
+            p_seg[i] = route.seg[i];
+        }
+        for (int i = threadIdx.x; i < A0; i += kPT) p_asn[i] = route.assign[i];
+        if (threadIdx.x == 0) {
+            sy.n_slots = n_act0;
+            sy.n_assign = A0;
+        }
     }
     __syncthreads();
+    const int n_act = sy.n_slots;
+    const int A = sy.n_assign;
     // HB's padding groups are zero in every staged buffer (staging writes only valid groups)
     zero_pad<BITS, NP>(Pd, NCHd, nc, HB, nhb, hb_bytes, threadIdx.x, kPT);
     __syncthreads();
