@@ -637,12 +637,7 @@ __device__ __forceinline__ int build_items(const Geo& g, int w, int nu, uint2* L
             }
             n_items = nit > 0 ? ntile * nit : 1;
         }
-        int incl = n_items;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += v;
-        }
+        const int incl = wave_scan_incl(n_items);        // inclusive prefix sum over the lanes (DPP)
         if (u < nu) {
             int k = base + incl - n_items;
             const uint32_t jk = (uint32_t)j | (uint32_t)kind << 10;
@@ -854,9 +849,12 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     __syncthreads();
     const int n_act = sy.n_slots;
     const int A = sy.n_assign;
-    // HB's padding groups are zero in every staged buffer (staging writes only valid groups)
-    zero_pad<BITS, NP>(Pd, NCHd, nc, HB, nhb, hb_bytes, threadIdx.x, kPT);
-    __syncthreads();
+    // HB's padding groups are zero in every staged buffer (staging writes only
+    // valid groups); a row of whole K-chunks has none
+    if (Pd < 4 * NCHd) {
+        zero_pad<BITS, NP>(Pd, NCHd, nc, HB, nhb, hb_bytes, threadIdx.x, kPT);
+        __syncthreads();
+    }
     g.n = n_act;
     g.lag = nhb >= n_act ? n_act : kLag;             // every slot has a buffer: all gate/up first
     if (wave == 0) PIPE_MARK(tr, 3);
