@@ -32,6 +32,10 @@ SHAPES = {
     "t1_e100": (1, 512, 128, 100, 4, 2, 6, 1, 4),
     # more tokens than LDS holds at H = 6144: tokens staged per segment
     "t8_h6144_segments": (8, 6144, 256, 64, 8, 4, 8, 1, 4),
+    # one token (the fused call writes the batch union from the routing wave):
+    # no shared expert; a single routed expert and two shared ones
+    "t1_noshared": (1, 512, 256, 32, 4, 2, 6, 0, 4),
+    "t1_top1_two_shared": (1, 768, 256, 24, 3, 1, 1, 2, 8),
 }
 
 
