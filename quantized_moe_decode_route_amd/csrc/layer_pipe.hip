@@ -545,6 +545,7 @@ struct Geo {
     int NCHg, NCHd;                // K-chunks of a gate/up row and of a down row
     int rd;                        // down rows of this workgroup
     int nwg, b;
+    int nwg_mask, nwg_log;         // nwg - 1 and log2(nwg) when nwg is a power of two, else -1
 };
 
 __device__ __forceinline__ void unit_of(int u, int n, int lag, int& kind, int& j) {
@@ -568,6 +569,10 @@ __device__ __forceinline__ void unit_of(int u, int n, int lag, int& kind, int& j
 
 // Tiles of slot j that workgroup b takes: i = i0, i0 + nwg, ... < NT.
 __device__ __forceinline__ int tiles_of(const Geo& g, int j, int& i0) {
+    if (g.nwg_mask >= 0) {                              // (the usual case: 256 compute units)
+        i0 = (g.b - j * g.NT) & g.nwg_mask;
+        return i0 < g.NT ? ((g.NT - 1 - i0) >> g.nwg_log) + 1 : 0;
+    }
     const int base = (j * g.NT) % g.nwg;                // j * NT < 2^31 (slots <= 520, NT <= 2048)
     i0 = (g.b - base + g.nwg) % g.nwg;
     return i0 < g.NT ? (g.NT - 1 - i0) / g.nwg + 1 : 0;
@@ -749,6 +754,8 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
     g.NCHd = NCHd;
     g.rd = rd;
     g.nwg = nwg;
+    g.nwg_mask = (nwg & (nwg - 1)) == 0 ? nwg - 1 : -1;
+    g.nwg_log = g.nwg_mask >= 0 ? __builtin_ctz(nwg) : -1;
     g.b = b;
 
     // streaming waves: this lane's part of an item
