@@ -1121,6 +1121,7 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
             tot[0][p] = tot[1][p] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         int hb_cur = -1;                                 // DN unit whose staged h this wave has waited for
+        int hb_j = 0;                                    // ... and its staged buffer (hb_cur % nhb)
 #ifdef MOEDEC_PIPE_TRACE
         if (wave == 0) PIPE_MARK(tr, 4);
         int mark_u = -1, mark_key = -1;
@@ -1166,11 +1167,12 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
                     lds_signal_add(&sy.gu_cnt[pb], 1);
                 }
             } else {
-                const int hb = j % nhb;
                 if (hb_cur != j) {
-                    lds_wait_ge(&sy.hb_ready[hb], j + 1, f.ws, lds_cap);
+                    hb_j = j % nhb;
+                    lds_wait_ge(&sy.hb_ready[hb_j], j + 1, f.ws, lds_cap);
                     hb_cur = j;
                 }
+                const int hb = hb_j;
                 const uint8_t* B = HB + hb * hb_bytes + (size_t)c * xb_chunk;
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
@@ -1238,7 +1240,8 @@ __global__ __launch_bounds__(kPT) void layer_pipe_kernel(const PipeArgs f) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {                // every load first, then the stores
                     const int idx = min(base + k * kWave + lane, total - 1);
-                    const int j = idx / per, rem = idx - j * per, tile = rem >> 4, r = rem & 15;
+                    const int j = f.ntile_max == 1 ? idx >> 4 : idx / per;   // (one tile: per = 16)
+                    const int rem = idx - j * per, tile = rem >> 4, r = rem & 15;
                     int i0;
                     const int nt = tiles_of(g, j, i0);
                     const int pair = 8 * (i0 + min(tile, max(nt - 1, 0)) * nwg) + (r & 7);
